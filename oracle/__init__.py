@@ -1,0 +1,60 @@
+"""fp64 CPU oracle for training-free block-sparse attention.
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and
+``bench.py``'s ``cpu_baseline`` leg may import this package.  The product
+path (``block_mean_pool_amd``) never imports, calls or links anything here,
+and nothing here imports the product path: the two share no code.
+
+Sources followed (the method as the pages state it):
+
+* SpargeAttn abstract (taxoreview.com page, and the same abstract on the
+  huggingface-mirror search page): a two-stage online filter; stage one
+  rapidly predicts the attention map so that some matrix multiplications can
+  be skipped, stage two is a softmax-aware filter inside the online softmax
+  that skips further multiplications; the attention is also quantized.
+* iCATS abstract (arxivdaily.com page, English abstract): training-free
+  sparse attention estimates the importance of query-key regions, derives a
+  sparse mask, and computes only the important candidates; prior work
+  estimates scores from tokens grouped independently on the query and the
+  key side; masks are built with a top-p rule.
+* DynSparse story (embedding.report page): top-p vs top-k selection and a
+  threshold built from the cumulative energy of the selected tokens, a
+  quantity the flash-attention operator already holds.
+
+Every concrete choice the pages leave open (block-mean pooling as the
+grouping, block sizes, the tie order, the cut rule, the lambda test, the
+quantisation formats) is a stated reading, listed in the module docstrings.
+
+Parity status: every function here is pinned by the CPU tests
+(``tests/test_oracle_*.py``) against brute force, closed forms, invariants
+or an independent library routine.  The pages' end-to-end model figures
+(VBench, PSNR) are parity unpinned: no weights or suites exist here.
+"""
+from .sparse_attn_oracle import (  # noqa: F401
+    Params,
+    n_blocks,
+    pool_means,
+    admissible_blocks,
+    block_scores,
+    block_weights,
+    forced_blocks,
+    processing_order,
+    cut_length,
+    predict_head,
+    sparse_attention_head,
+    dense_attention_head,
+    oracle_head,
+)
+from .quant import (  # noqa: F401
+    e4m3_round,
+    e4m3_encode,
+    int8_quantize_blocks,
+    fp8_quantize_v_blocks,
+    sparse_attention_quant_head,
+)
+from .metrics import (  # noqa: F401
+    rel_l1,
+    block_sparsity,
+    skip_fraction,
+    true_recall,
+)

@@ -1,0 +1,164 @@
+"""Quantised variant of the oracle: INT8 Q.K^T and FP8 (e4m3) P.V.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring).
+
+Passages: the SpargeAttn abstract calls the attention "sparse and quantized";
+the DynSparse story says the filter combines with quantization.  The pages
+fix no format, so the readings are:
+
+* Q and K: one scale per (batch, head, block) -- query blocks of BQ rows,
+  key blocks of BK rows -- equal to the block's absolute maximum / 127
+  (1 when the block is all zero); code = round-half-even(x / scale) clamped
+  to [-127, 127].  The scale and the quotient are float32 operations, the
+  same precision the kernel decides the codes in.
+* V: one scale per key block = absmax / 448 (1 when zero); code = e4m3 of
+  the float32 quotient.
+* P: multiplied by exactly 2^8 before the e4m3 conversion and by 2^-8 after
+  (a plain cast would flush P below about 2^-10 to zero).  The running sum l
+  uses the unquantised P.
+* e4m3 is the OCP 8-bit floating point E4M3 format: 1 sign, 4 exponent bits
+  with bias 7, 3 mantissa bits, no infinities, largest finite 448, smallest
+  normal 2^-6, subnormals k * 2^-9.  Conversion rounds to nearest, ties to
+  even, and saturates finite overflow to +-448.
+* Stage one (pooling, scores, mask) uses the unquantised inputs.
+"""
+from __future__ import annotations
+
+import math
+from typing import List, Optional
+
+import numpy as np
+
+from .sparse_attn_oracle import Params, n_blocks
+
+
+def e4m3_round(x) -> np.ndarray:
+    """Round float64 values to the nearest e4m3 value (ties to even),
+    saturating at +-448.  NaN stays NaN."""
+    x = np.asarray(x, dtype=np.float64)
+    a = np.abs(x)
+    _, E = np.frexp(a)                  # a = f * 2^E, f in [0.5, 1)
+    e = np.maximum(E - 1, -6)           # binade exponent; subnormals use 2^-6's
+    quantum = np.ldexp(1.0, e - 3)      # 3 mantissa bits
+    r = np.rint(a / quantum) * quantum  # exact scaling by a power of two
+    r = np.minimum(r, 448.0)
+    out = np.copysign(r, x)
+    out[np.isnan(x)] = np.nan
+    return out
+
+
+def e4m3_encode(x) -> np.ndarray:
+    """Bit patterns (uint8) of e4m3_round(x)."""
+    r = e4m3_round(x)
+    a = np.abs(r)
+    sign = np.signbit(r).astype(np.uint8) << 7
+    code = np.zeros(a.shape, dtype=np.uint8)
+    sub = (a > 0) & (a < 2.0 ** -6)
+    code[sub] = np.rint(a[sub] / 2.0 ** -9).astype(np.uint8)
+    nrm = a >= 2.0 ** -6
+    _, E = np.frexp(a[nrm])
+    e = E - 1
+    mant = np.rint(a[nrm] / np.ldexp(1.0, e) * 8.0 - 8.0).astype(np.int64)
+    code[nrm] = ((e + 7) << 3 | mant).astype(np.uint8)
+    code = code | sign
+    code[np.isnan(r)] = 0x7F
+    return code
+
+
+def int8_quantize_blocks(X, bs: int):
+    """Per-block symmetric INT8 codes.  Returns (codes int8 [N, d],
+    scales float32 [NB])."""
+    X = np.asarray(X, dtype=np.float32)
+    N, d = X.shape
+    nb = n_blocks(N, bs)
+    codes = np.zeros((N, d), dtype=np.int8)
+    scales = np.zeros(nb, dtype=np.float32)
+    for b in range(nb):
+        blk = X[b * bs:min(N, (b + 1) * bs)]
+        amax = np.float32(np.abs(blk).max())
+        s = np.float32(amax / np.float32(127.0)) if amax > 0 else np.float32(1.0)
+        q = np.rint(blk / s)                      # float32 division, half-even
+        codes[b * bs:min(N, (b + 1) * bs)] = np.clip(q, -127, 127).astype(np.int8)
+        scales[b] = s
+    return codes, scales
+
+
+def fp8_quantize_v_blocks(V, bk: int):
+    """Per-key-block e4m3 values of V.  Returns (values float64 on the e4m3
+    grid [N, d], scales float32 [NKB])."""
+    V = np.asarray(V, dtype=np.float32)
+    N, d = V.shape
+    nb = n_blocks(N, bk)
+    vals = np.zeros((N, d), dtype=np.float64)
+    scales = np.zeros(nb, dtype=np.float32)
+    for b in range(nb):
+        blk = V[b * bk:min(N, (b + 1) * bk)]
+        amax = np.float32(np.abs(blk).max())
+        s = np.float32(amax / np.float32(448.0)) if amax > 0 else np.float32(1.0)
+        vals[b * bk:min(N, (b + 1) * bk)] = e4m3_round((blk / s).astype(np.float64))
+        scales[b] = s
+    return vals, scales
+
+
+def sparse_attention_quant_head(Q, K, V, kept: List[np.ndarray], p: Params,
+                                force_skip: Optional[List[np.ndarray]] = None):
+    """Quantised stage two: the same online softmax, processing order and
+    skip rule as the unquantised oracle, with
+    S = sm * s_q(i) * s_k(j) * (Qcode . Kcode)  (exact integer dot product) and
+    the P.V term  s_v(j) * 2^-8 * sum_c e4m3(2^8 * P) * Vcode.
+    Returns (O, lse, skips)."""
+    N, d = np.asarray(Q).shape
+    sm = p.sm(d)
+    lam = float(p.lam)
+    qc, qs = int8_quantize_blocks(Q, p.BQ)
+    kc, ks = int8_quantize_blocks(K, p.BK)
+    vq, vs = fp8_quantize_v_blocks(V, p.BK)
+    qc = qc.astype(np.int64)
+    kc = kc.astype(np.int64)
+    n_groups = (p.BQ + p.G - 1) // p.G
+    O = np.zeros((N, d))
+    lse = np.full(N, -np.inf)
+    skips = []
+    for i, lst in enumerate(kept):
+        rows = np.arange(i * p.BQ, min(N, (i + 1) * p.BQ))
+        nr = len(rows)
+        m = np.full(nr, -np.inf)
+        l = np.zeros(nr)
+        acc = np.zeros((nr, d))
+        sk = np.zeros((len(lst), n_groups), dtype=bool)
+        for t, j in enumerate(lst):
+            cols = np.arange(j * p.BK, min(N, (j + 1) * p.BK))
+            idot = qc[rows] @ kc[cols].T               # exact in int64
+            S = sm * float(qs[i]) * float(ks[j]) * idot.astype(np.float64)
+            if p.causal:
+                S = np.where(cols[None, :] > rows[:, None], -np.inf, S)
+            mloc = S.max(axis=1)
+            mnew = np.maximum(m, mloc)
+            alpha = np.ones(nr)
+            moved = np.isfinite(mnew) & (m != mnew)
+            alpha[moved] = np.exp(m[moved] - mnew[moved])   # exp(-inf) = 0
+            safe = np.where(np.isfinite(mnew), mnew, 0.0)
+            P = np.where(np.isfinite(S), np.exp(S - safe[:, None]), 0.0)
+            l = alpha * l + P.sum(axis=1)
+            acc = alpha[:, None] * acc
+            Pq = e4m3_round(P * 256.0) / 256.0
+            delta_r = np.where(np.isfinite(mloc), mloc - safe, -np.inf)
+            for g in range(n_groups):
+                gr = slice(g * p.G, min(nr, (g + 1) * p.G))
+                dg = delta_r[gr].max() if gr.start < nr else -np.inf
+                skip = bool(dg < lam)
+                if force_skip is not None:
+                    skip = bool(force_skip[i][t, g])
+                sk[t, g] = skip
+                if not skip and gr.start < nr:
+                    acc[gr] += float(vs[j]) * (Pq[gr] @ vq[cols])
+            m = mnew
+        skips.append(sk)
+        ok = l > 0
+        O[rows[ok]] = acc[ok] / l[ok, None]
+        lse[rows[ok]] = m[ok] + np.log(l[ok])
+    return O, lse, skips
+
+
+__all__ = ["e4m3_round", "e4m3_encode", "int8_quantize_blocks",
+           "fp8_quantize_v_blocks", "sparse_attention_quant_head", "math"]
