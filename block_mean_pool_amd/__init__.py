@@ -1,0 +1,192 @@
+"""Python binding of libsparse_attn.so (the C ABI in include/sparse_attn.h).
+
+Argument marshalling only: every step of block-sparse attention runs in the
+library's HIP kernels.  PyTorch supplies device memory and the current
+stream; tensors are passed by ``data_ptr()``.  Importing this module fails
+loudly when the library has not been built (``python
+block_mean_pool_amd/build.py``) -- there is no CPU fallback.
+
+Entry points have the C names:
+
+    sparse_attn_mask_shape(params) -> (nqb, nkb)
+    sparse_attn_workspace_size(params) -> (predict_bytes, forward_bytes)
+    sparse_attn_predict(params, q, k, mask, ws, stream=None)
+    sparse_attn_forward(params, q, k, v, mask, o, lse=None, skip_bits=None,
+                        ws=None, stream=None)
+    sparse_attn_info() -> (default_group_rows, version)
+    sparse_attn_status_str(code) -> str
+    sparse_attn_last_error() -> str
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libsparse_attn.so")
+HEADER = os.path.join(os.path.dirname(HERE), "include", "sparse_attn.h")
+
+SA_OK, SA_ERR_INVALID_ARG, SA_ERR_UNSUPPORTED, SA_ERR_WORKSPACE, SA_ERR_HIP = range(5)
+SA_F32, SA_BF16 = 0, 1
+SA_PREC_NATIVE, SA_PREC_I8_FP8 = 0, 1
+SA_RULE_TOPCDF, SA_RULE_ENERGY = 0, 1
+
+
+class SaParams(ctypes.Structure):
+    _fields_ = [
+        ("B", ctypes.c_int32), ("H", ctypes.c_int32), ("N", ctypes.c_int32),
+        ("D", ctypes.c_int32), ("block_q", ctypes.c_int32), ("block_k", ctypes.c_int32),
+        ("causal", ctypes.c_int32), ("dtype", ctypes.c_int32), ("prec", ctypes.c_int32),
+        ("rule", ctypes.c_int32), ("tau", ctypes.c_float), ("lam", ctypes.c_float),
+        ("sm_scale", ctypes.c_float), ("keep_prefix_kblocks", ctypes.c_int32),
+        ("lambda_group_rows", ctypes.c_int32), ("o_fp32", ctypes.c_int32),
+        ("stride_b", ctypes.c_int64),
+        ("stride_h", ctypes.c_int64), ("stride_n", ctypes.c_int64),
+    ]
+
+
+class SaMask(ctypes.Structure):
+    _fields_ = [("kept_idx", ctypes.c_void_p), ("kept_cnt", ctypes.c_void_p),
+                ("block_prob", ctypes.c_void_p)]
+
+
+class SparseAttnError(RuntimeError):
+    def __init__(self, code: int, where: str, msg: str):
+        super().__init__(f"{where}: {status_name(code)}: {msg}")
+        self.code = code
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is missing: build the HIP library first "
+            "(python block_mean_pool_amd/build.py); there is no fallback path")
+    lib = ctypes.CDLL(LIB_PATH)
+    P = ctypes.POINTER
+    vp = ctypes.c_void_p
+    sig = {
+        "sparse_attn_mask_shape": [P(SaParams), P(ctypes.c_int64), P(ctypes.c_int64)],
+        "sparse_attn_workspace_size": [P(SaParams), P(ctypes.c_size_t), P(ctypes.c_size_t)],
+        "sparse_attn_predict": [P(SaParams), vp, vp, P(SaMask), vp, ctypes.c_size_t, vp],
+        "sparse_attn_forward": [P(SaParams), vp, vp, vp, P(SaMask), vp, vp, vp, vp,
+                                ctypes.c_size_t, vp],
+        "sparse_attn_info": [P(ctypes.c_int32), P(ctypes.c_int32)],
+    }
+    for name, args in sig.items():
+        f = getattr(lib, name)
+        f.argtypes = args
+        f.restype = ctypes.c_int
+    lib.sparse_attn_status_str.argtypes = [ctypes.c_int32]
+    lib.sparse_attn_status_str.restype = ctypes.c_char_p
+    lib.sparse_attn_last_error.argtypes = []
+    lib.sparse_attn_last_error.restype = ctypes.c_char_p
+    return lib
+
+
+lib = _load()
+
+
+def status_name(code: int) -> str:
+    return lib.sparse_attn_status_str(int(code)).decode()
+
+
+def sparse_attn_status_str(code: int) -> str:
+    return status_name(code)
+
+
+def sparse_attn_last_error() -> str:
+    return lib.sparse_attn_last_error().decode()
+
+
+def _check(code: int, where: str):
+    if code != SA_OK:
+        raise SparseAttnError(code, where, sparse_attn_last_error())
+
+
+def make_params(B, H, N, D, *, dtype="bf16", causal=False, tau=0.95, lam=-math.inf,
+                sm_scale=0.0, rule="topcdf", prec="native", keep_prefix_kblocks=0,
+                block_q=128, block_k=64, lambda_group_rows=0, o_fp32=False,
+                strides=(0, 0, 0)) -> SaParams:
+    """A parameter block; ``strides`` are element strides (b, h, n), 0 =
+    packed [B, H, N, D]; ``o_fp32`` writes O as float32."""
+    return SaParams(
+        B, H, N, D, block_q, block_k, int(bool(causal)),
+        {"f32": SA_F32, "bf16": SA_BF16}[dtype] if isinstance(dtype, str) else int(dtype),
+        {"native": SA_PREC_NATIVE, "i8fp8": SA_PREC_I8_FP8}[prec] if isinstance(prec, str) else int(prec),
+        {"topcdf": SA_RULE_TOPCDF, "energy": SA_RULE_ENERGY}[rule] if isinstance(rule, str) else int(rule),
+        float(tau), float(lam), float(sm_scale), int(keep_prefix_kblocks),
+        int(lambda_group_rows), int(bool(o_fp32)), int(strides[0]), int(strides[1]),
+        int(strides[2]))
+
+
+def _ptr(t) -> Optional[int]:
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _nbytes(t) -> int:
+    return 0 if t is None else t.numel() * t.element_size()
+
+
+def sparse_attn_mask_shape(p: SaParams):
+    nq, nk = ctypes.c_int64(), ctypes.c_int64()
+    _check(lib.sparse_attn_mask_shape(ctypes.byref(p), ctypes.byref(nq), ctypes.byref(nk)),
+           "sparse_attn_mask_shape")
+    return nq.value, nk.value
+
+
+def sparse_attn_workspace_size(p: SaParams):
+    a, b = ctypes.c_size_t(), ctypes.c_size_t()
+    _check(lib.sparse_attn_workspace_size(ctypes.byref(p), ctypes.byref(a), ctypes.byref(b)),
+           "sparse_attn_workspace_size")
+    return a.value, b.value
+
+
+def sparse_attn_info():
+    g, v = ctypes.c_int32(), ctypes.c_int32()
+    _check(lib.sparse_attn_info(ctypes.byref(g), ctypes.byref(v)), "sparse_attn_info")
+    return g.value, v.value
+
+
+def make_mask(kept_idx, kept_cnt, block_prob=None) -> SaMask:
+    return SaMask(_ptr(kept_idx), _ptr(kept_cnt), _ptr(block_prob))
+
+
+def sparse_attn_predict(p: SaParams, q, k, mask: SaMask, ws, stream=None, ws_bytes=None):
+    """Stage one.  ``q``, ``k``: device tensors; ``mask``: SaMask over device
+    int32 buffers; ``ws``: device buffer of sparse_attn_workspace_size()[0]
+    bytes."""
+    nb = _nbytes(ws) if ws_bytes is None else ws_bytes
+    _check(lib.sparse_attn_predict(ctypes.byref(p), _ptr(q), _ptr(k), ctypes.byref(mask),
+                                   _ptr(ws), nb, _stream(stream)), "sparse_attn_predict")
+
+
+def sparse_attn_forward(p: SaParams, q, k, v, mask: SaMask, o, lse=None, skip_bits=None,
+                        ws=None, stream=None, ws_bytes=None):
+    """Stage two.  Writes ``o`` (and ``lse`` / ``skip_bits`` when given)."""
+    nb = _nbytes(ws) if ws_bytes is None else ws_bytes
+    _check(lib.sparse_attn_forward(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v),
+                                   ctypes.byref(mask), _ptr(o), _ptr(lse), _ptr(skip_bits),
+                                   _ptr(ws), nb, _stream(stream)), "sparse_attn_forward")
+
+
+__all__ = [
+    "SaParams", "SaMask", "SparseAttnError", "make_params", "make_mask",
+    "sparse_attn_mask_shape", "sparse_attn_workspace_size", "sparse_attn_predict",
+    "sparse_attn_forward", "sparse_attn_info", "sparse_attn_status_str",
+    "sparse_attn_last_error", "lib", "LIB_PATH", "HEADER",
+]

@@ -1,0 +1,248 @@
+// Host side of the C ABI declared in include/sparse_attn.h: argument
+// validation, workspace layout, launch of the gfx950 kernels on the caller's
+// stream, and error reporting.  Nothing is enqueued unless every check
+// passes; no exception crosses the ABI.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "sa_internal.h"
+#include "../../include/sparse_attn.h"
+
+namespace {
+
+thread_local char g_err[512];
+
+sa_status fail(sa_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+sa_status ok() {
+  g_err[0] = 0;
+  return SA_OK;
+}
+
+constexpr size_t kAlign = 256;
+size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Validates the parameter block and fills the geometry.  `empty` is set for
+// problems with B, H or N equal to zero.
+sa_status check_params(const sa_params* p, sa::Geometry* g, bool* empty) {
+  if (!p) return fail(SA_ERR_INVALID_ARG, "params is NULL");
+  if (p->B < 0 || p->H < 0 || p->N < 0 || p->D <= 0)
+    return fail(SA_ERR_INVALID_ARG, "negative shape (B=%d H=%d N=%d D=%d)", p->B, p->H, p->N, p->D);
+  if (p->D != 64 && p->D != 128) return fail(SA_ERR_UNSUPPORTED, "D=%d (supported: 64, 128)", p->D);
+  if (p->block_q != 128 || p->block_k != 64)
+    return fail(SA_ERR_UNSUPPORTED, "block sizes %dx%d (supported: 128x64)", p->block_q, p->block_k);
+  if (p->dtype != SA_F32 && p->dtype != SA_BF16) return fail(SA_ERR_INVALID_ARG, "dtype=%d", p->dtype);
+  if (p->prec != SA_PREC_NATIVE && p->prec != SA_PREC_I8_FP8)
+    return fail(SA_ERR_INVALID_ARG, "prec=%d", p->prec);
+  if (p->prec == SA_PREC_I8_FP8 && (p->dtype != SA_BF16 || p->D != 128))
+    return fail(SA_ERR_UNSUPPORTED, "INT8/FP8 variant needs bf16 inputs and D=128");
+  if (p->rule != SA_RULE_TOPCDF && p->rule != SA_RULE_ENERGY)
+    return fail(SA_ERR_INVALID_ARG, "rule=%d", p->rule);
+  if (p->causal != 0 && p->causal != 1) return fail(SA_ERR_INVALID_ARG, "causal=%d", p->causal);
+  if (!(p->tau > 0.f) || std::isnan(p->tau))
+    return fail(SA_ERR_INVALID_ARG, "tau=%g (must be in (0, 1]; >= 1 keeps all)", (double)p->tau);
+  if (std::isnan(p->lambda)) return fail(SA_ERR_INVALID_ARG, "lambda is NaN");
+  if (!(p->sm_scale >= 0.f) || std::isinf(p->sm_scale))
+    return fail(SA_ERR_INVALID_ARG, "sm_scale=%g", (double)p->sm_scale);
+  if (p->keep_prefix_kblocks < 0) return fail(SA_ERR_INVALID_ARG, "keep_prefix_kblocks < 0");
+  if (p->lambda_group_rows != 0 && p->lambda_group_rows != 32)
+    return fail(SA_ERR_UNSUPPORTED, "lambda_group_rows=%d (supported: 32)", p->lambda_group_rows);
+  if (p->N > 262144) return fail(SA_ERR_UNSUPPORTED, "N=%d > 262144", p->N);
+  if (p->o_fp32 != 0 && p->o_fp32 != 1) return fail(SA_ERR_INVALID_ARG, "o_fp32=%d", p->o_fp32);
+  const int64_t esz = p->dtype == SA_BF16 ? 2 : 4;
+  g->B = p->B;
+  g->H = p->H;
+  g->N = p->N;
+  g->D = p->D;
+  g->nqb = (p->N + 127) / 128;
+  g->nkb = (p->N + 63) / 64;
+  g->dtype = p->dtype;
+  g->sn = p->stride_n ? p->stride_n : p->D;
+  g->sh = p->stride_h ? p->stride_h : (int64_t)p->N * g->sn;
+  g->sb = p->stride_b ? p->stride_b : (int64_t)p->H * g->sh;
+  if (g->sn < p->D || g->sh < 0 || g->sb < 0)
+    return fail(SA_ERR_INVALID_ARG, "strides (b=%lld h=%lld n=%lld) do not fit D=%d",
+                (long long)g->sb, (long long)g->sh, (long long)g->sn, p->D);
+  if ((g->sn * esz) % 16 || (g->sh * esz) % 16 || (g->sb * esz) % 16)
+    return fail(SA_ERR_INVALID_ARG, "strides must keep rows 16-byte aligned");
+  *empty = p->B == 0 || p->H == 0 || p->N == 0;
+  const int64_t wgs = (int64_t)p->B * p->H * (g->nqb + g->nkb);
+  if (wgs > 0x7fffffffLL) return fail(SA_ERR_UNSUPPORTED, "problem too large for one grid");
+  return SA_OK;
+}
+
+struct PredictLayout {
+  size_t qbar, kbar, total;
+};
+PredictLayout predict_layout(const sa::Geometry& g) {
+  PredictLayout L;
+  L.qbar = 0;
+  L.kbar = round_up((size_t)g.B * g.H * g.nqb * g.D * sizeof(float));
+  L.total = L.kbar + round_up((size_t)g.B * g.H * g.nkb * g.D * sizeof(float));
+  return L;
+}
+
+struct ForwardLayout {
+  size_t qc, kc, vt, sq, sk, sv, total;
+};
+ForwardLayout forward_layout(const sa::Geometry& g, int prec) {
+  ForwardLayout L{};
+  if (prec != SA_PREC_I8_FP8) return L;
+  const size_t bh = (size_t)g.B * g.H;
+  L.qc = 0;
+  L.kc = L.qc + round_up(bh * g.N * g.D);
+  L.vt = L.kc + round_up(bh * g.N * g.D);
+  L.sq = L.vt + round_up(bh * g.nkb * g.D * 64);
+  L.sk = L.sq + round_up(bh * g.nqb * sizeof(float));
+  L.sv = L.sk + round_up(bh * g.nkb * sizeof(float));
+  L.total = L.sv + round_up(bh * g.nkb * sizeof(float));
+  return L;
+}
+
+float softmax_scale(const sa_params* p) {
+  return p->sm_scale > 0.f ? p->sm_scale : 1.0f / sqrtf((float)p->D);
+}
+
+}  // namespace
+
+extern "C" {
+
+sa_status sparse_attn_mask_shape(const sa_params* p, int64_t* nqb, int64_t* nkb) {
+  sa::Geometry g;
+  bool empty;
+  sa_status st = check_params(p, &g, &empty);
+  if (st) return st;
+  if (nqb) *nqb = g.nqb;
+  if (nkb) *nkb = g.nkb;
+  return ok();
+}
+
+sa_status sparse_attn_workspace_size(const sa_params* p, size_t* predict_ws, size_t* forward_ws) {
+  sa::Geometry g;
+  bool empty;
+  sa_status st = check_params(p, &g, &empty);
+  if (st) return st;
+  if (predict_ws) *predict_ws = empty ? 0 : predict_layout(g).total;
+  if (forward_ws) *forward_ws = empty ? 0 : forward_layout(g, p->prec).total;
+  return ok();
+}
+
+sa_status sparse_attn_predict(const sa_params* p, const void* q, const void* k, const sa_mask* out,
+                              void* ws, size_t ws_bytes, void* stream) {
+  sa::Geometry g;
+  bool empty;
+  sa_status st = check_params(p, &g, &empty);
+  if (st) return st;
+  if (empty) return ok();
+  if (!q || !k) return fail(SA_ERR_INVALID_ARG, "q or k is NULL");
+  if (!aligned16(q) || !aligned16(k)) return fail(SA_ERR_INVALID_ARG, "q/k not 16-byte aligned");
+  if (!out || !out->kept_idx || !out->kept_cnt)
+    return fail(SA_ERR_INVALID_ARG, "mask output (kept_idx, kept_cnt) is NULL");
+  const PredictLayout L = predict_layout(g);
+  if (!ws || ws_bytes < L.total)
+    return fail(SA_ERR_WORKSPACE, "predict workspace %zu < %zu bytes", ws_bytes, L.total);
+  if (!aligned16(ws)) return fail(SA_ERR_INVALID_ARG, "workspace not 16-byte aligned");
+  sa::PredictLaunch a;
+  a.g = g;
+  a.q = q;
+  a.k = k;
+  a.qbar = reinterpret_cast<float*>(static_cast<char*>(ws) + L.qbar);
+  a.kbar = reinterpret_cast<float*>(static_cast<char*>(ws) + L.kbar);
+  a.kept_idx = out->kept_idx;
+  a.kept_cnt = out->kept_cnt;
+  a.block_prob = out->block_prob;
+  a.causal = p->causal;
+  a.rule = p->rule;
+  a.keep_prefix = p->keep_prefix_kblocks;
+  a.sm = softmax_scale(p);
+  a.tau = p->tau;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = sa::launch_pool(a, s);
+  if (e != hipSuccess) return fail(SA_ERR_HIP, "pool launch: %s", hipGetErrorString(e));
+  e = sa::launch_mask(a, s);
+  if (e != hipSuccess) return fail(SA_ERR_HIP, "mask launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+sa_status sparse_attn_forward(const sa_params* p, const void* q, const void* k, const void* v,
+                              const sa_mask* mask, void* o, float* lse, uint32_t* skip_bits,
+                              void* ws, size_t ws_bytes, void* stream) {
+  sa::Geometry g;
+  bool empty;
+  sa_status st = check_params(p, &g, &empty);
+  if (st) return st;
+  if (empty) return ok();
+  if (!q || !k || !v || !o) return fail(SA_ERR_INVALID_ARG, "q, k, v or o is NULL");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
+    return fail(SA_ERR_INVALID_ARG, "q/k/v/o not 16-byte aligned");
+  if (!mask || !mask->kept_idx || !mask->kept_cnt)
+    return fail(SA_ERR_INVALID_ARG, "mask (kept_idx, kept_cnt) is NULL");
+  const ForwardLayout L = forward_layout(g, p->prec);
+  if (L.total && (!ws || ws_bytes < L.total))
+    return fail(SA_ERR_WORKSPACE, "forward workspace %zu < %zu bytes", ws_bytes, L.total);
+  if (L.total && !aligned16(ws)) return fail(SA_ERR_INVALID_ARG, "workspace not 16-byte aligned");
+  sa::ForwardLaunch a{};
+  a.g = g;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  a.skip_bits = skip_bits;
+  a.kept_idx = mask->kept_idx;
+  a.kept_cnt = mask->kept_cnt;
+  a.causal = p->causal;
+  a.sm = softmax_scale(p);
+  a.lambda = p->lambda;
+  a.o_fp32 = p->o_fp32 || p->dtype == SA_F32;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  if (p->prec == SA_PREC_I8_FP8) {
+    char* w = static_cast<char*>(ws);
+    a.qc = reinterpret_cast<int8_t*>(w + L.qc);
+    a.kc = reinterpret_cast<int8_t*>(w + L.kc);
+    a.vt = reinterpret_cast<uint8_t*>(w + L.vt);
+    a.sq = reinterpret_cast<float*>(w + L.sq);
+    a.sk = reinterpret_cast<float*>(w + L.sk);
+    a.sv = reinterpret_cast<float*>(w + L.sv);
+    e = sa::launch_quant(a, s);
+    if (e != hipSuccess) return fail(SA_ERR_HIP, "quantise launch: %s", hipGetErrorString(e));
+    e = sa::launch_attn_q(a, s);
+    if (e != hipSuccess) return fail(SA_ERR_HIP, "attention (int8/fp8) launch: %s", hipGetErrorString(e));
+  } else {
+    e = sa::launch_attn(a, s);
+    if (e != hipSuccess) return fail(SA_ERR_HIP, "attention launch: %s", hipGetErrorString(e));
+  }
+  return ok();
+}
+
+sa_status sparse_attn_info(int32_t* default_group_rows, int32_t* version) {
+  if (default_group_rows) *default_group_rows = 32;
+  if (version) *version = SPARSE_ATTN_VERSION;
+  return ok();
+}
+
+const char* sparse_attn_status_str(int32_t status) {
+  switch (status) {
+    case SA_OK: return "SA_OK";
+    case SA_ERR_INVALID_ARG: return "SA_ERR_INVALID_ARG";
+    case SA_ERR_UNSUPPORTED: return "SA_ERR_UNSUPPORTED";
+    case SA_ERR_WORKSPACE: return "SA_ERR_WORKSPACE";
+    case SA_ERR_HIP: return "SA_ERR_HIP";
+    default: return "SA_ERR_UNKNOWN";
+  }
+}
+
+const char* sparse_attn_last_error(void) { return g_err; }
+
+}  // extern "C"

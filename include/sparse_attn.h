@@ -1,0 +1,188 @@
+/*
+ * sparse_attn.h -- C ABI of the block-sparse attention library for MI355X
+ * (gfx950).  Training-free block-sparse attention in two calls:
+ *
+ *   sparse_attn_predict   stage one: block-mean pooled Q and K, a compressed
+ *                         Q.K^T that predicts the block attention map, and a
+ *                         per-query-block cumulative-mass mask written as a
+ *                         kept-block list per query block.
+ *   sparse_attn_forward   stage two: block-sparse flash attention over the
+ *                         kept lists, skipping a tile's P.V product for a
+ *                         group of rows when the tile cannot matter there
+ *                         (the softmax-aware lambda test inside the online
+ *                         softmax).  Native precision (bf16 / fp32) or the
+ *                         quantised variant (INT8 Q.K^T, FP8 e4m3 P.V).
+ *
+ * Sources: the SpargeAttn abstract (taxoreview.com page; also on the
+ * huggingface-mirror search page) defines the two-stage online filter --
+ * predict the attention map to skip products, then an online softmax-aware
+ * filter that skips more -- and calls the attention quantized.  The iCATS
+ * abstract (arxivdaily.com page) describes the pipeline as estimating the
+ * importance of query-key regions, deriving a sparse mask and computing only
+ * the important candidates, with a top-p rule.  The DynSparse story
+ * (embedding.report page) adds the cumulative-energy threshold and notes
+ * that masks can be precomputed, which is why the mask is an explicit,
+ * reusable object passed between the two calls.
+ *
+ * Conventions for every entry point
+ * ---------------------------------
+ * - Device pointers unless marked "host".  Q, K, V, O are [B, H, N, D]
+ *   tensors of `dtype` with D contiguous (O is fp32 when o_fp32 is set);
+ *   element strides of the B, H and N dimensions come from sa_params
+ *   (0 = packed B,H,N,D).  All four share the strides, counted in elements
+ *   of their own type.  Base pointers must be 16-byte aligned and strides must
+ *   keep every row 16-byte aligned.
+ * - The caller owns every buffer (inputs, outputs, mask, workspace).  The
+ *   library allocates no device memory and keeps no pointer after a call
+ *   returns.  Calls are asynchronous on `stream` (a hipStream_t passed as
+ *   void*; NULL = the default stream).
+ * - Arguments are validated on the host before anything is enqueued.  On
+ *   any error nothing is enqueued and the call returns a non-zero sa_status;
+ *   sparse_attn_last_error() then returns a message (thread-local).
+ *   SA_ERR_HIP reports a failed kernel launch.  No C++ exception crosses the
+ *   ABI.  NaN/Inf inside Q, K, V are not checked and propagate.
+ * - An empty problem (B, H or N equal to 0) is valid and enqueues nothing.
+ * - Supported: D in {64, 128}; block_q = 128, block_k = 64; lambda group of
+ *   32 rows (one wavefront's rows); N <= 262144 (4096 key blocks).  The
+ *   quantised variant needs dtype = SA_BF16 and D = 128.  Anything else
+ *   returns SA_ERR_UNSUPPORTED.
+ */
+#ifndef SPARSE_ATTN_H
+#define SPARSE_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SPARSE_ATTN_VERSION 1
+
+#if defined(__GNUC__)
+#define SA_API __attribute__((visibility("default")))
+#else
+#define SA_API
+#endif
+
+typedef enum sa_status {
+  SA_OK = 0,
+  SA_ERR_INVALID_ARG = 1,   /* bad pointer, shape, stride or parameter     */
+  SA_ERR_UNSUPPORTED = 2,   /* valid but not implemented (D, block sizes)  */
+  SA_ERR_WORKSPACE = 3,     /* workspace missing or smaller than required  */
+  SA_ERR_HIP = 4            /* the HIP runtime reported a launch failure   */
+} sa_status;
+
+/* Storage type of Q, K, V and O. */
+enum { SA_F32 = 0, SA_BF16 = 1 };
+/* Arithmetic of stage two: native (bf16 MFMA / fp32 MFMA) or INT8 Q.K^T with
+ * FP8 e4m3 P.V (per-block scales: Q and K absmax/127, V absmax/448 per key
+ * block; P pre-scaled by 2^8). */
+enum { SA_PREC_NATIVE = 0, SA_PREC_I8_FP8 = 1 };
+/* Mask rule of stage one.  TOPCDF: P-hat = softmax of the block scores over
+ * the admissible key blocks.  ENERGY: P-hat_j proportional to
+ * n_j * exp(s_j), n_j the number of keys in block j (a cumulative-energy
+ * target; equal to TOPCDF when every block is full). */
+enum { SA_RULE_TOPCDF = 0, SA_RULE_ENERGY = 1 };
+
+typedef struct sa_params {
+  int32_t B, H, N, D;          /* batch, heads, tokens, head dimension         */
+  int32_t block_q, block_k;    /* query / key block rows: 128 and 64           */
+  int32_t causal;              /* 1: key c visible to row r only if c <= r     */
+  int32_t dtype;               /* SA_F32 | SA_BF16                             */
+  int32_t prec;                /* SA_PREC_NATIVE | SA_PREC_I8_FP8              */
+  int32_t rule;                /* SA_RULE_TOPCDF | SA_RULE_ENERGY              */
+  float tau;                   /* cumulative-mass target in (0, 1]; >= 1 keeps */
+                               /* every admissible block                       */
+  float lambda;                /* skip threshold, natural-log units of the     */
+                               /* scaled logits; -INFINITY never skips; NaN is */
+                               /* invalid                                      */
+  float sm_scale;              /* softmax scale; 0 -> 1/sqrt(D)                */
+  int32_t keep_prefix_kblocks; /* leading key blocks that are always kept      */
+  int32_t lambda_group_rows;   /* rows per skip group; 0 -> 32; only 32        */
+  int32_t o_fp32;              /* 1: O is written as fp32 whatever `dtype` is; */
+                               /* 0: O has `dtype` (bf16 O = the fp32 result  */
+                               /* rounded to nearest even)                    */
+  int64_t stride_b, stride_h, stride_n;  /* element strides; 0 -> packed       */
+} sa_params;
+
+/* The mask: output of predict, input of forward.  Caller-allocated; sizes
+ * from sparse_attn_mask_shape().
+ *   kept_idx   int32 [B, H, NQB, NKB]: for query block i the first
+ *              kept_cnt[b,h,i] entries are the kept key blocks in processing
+ *              order (forced blocks first, then predicted score descending,
+ *              then index ascending); later entries are not written.
+ *   kept_cnt   int32 [B, H, NQB].
+ *   block_prob optional float [B, H, NQB, NKB] predicted map P-hat in key
+ *              block order (0 for inadmissible blocks); NULL skips it. */
+typedef struct sa_mask {
+  int32_t* kept_idx;
+  int32_t* kept_cnt;
+  float* block_prob;
+} sa_mask;
+
+/* Host.  NQB = ceil(N / block_q), NKB = ceil(N / block_k). */
+SA_API sa_status sparse_attn_mask_shape(const sa_params* p, int64_t* nqb, int64_t* nkb);
+
+/* Host.  Workspace bytes needed by predict and by forward (either output
+ * pointer may be NULL).  Layouts (offsets rounded up to 256 bytes):
+ *   predict: qbar float [B,H,NQB,D], then kbar float [B,H,NKB,D] -- the
+ *            block means, left in place after the call.
+ *   forward, SA_PREC_I8_FP8: Q codes int8 [B,H,N,D], K codes int8 [B,H,N,D],
+ *            V codes e4m3 [B,H,NKB,D,64] (each key block stored transposed:
+ *            byte (d, c) holds key j*64 + c), then float scales
+ *            sq [B,H,NQB], sk [B,H,NKB], sv [B,H,NKB].
+ *   forward, SA_PREC_NATIVE: 0 bytes. */
+SA_API sa_status sparse_attn_workspace_size(const sa_params* p, size_t* predict_ws,
+                                     size_t* forward_ws);
+
+/* Stage one.  Reads Q and K; writes out->kept_idx, out->kept_cnt and, if
+ * non-NULL, out->block_prob.  Steps, per (b, h):
+ *   block means qbar_i (query block rows valid only) and kbar_j;
+ *   admissible key blocks A_i (all; causal: first key <= last row of R_i);
+ *   scores s_ij = sm * qbar_i . kbar_j  (fp32 means, fp64 dot product);
+ *   weights P-hat per `rule`, in fp64;
+ *   forced blocks F_i: j < keep_prefix_kblocks, and under causality the key
+ *   blocks that reach the query block's diagonal;
+ *   order: forced first, s descending, j ascending;
+ *   cut: the shortest prefix whose fp64 running sum of P-hat reaches tau,
+ *   never fewer than |F_i|; tau >= 1 keeps all of A_i.
+ * `ws` must hold the predict workspace. */
+SA_API sa_status sparse_attn_predict(const sa_params* p, const void* q, const void* k,
+                              const sa_mask* out, void* ws, size_t ws_bytes,
+                              void* stream);
+
+/* Stage two.  For each query block, processes mask->kept_idx in list order
+ * with an online softmax (running max m, running sum l).  For each group of
+ * 32 consecutive rows (one wavefront), delta = max over the group's rows of
+ * (tile max - new running max); when delta < lambda the group skips the
+ * tile's P.V product (m and l are still updated).  Writes
+ *   o          [B,H,N,D] dtype (fp32 if o_fp32): acc / l;
+ *   lse        optional float [B,H,N]: m + log(l) in natural-log units;
+ *   skip_bits  optional uint32 [B,H,NQB,4,ceil(NKB/32)]: bit (t % 32) of
+ *              word t / 32 of group g is 1 when group g skipped the P.V
+ *              product of list entry t; only words that cover entries
+ *              t < kept_cnt are written, with zero bits past kept_cnt.
+ * Every kept_idx entry must be an admissible key block for its query block
+ * (causal) and kept_cnt must lie in [1, NKB]; predict produces such masks.
+ * `ws` must hold the forward workspace (none for SA_PREC_NATIVE). */
+SA_API sa_status sparse_attn_forward(const sa_params* p, const void* q, const void* k,
+                              const void* v, const sa_mask* mask, void* o,
+                              float* lse, uint32_t* skip_bits, void* ws,
+                              size_t ws_bytes, void* stream);
+
+/* Host.  Library defaults and version (either pointer may be NULL). */
+SA_API sa_status sparse_attn_info(int32_t* default_group_rows, int32_t* version);
+
+/* Host.  Static string naming a status code. */
+SA_API const char* sparse_attn_status_str(int32_t status);
+
+/* Host.  Message describing the last failed call on this thread ("" if the
+ * last call succeeded).  Valid until the next call on this thread. */
+SA_API const char* sparse_attn_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPARSE_ATTN_H */

@@ -101,11 +101,13 @@ def fp8_quantize_v_blocks(V, bk: int):
 
 
 def sparse_attention_quant_head(Q, K, V, kept: List[np.ndarray], p: Params,
-                                force_skip: Optional[List[np.ndarray]] = None):
+                                force_skip: Optional[List[np.ndarray]] = None,
+                                deltas: Optional[list] = None):
     """Quantised stage two: the same online softmax, processing order and
     skip rule as the unquantised oracle, with
     S = sm * s_q(i) * s_k(j) * (Qcode . Kcode)  (exact integer dot product) and
     the P.V term  s_v(j) * 2^-8 * sum_c e4m3(2^8 * P) * Vcode.
+    ``deltas`` collects delta_g as in the unquantised oracle.
     Returns (O, lse, skips)."""
     N, d = np.asarray(Q).shape
     sm = p.sm(d)
@@ -126,6 +128,7 @@ def sparse_attention_quant_head(Q, K, V, kept: List[np.ndarray], p: Params,
         l = np.zeros(nr)
         acc = np.zeros((nr, d))
         sk = np.zeros((len(lst), n_groups), dtype=bool)
+        dl = np.full((len(lst), n_groups), -np.inf)
         for t, j in enumerate(lst):
             cols = np.arange(j * p.BK, min(N, (j + 1) * p.BK))
             idot = qc[rows] @ kc[cols].T               # exact in int64
@@ -146,6 +149,7 @@ def sparse_attention_quant_head(Q, K, V, kept: List[np.ndarray], p: Params,
             for g in range(n_groups):
                 gr = slice(g * p.G, min(nr, (g + 1) * p.G))
                 dg = delta_r[gr].max() if gr.start < nr else -np.inf
+                dl[t, g] = dg
                 skip = bool(dg < lam)
                 if force_skip is not None:
                     skip = bool(force_skip[i][t, g])
@@ -154,6 +158,8 @@ def sparse_attention_quant_head(Q, K, V, kept: List[np.ndarray], p: Params,
                     acc[gr] += float(vs[j]) * (Pq[gr] @ vq[cols])
             m = mnew
         skips.append(sk)
+        if deltas is not None:
+            deltas.append(dl)
         ok = l > 0
         O[rows[ok]] = acc[ok] / l[ok, None]
         lse[rows[ok]] = m[ok] + np.log(l[ok])

@@ -207,13 +207,16 @@ def predict_head(Q: np.ndarray, K: np.ndarray, p: Params) -> dict:
 
 # --------------------------------------------------------------------- O8
 def sparse_attention_head(Q, K, V, kept: List[np.ndarray], p: Params,
-                          force_skip: Optional[List[np.ndarray]] = None):
+                          force_skip: Optional[List[np.ndarray]] = None,
+                          deltas: Optional[list] = None):
     """O8: block-sparse online-softmax attention with the per-group skip.
 
     ``kept[i]`` lists key blocks for query block i in processing order.
     ``force_skip[i]`` (bool [len(kept[i]), n_groups]) replaces the skip
-    decision when given.  Returns (O [N,d], lse [N] natural log,
-    skips: list of bool [len(kept[i]), n_groups]).
+    decision when given.  If ``deltas`` is a list, the group statistics
+    delta_g (float [len(kept[i]), n_groups]) are appended to it.  Returns
+    (O [N,d], lse [N] natural log, skips: list of bool
+    [len(kept[i]), n_groups]).
     """
     Q = np.asarray(Q, dtype=np.float64)
     K = np.asarray(K, dtype=np.float64)
@@ -232,6 +235,7 @@ def sparse_attention_head(Q, K, V, kept: List[np.ndarray], p: Params,
         l = np.zeros(nr)
         acc = np.zeros((nr, d))
         sk = np.zeros((len(lst), n_groups), dtype=bool)
+        dl = np.full((len(lst), n_groups), -np.inf)
         for t, j in enumerate(lst):
             cols = np.arange(j * p.BK, min(N, (j + 1) * p.BK))
             S = sm * (Q[rows] @ K[cols].T)
@@ -250,6 +254,7 @@ def sparse_attention_head(Q, K, V, kept: List[np.ndarray], p: Params,
             for g in range(n_groups):
                 gr = slice(g * p.G, min(nr, (g + 1) * p.G))
                 dg = delta_r[gr].max() if gr.start < nr else -np.inf
+                dl[t, g] = dg
                 skip = bool(dg < lam)
                 if force_skip is not None:
                     skip = bool(force_skip[i][t, g])
@@ -258,6 +263,8 @@ def sparse_attention_head(Q, K, V, kept: List[np.ndarray], p: Params,
                     acc[gr] += P[gr] @ V[cols]
             m = mnew
         skips.append(sk)
+        if deltas is not None:
+            deltas.append(dl)
         ok = l > 0
         O[rows[ok]] = acc[ok] / l[ok, None]
         lse[rows[ok]] = m[ok] + np.log(l[ok])

@@ -1,0 +1,120 @@
+"""CPU checks of the C-ABI library: it loads, exports every function that
+include/sparse_attn.h declares, and its host-only entry points (shapes,
+workspace sizes, info, status strings) and argument validation work
+without a GPU.  Validation failures return before anything is enqueued, so
+the fake device pointers used here are never dereferenced."""
+import ctypes
+import math
+import re
+
+import pytest
+
+import block_mean_pool_amd as sa
+
+
+def declared_functions():
+    text = open(sa.HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sparse_attn_\w+)\s*\(", text)))
+
+
+def test_exports_every_declared_function():
+    names = declared_functions()
+    assert {"sparse_attn_predict", "sparse_attn_forward"} <= set(names)
+    for n in names:
+        assert hasattr(sa.lib, n), n
+
+
+def test_binding_exposes_the_same_names():
+    for n in declared_functions():
+        assert callable(getattr(sa, n)), n
+
+
+def test_struct_layout_matches_header():
+    # 10 int32 + 3 float + 3 int32 = 64 bytes, + 3 int64
+    assert ctypes.sizeof(sa.SaParams) == 88
+    assert sa.SaParams.stride_b.offset == 64
+    assert ctypes.sizeof(sa.SaMask) == 24
+
+
+def test_shapes_and_workspace():
+    p = sa.make_params(1, 40, 32760, 128)
+    assert sa.sparse_attn_mask_shape(p) == (256, 512)
+    pw, fw = sa.sparse_attn_workspace_size(p)
+    assert pw == 40 * 256 * 128 * 4 + 40 * 512 * 128 * 4
+    assert fw == 0
+    q = sa.make_params(1, 16, 65536, 128, prec="i8fp8", rule="energy")
+    _, fw = sa.sparse_attn_workspace_size(q)
+    bh = 16
+    assert fw == 2 * bh * 65536 * 128 + bh * 1024 * 128 * 64 + bh * 512 * 4 + 2 * bh * 1024 * 4
+    assert sa.sparse_attn_info() == (32, 1)
+    assert sa.sparse_attn_status_str(3) == "SA_ERR_WORKSPACE"
+    assert sa.sparse_attn_status_str(99) == "SA_ERR_UNKNOWN"
+    p = sa.make_params(2, 3, 0, 64)
+    assert sa.sparse_attn_mask_shape(p) == (0, 0)
+    assert sa.sparse_attn_workspace_size(p) == (0, 0)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(D=96), sa.SA_ERR_UNSUPPORTED),
+    (dict(block_q=64), sa.SA_ERR_UNSUPPORTED),
+    (dict(tau=0.0), sa.SA_ERR_INVALID_ARG),
+    (dict(tau=float("nan")), sa.SA_ERR_INVALID_ARG),
+    (dict(lam=float("nan")), sa.SA_ERR_INVALID_ARG),
+    (dict(sm_scale=-1.0), sa.SA_ERR_INVALID_ARG),
+    (dict(lambda_group_rows=16), sa.SA_ERR_UNSUPPORTED),
+    (dict(prec="i8fp8", dtype="f32"), sa.SA_ERR_UNSUPPORTED),
+    (dict(keep_prefix_kblocks=-1), sa.SA_ERR_INVALID_ARG),
+    (dict(N=300000), sa.SA_ERR_UNSUPPORTED),
+    (dict(strides=(0, 0, 100)), sa.SA_ERR_INVALID_ARG),
+    (dict(strides=(0, 0, 130)), sa.SA_ERR_INVALID_ARG),
+])
+def test_invalid_params_rejected_before_launch(kw, code):
+    base = dict(B=1, H=2, N=1000, D=128)
+    shape = {k: kw.pop(k) for k in list(kw) if k in base}
+    base.update(shape)
+    p = sa.make_params(base["B"], base["H"], base["N"], base["D"], **kw)
+    fake = 1 << 20  # never dereferenced: validation fails first
+    mask = sa.make_mask(fake, fake)
+    with pytest.raises(sa.SparseAttnError) as e:
+        sa.sparse_attn_predict(p, fake, fake, mask, fake, ws_bytes=1 << 40, stream=0)
+    assert e.value.code == code
+    assert sa.sparse_attn_last_error()
+    with pytest.raises(sa.SparseAttnError) as e:
+        sa.sparse_attn_forward(p, fake, fake, fake, mask, fake, ws=fake, ws_bytes=1 << 40,
+                               stream=0)
+    assert e.value.code == code
+
+
+def test_null_and_workspace_errors():
+    p = sa.make_params(1, 2, 1000, 128)
+    fake = 1 << 20
+    with pytest.raises(sa.SparseAttnError) as e:
+        sa.sparse_attn_predict(p, None, fake, sa.make_mask(fake, fake), fake, ws_bytes=1 << 30,
+                               stream=0)
+    assert e.value.code == sa.SA_ERR_INVALID_ARG
+    with pytest.raises(sa.SparseAttnError) as e:
+        sa.sparse_attn_predict(p, fake, fake, sa.make_mask(None, fake), fake, ws_bytes=1 << 30,
+                               stream=0)
+    assert e.value.code == sa.SA_ERR_INVALID_ARG
+    with pytest.raises(sa.SparseAttnError) as e:
+        sa.sparse_attn_predict(p, fake, fake, sa.make_mask(fake, fake), fake, ws_bytes=16,
+                               stream=0)
+    assert e.value.code == sa.SA_ERR_WORKSPACE
+    with pytest.raises(sa.SparseAttnError) as e:
+        sa.sparse_attn_predict(p, fake + 2, fake, sa.make_mask(fake, fake), fake,
+                               ws_bytes=1 << 30, stream=0)
+    assert e.value.code == sa.SA_ERR_INVALID_ARG
+    q = sa.make_params(1, 2, 1000, 128, prec="i8fp8")
+    with pytest.raises(sa.SparseAttnError) as e:
+        sa.sparse_attn_forward(q, fake, fake, fake, sa.make_mask(fake, fake), fake, ws=None,
+                               ws_bytes=0, stream=0)
+    assert e.value.code == sa.SA_ERR_WORKSPACE
+
+
+def test_empty_problem_is_ok_without_pointers():
+    p = sa.make_params(0, 4, 100, 128)
+    sa.sparse_attn_predict(p, None, None, sa.make_mask(None, None), None, stream=0)
+    sa.sparse_attn_forward(p, None, None, None, sa.make_mask(None, None), None, stream=0)
+    assert sa.sparse_attn_last_error() == ""
+    assert not math.isnan(0.0)

@@ -1,0 +1,219 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 oracle, on
+seeded inputs small enough for the oracle (seconds) that still span several
+tiles and ragged tails.
+
+Bars:
+  * block means: |gpu - oracle| <= 1e-5 * |oracle| + 1e-6 (fp32 accumulate);
+  * P-hat: |gpu - oracle| <= 1e-6;
+  * masks: bit-exact kept lists except the near-threshold / near-tie rules
+    in tests/compare.py;
+  * skip bits: exact except groups with |delta - lambda| <= 1e-3 (bf16),
+    1e-4 (fp32), 1e-3 (INT8);
+  * outputs: max-abs vs the oracle under the GPU's own mask and skip bits
+    <= 1e-2 (bf16, fp32) and <= 5e-2 (INT8/FP8), measured on the fp32 output
+    the kernel computes (o_fp32); the bf16-stored output must equal that
+    result rounded to nearest even, bit for bit (the storage rounding alone
+    is up to half a bf16 ulp, 0.0078 at |O| in [2, 4), so it is checked
+    exactly rather than folded into the tolerance); lse within 1e-3.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():  # pragma: no cover
+    pytest.skip("no GPU", allow_module_level=True)
+
+import oracle as O  # noqa: E402
+from synth import Workload, make_workload, round_to_bf16  # noqa: E402
+import compare  # noqa: E402
+import gpu_harness  # noqa: E402
+
+OUT_TOL = {"bf16": 1e-2, "f32": 1e-2, "i8fp8": 5e-2}
+SKIP_TOL = {"bf16": 1e-3, "f32": 1e-4, "i8fp8": 1e-3}
+
+
+def log(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def stacked(w: Workload):
+    heads = [(b, h) for b in range(w.B) for h in range(w.H)]
+    qs, ks, vs = zip(*(w.head(b, h) for b, h in heads))
+    shape = (w.B, w.H, w.N, w.D)
+    return (np.stack(qs).reshape(shape), np.stack(ks).reshape(shape),
+            np.stack(vs).reshape(shape))
+
+
+def check_case(w: Workload, layout="bhnd", check_out=True):
+    log(f"[case] {w.name} B={w.B} H={w.H} N={w.N} D={w.D} {w.dtype} causal={w.causal} "
+        f"tau={w.tau} lam={w.lam} rule={w.rule} prec={w.prec} kp={w.keep_prefix_kblocks} "
+        f"layout={layout}")
+    Q, K, V = stacked(w)
+    tau32 = float(np.float32(w.tau))
+    lam32 = float(np.float32(w.lam))
+    r = gpu_harness.run(Q, K, V, dtype=w.dtype, causal=w.causal, tau=w.tau, lam=w.lam,
+                        rule=w.rule, prec=w.prec, keep_prefix_kblocks=w.keep_prefix_kblocks,
+                        layout=layout)
+    p = O.Params(BQ=128, BK=64, causal=w.causal, tau=tau32, lam=lam32, rule=w.rule,
+                 keep_prefix_kblocks=w.keep_prefix_kblocks, G=32,
+                 sm_scale=float(np.float32(1.0 / math.sqrt(w.D))))
+    mode = w.prec if w.prec == "i8fp8" else w.dtype
+    worst = 0.0
+    n_rows = n_exact = 0
+    skip_n = skip_mis = 0
+    for b in range(w.B):
+        for h in range(w.H):
+            hid = b * w.H + h
+            q, k, v = Q[b, h], K[b, h], V[b, h]
+            pred = O.predict_head(q, k, p)
+            np.testing.assert_allclose(r["qbar"][b, h], pred["qbar"], rtol=1e-5, atol=1e-6)
+            np.testing.assert_allclose(r["kbar"][b, h], pred["kbar"], rtol=1e-5, atol=1e-6)
+            np.testing.assert_allclose(r["block_prob"][b, h], pred["P"], rtol=0, atol=1e-6)
+            n, ex, fails = compare.compare_masks([r["kept"][hid]], [pred], tau32)
+            assert not fails, f"mask mismatch head {hid}: {fails[:3]}"
+            n_rows += n
+            n_exact += ex
+            if not check_out:
+                continue
+            gk = r["kept"][hid]
+            deltas = []
+            if w.prec == "i8fp8":
+                _, _, osk = O.sparse_attention_quant_head(q, k, v, gk, p, deltas=deltas)
+            else:
+                _, _, osk = O.sparse_attention_head(q, k, v, gk, p, deltas=deltas)
+            gs = r["skips"][hid]
+            n, mis, sf = compare.compare_skips(gs, osk, deltas, lam32, SKIP_TOL[mode])
+            assert not sf, f"skip mismatch head {hid}: {sf[:3]}"
+            skip_n += n
+            skip_mis += mis
+            if w.prec == "i8fp8":
+                Oref, lse_ref, _ = O.sparse_attention_quant_head(q, k, v, gk, p, force_skip=gs)
+            else:
+                Oref, lse_ref, _ = O.sparse_attention_head(q, k, v, gk, p, force_skip=gs)
+            err = float(np.abs(r["O"][b, h] - Oref).max())
+            worst = max(worst, err)
+            assert err <= OUT_TOL[mode], f"head {hid}: max-abs {err}"
+            if w.dtype == "bf16":   # stored O = fp32 result rounded to bf16
+                np.testing.assert_array_equal(r["O_store"][b, h],
+                                              round_to_bf16(r["O"][b, h]))
+            fin = np.isfinite(lse_ref)
+            np.testing.assert_allclose(r["lse"][b, h][fin], lse_ref[fin], atol=1e-3, rtol=0)
+            if w.prec == "i8fp8":
+                qc, qs = O.int8_quantize_blocks(q, 128)
+                kc, ks = O.int8_quantize_blocks(k, 64)
+                np.testing.assert_array_equal(r["qc"][b, h], qc)
+                np.testing.assert_array_equal(r["kc"][b, h], kc)
+                np.testing.assert_array_equal(r["sq"][b, h], qs)
+                np.testing.assert_array_equal(r["sk"][b, h], ks)
+                vq, vs = O.fp8_quantize_v_blocks(v, 64)
+                np.testing.assert_array_equal(r["sv"][b, h], vs)
+                codes = np.zeros((r["nkb"] * 64, w.D), dtype=np.uint8)
+                codes[:w.N] = O.e4m3_encode(vq)
+                want = codes.reshape(r["nkb"], 64, w.D).transpose(0, 2, 1)
+                np.testing.assert_array_equal(r["vt"][b, h], want)
+    log(f"   masks {n_exact}/{n_rows} exact; skips {skip_mis}/{skip_n} near-lambda "
+        f"mismatches; max-abs {worst:.3g}")
+    return r
+
+
+def wl(name, index, B, H, N, D, dtype="bf16", structure="field", grid=None, **kw):
+    return Workload(name, index, B, H, N, D, dtype, structure=structure, grid=grid, **kw)
+
+
+CASES = [
+    make_workload("tiny_fp32"),
+    wl("field_ragged", 101, 2, 2, 1000, 128, grid=(10, 10, 10), tau=0.9, lam=-5.0),
+    wl("lm_causal_prefix", 102, 1, 2, 777, 128, structure="lm", causal=True, tau=0.95,
+       lam=-5.0, keep_prefix_kblocks=2),
+    wl("field_d64", 103, 1, 3, 515, 64, grid=(5, 103, 1), tau=0.8, lam=-2.0),
+    wl("energy_text", 104, 1, 2, 1064, 128, grid=(8, 10, 10), n_text=264, tau=0.95,
+       lam=-5.0, rule="energy", keep_prefix_kblocks=4),
+    wl("lam_zero", 105, 1, 2, 640, 128, grid=(4, 10, 16), tau=1.0, lam=0.0),
+    wl("fp32_causal_d128", 106, 1, 2, 333, 128, dtype="f32", structure="lm", causal=True,
+       tau=0.9, lam=-3.0),
+    wl("quant_energy", 107, 1, 2, 1000, 128, grid=(10, 10, 10), tau=0.95, lam=-5.0,
+       rule="energy", prec="i8fp8"),
+    wl("quant_causal", 108, 1, 1, 700, 128, structure="lm", causal=True, tau=0.9,
+       lam=-5.0, prec="i8fp8"),
+]
+
+
+@pytest.mark.parametrize("w", CASES, ids=[c.name for c in CASES])
+def test_parity_small(w):
+    check_case(w)
+
+
+def test_parity_strided_layout():
+    w = wl("strided_bnhd", 109, 2, 3, 600, 128, grid=(6, 10, 10), tau=0.9, lam=-5.0)
+    check_case(w, layout="bnhd")
+
+
+def test_dense_identity_on_gpu():
+    """tau = 1, lambda = -inf: every admissible block is kept and nothing is
+    skipped, so the GPU output equals dense softmax attention."""
+    for causal in (False, True):
+        w = wl("dense_identity", 110, 1, 2, 900, 128, structure="lm", causal=causal,
+               tau=1.0, lam=-math.inf)
+        log(f"[case] dense identity causal={causal}")
+        Q, K, V = stacked(w)
+        r = gpu_harness.run(Q, K, V, causal=causal, tau=1.0, lam=-math.inf)
+        for h in range(2):
+            adm = O.admissible_blocks(900, 128, 64, causal)
+            for i, lst in enumerate(r["kept"][h]):
+                assert sorted(lst.tolist()) == list(np.flatnonzero(adm[i]))
+            assert not any(s.any() for s in r["skips"][h])
+            od, lse_d = O.dense_attention_head(Q[0, h], K[0, h], V[0, h], 1 / math.sqrt(128), causal)
+            err = np.abs(r["O"][0, h] - od).max()
+            log(f"   head {h}: max-abs vs dense {err:.3g}")
+            assert err <= 1e-2
+            np.testing.assert_allclose(r["lse"][0, h], lse_d, atol=1e-3)
+
+
+def test_positive_lambda_zeroes_output():
+    w = wl("lam_pos", 111, 1, 2, 500, 128, grid=(5, 10, 10), tau=0.9, lam=0.5)
+    Q, K, V = stacked(w)
+    for prec in ("native", "i8fp8"):
+        log(f"[case] lambda > 0, {prec}")
+        r = gpu_harness.run(Q, K, V, tau=0.9, lam=0.5, prec=prec)
+        assert np.all(r["O"] == 0.0)
+        assert all(s.all() for hs in r["skips"] for s in hs)
+
+
+def test_deterministic_repeat():
+    w = wl("repeat", 112, 1, 4, 2000, 128, grid=(20, 10, 10), tau=0.9, lam=-5.0)
+    Q, K, V = stacked(w)
+    log("[case] determinism")
+    a = gpu_harness.run(Q, K, V, tau=0.9, lam=-5.0)
+    b = gpu_harness.run(Q, K, V, tau=0.9, lam=-5.0)
+    assert np.array_equal(a["O"], b["O"])
+    assert np.array_equal(a["kept_cnt"], b["kept_cnt"])
+    assert all(np.array_equal(x, y) for hx, hy in zip(a["kept"], b["kept"]) for x, y in zip(hx, hy))
+
+
+def test_empty_and_error_paths_on_gpu():
+    import block_mean_pool_amd as sa
+    log("[case] empty / error paths")
+    p = sa.make_params(1, 1, 0, 128)
+    assert sa.sparse_attn_mask_shape(p) == (0, 0)
+    assert sa.sparse_attn_workspace_size(p) == (0, 0)
+    mask = sa.make_mask(None, None)
+    sa.sparse_attn_predict(p, None, None, mask, None)      # empty: nothing enqueued
+    sa.sparse_attn_forward(p, None, None, None, mask, None)
+    p = sa.make_params(1, 2, 300, 128)
+    q = torch.zeros((1, 2, 300, 128), dtype=torch.bfloat16, device="cuda")
+    nqb, nkb = sa.sparse_attn_mask_shape(p)
+    idx = torch.zeros((1, 2, nqb, nkb), dtype=torch.int32, device="cuda")
+    cnt = torch.zeros((1, 2, nqb), dtype=torch.int32, device="cuda")
+    pws, _ = sa.sparse_attn_workspace_size(p)
+    small = torch.empty(pws - 1, dtype=torch.uint8, device="cuda")
+    with pytest.raises(sa.SparseAttnError) as e:
+        sa.sparse_attn_predict(p, q, q, sa.make_mask(idx, cnt), small)
+    assert e.value.code == sa.SA_ERR_WORKSPACE
+    torch.cuda.synchronize()
+    assert int(cnt.abs().sum()) == 0  # nothing ran
