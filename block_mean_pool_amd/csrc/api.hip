@@ -75,6 +75,9 @@ sa_status check_params(const sa_params* p, sa::Geometry* g, bool* empty) {
                 (long long)g->sb, (long long)g->sh, (long long)g->sn, p->D);
   if ((g->sn * esz) % 16 || (g->sh * esz) % 16 || (g->sb * esz) % 16)
     return fail(SA_ERR_INVALID_ARG, "strides must keep rows 16-byte aligned");
+  if ((int64_t)(p->N + 64) * g->sn * esz >= (1LL << 31))
+    return fail(SA_ERR_UNSUPPORTED, "one head spans >= 2 GiB (N=%d, stride_n=%lld)", p->N,
+                (long long)g->sn);
   *empty = p->B == 0 || p->H == 0 || p->N == 0;
   const int64_t wgs = (int64_t)p->B * p->H * (g->nqb + g->nkb);
   if (wgs > 0x7fffffffLL) return fail(SA_ERR_UNSUPPORTED, "problem too large for one grid");

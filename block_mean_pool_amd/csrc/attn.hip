@@ -9,22 +9,29 @@
 // sorted order), which fixes which tiles the filter can skip.
 //
 // Workgroup = one (batch, head, 128-row query block), 4 wavefronts x 32 rows.
-// Per kept key block j (64 keys):
-//   S^T = K_j Q^T   on v_mfma_f32_32x32x16_bf16 (fp32 inputs: 32x32x2f32),
+// Per kept key block j (64 keys), per wavefront:
+//   S^T = K_j Q^T   v_mfma_f32_32x32x16_bf16 (fp32 inputs: 32x32x2f32),
 //                   computed transposed so that a lane owns one query row
 //                   and 32 of the 64 keys: the row max and row sum are
-//                   in-lane reductions plus one exchange with lane ^ 32;
+//                   in-lane reductions plus one v_permlane32_swap;
 //   online softmax in the exp2 domain (scale * log2 e folded into one FMA);
 //   lambda test: one wave-wide ballot, a uniform branch around P.V;
 //   O^T += V_j^T P^T  with P taken straight from the S^T accumulator
 //                   layout as the B operand (the key order inside one MFMA
 //                   is permuted identically on both operands).
-// K_j is staged row-major and V_j transposed (d-major) in LDS, double
-// buffered: tile t+1 is loaded into registers while tile t is computed and
-// written to the other buffer afterwards, one barrier per tile.  Row
-// paddings of 16 B (K) and 8/16 B (V^T) make the MFMA operand reads
-// bank-conflict free.  Workgroup ids are remapped so that consecutive query
-// blocks of one head run on one XCD and share its L2.
+//
+// LDS layout: K and V tiles are both stored row-major (a row = one key,
+// D elements), with the 16-byte chunks of each row permuted by an XOR of
+// the row index, so that the staging stores are contiguous 16-byte writes
+// and every operand read spreads over all LDS banks.  The V^T operand of
+// P.V is read with ds_read_b64_tr_b16: within 16 lanes, source lane
+// 4 j + q names 4 d-values of key K0 + j and lane i receives key K0 + j's
+// value at d = D0 + i, i.e. a 4-key column segment of V^T per lane.
+// K/V tiles are double buffered: tile t+1 is loaded into registers while
+// tile t is computed and written to the other buffer afterwards, one barrier
+// per tile.  K and V are read through buffer resources that end at row N-1,
+// so ragged or empty tiles read zeros without branches.  Workgroup ids are
+// remapped so that consecutive query blocks of one head run on one XCD.
 #include "sa_device.h"
 #include "sa_internal.h"
 #include "../../include/sparse_attn.h"
@@ -32,42 +39,26 @@
 namespace sa {
 namespace {
 
-template <typename T>
-struct Mfma;
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
-template <>
-struct Mfma<__bf16> {
-  // 8 consecutive bf16 of one row / column: one 16-byte fragment
-  struct Frag {
-    u32x4 v;
-  };
-  __device__ static Frag load(const void* p) { return Frag{*reinterpret_cast<const u32x4*>(p)}; }
-  __device__ static Frag zero() { return Frag{u32x4{0u, 0u, 0u, 0u}}; }
-  __device__ static f32x16 mma(const Frag& a, const Frag& b, f32x16 c) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a.v),
-                                                   __builtin_bit_cast(bf16x8, b.v), c, 0, 0, 0);
-  }
-};
+// two fp32 -> packed bf16x2 (round to nearest even), one v_cvt_pk_bf16_f32
+__device__ __forceinline__ uint32_t pack2(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
+}
 
-template <>
-struct Mfma<float> {
-  // 8 consecutive fp32: eight k=2 MFMAs, k-slot (lane / 32) <-> element e
-  struct Frag {
-    f32x4 lo, hi;
-  };
-  __device__ static Frag load(const void* p) {
-    const f32x4* q = reinterpret_cast<const f32x4*>(p);
-    return Frag{q[0], q[1]};
-  }
-  __device__ static Frag zero() { return Frag{f32x4{0, 0, 0, 0}, f32x4{0, 0, 0, 0}}; }
-  __device__ static f32x16 mma(const Frag& a, const Frag& b, f32x16 c) {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) c = __builtin_amdgcn_mfma_f32_32x32x2f32(a.lo[e], b.lo[e], c, 0, 0, 0);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) c = __builtin_amdgcn_mfma_f32_32x32x2f32(a.hi[e], b.hi[e], c, 0, 0, 0);
-    return c;
-  }
-};
+// max / sum of x over this lane and lane ^ 32 (the other half of the wave):
+// after v_permlane32_swap each lane holds both values, in some order.
+__device__ __forceinline__ float xhalf_max(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xhalf_sum(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
 struct AttnArgs {
   const void* q;
@@ -89,93 +80,102 @@ struct AttnArgs {
 template <typename T, int D>
 struct Tile {
   static constexpr int E = sizeof(T);
-  static constexpr int VEC = 16 / E;                     // elements per 16 B
-  static constexpr int CPR = D * E / 16;                 // 16 B chunks per row
-  static constexpr int KS = D * E + 16;                  // K row stride (bytes)
-  static constexpr int VS = 64 * E + (E == 2 ? 8 : 16);  // V^T row stride (bytes)
-  static constexpr int KBYTES = 64 * KS;
-  static constexpr int VBYTES = D * VS;
-  static constexpr int STAGE = KBYTES + VBYTES;
-  static constexpr int KLD = CPR / 4;                    // K 16 B loads per thread
-  static constexpr int VTASK = (16 * CPR + 255) / 256;   // 4-key x 16 B tasks per thread
-  static constexpr int NKK = D / 16;                     // 16-wide k chunks of S
-  static constexpr int NDT = D / 32;                     // 32-row d tiles of O^T
+  static constexpr int RB = D * E;        // LDS row bytes (one key)
+  static constexpr int CPR = RB / 16;     // 16-byte chunks per row
+  static constexpr int TBYTES = 64 * RB;  // one K or V tile
+  static constexpr int STAGE = 2 * TBYTES;
+  static constexpr int NLD = CPR / 4;     // 16 B loads per thread per tile
+  static constexpr int NKK = D / 16;      // 16-wide k chunks of S
+  static constexpr int NDT = D / 32;      // 32-row d tiles of O^T
+  // chunk permutation of row r: K rows are read 16 consecutive rows at a
+  // time (one chunk each), V rows 4 at a time (64 bytes each)
+  __device__ static int swz_k(int r) { return CPR >= 16 ? (r & 15) : ((r >> 1) & 7); }
+  __device__ static int swz_v(int r) {
+    if constexpr (E != 2) return 0;
+    return CPR >= 16 ? 4 * (r & 3) : 4 * ((r >> 1) & 1);
+  }
+  __device__ static int k_off(int r, int c) { return r * RB + ((c ^ swz_k(r)) << 4); }
+  __device__ static int v_off(int r, int c) { return r * RB + ((c ^ swz_v(r)) << 4); }
 };
 
-// Global -> registers for one K/V tile (rows >= N read as zero).
+// Global -> registers -> LDS for one K/V tile.  K and V of the head are read
+// through buffer resources whose size ends at row N - 1, so rows >= N (the
+// ragged last block, or an empty tile whose offset starts at row N) read as
+// zero without a branch.
 template <typename T, int D>
 struct Stager {
   using TL = Tile<T, D>;
-  u32x4 kr[TL::KLD];
-  u32x4 vr[TL::VTASK][4];
+  u32x4 kr[TL::NLD];
+  u32x4 vr[TL::NLD];
+  __amdgpu_buffer_rsrc_t krs, vrs;
+  uint32_t row_bytes;
 
-  __device__ void load(const char* kbase, const char* vbase, int64_t row_bytes, int key0,
-                       int N, int tid) {
+  __device__ void init(const char* kbase, const char* vbase, uint32_t rb, uint32_t span) {
+    krs = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(kbase), (short)0, (int)span, 0x00020000);
+    vrs = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(vbase), (short)0, (int)span, 0x00020000);
+    row_bytes = rb;
+  }
+
+  // tile_off = first key of the tile * row_bytes; chunk id = tid + 256 s
+  __device__ void load(uint32_t tile_off, int tid) {
 #pragma unroll
-    for (int s = 0; s < TL::KLD; ++s) {
+    for (int s = 0; s < TL::NLD; ++s) {
       const int id = tid + s * 256;
-      const int r = id / TL::CPR, c = id % TL::CPR;
-      const int key = key0 + r;
-      kr[s] = key < N ? *reinterpret_cast<const u32x4*>(kbase + (int64_t)key * row_bytes + c * 16)
-                      : u32x4{0u, 0u, 0u, 0u};
-    }
-#pragma unroll
-    for (int s = 0; s < TL::VTASK; ++s) {
-      const int task = tid + s * 256;
-      if (task < 16 * TL::CPR) {
-        const int quad = task / TL::CPR, c = task % TL::CPR;
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int key = key0 + 4 * quad + u;
-          vr[s][u] = key < N ? *reinterpret_cast<const u32x4*>(vbase + (int64_t)key * row_bytes + c * 16)
-                             : u32x4{0u, 0u, 0u, 0u};
-        }
-      }
+      const uint32_t off = tile_off + (uint32_t)(id / TL::CPR) * row_bytes + (id % TL::CPR) * 16;
+      kr[s] = __builtin_amdgcn_raw_buffer_load_b128(krs, off, 0, 0);
+      vr[s] = __builtin_amdgcn_raw_buffer_load_b128(vrs, off, 0, 0);
     }
   }
 
   __device__ void store(char* stage, int tid) {
-    char* ks = stage;
-    char* vs = stage + TL::KBYTES;
 #pragma unroll
-    for (int s = 0; s < TL::KLD; ++s) {
+    for (int s = 0; s < TL::NLD; ++s) {
       const int id = tid + s * 256;
       const int r = id / TL::CPR, c = id % TL::CPR;
-      *reinterpret_cast<u32x4*>(ks + r * TL::KS + c * 16) = kr[s];
-    }
-#pragma unroll
-    for (int s = 0; s < TL::VTASK; ++s) {
-      const int task = tid + s * 256;
-      if (task < 16 * TL::CPR) {
-        const int quad = task / TL::CPR, c = task % TL::CPR;
-        if constexpr (TL::E == 2) {
-          // 4 keys x 8 bf16 -> for each of the 8 d: 4 keys = 8 bytes of V^T
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const int w = e >> 1;
-            const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
-            u32x2 out;
-            out[0] = __builtin_amdgcn_perm(vr[s][1][w], vr[s][0][w], sel);
-            out[1] = __builtin_amdgcn_perm(vr[s][3][w], vr[s][2][w], sel);
-            *reinterpret_cast<u32x2*>(vs + (c * 8 + e) * TL::VS + quad * 8) = out;
-          }
-        } else {
-          // 4 keys x 4 fp32 -> for each of the 4 d: 4 keys = 16 bytes of V^T
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            u32x4 out{vr[s][0][e], vr[s][1][e], vr[s][2][e], vr[s][3][e]};
-            *reinterpret_cast<u32x4*>(vs + (c * 4 + e) * TL::VS + quad * 16) = out;
-          }
-        }
-      }
+      *reinterpret_cast<u32x4*>(stage + TL::k_off(r, c)) = kr[s];
+      *reinterpret_cast<u32x4*>(stage + TL::TBYTES + TL::v_off(r, c)) = vr[s];
     }
   }
 };
 
+// S^T sub-tile kt (32 keys) = K Q^T.  Q fragment kk holds d = 16 kk + 8 hh
+// + [0, 8) of this lane's query row (fp32: fragments 2 kk and 2 kk + 1).
+template <typename T, int D>
+__device__ __forceinline__ f32x16 qk_sub(const char* ks, const u32x4* qf, int kt, int l32, int hh) {
+  using TL = Tile<T, D>;
+  f32x16 s;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) s[r] = 0.f;
+  const int row = 32 * kt + l32;
+  if constexpr (TL::E == 2) {
+#pragma unroll
+    for (int kk = 0; kk < TL::NKK; ++kk) {
+      const u32x4 kv = *reinterpret_cast<const u32x4*>(ks + TL::k_off(row, 2 * kk + hh));
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kv),
+                                                  __builtin_bit_cast(bf16x8, qf[kk]), s, 0, 0, 0);
+    }
+  } else {
+    // 8 fp32 values = 2 chunks; eight k=2 MFMAs, k-slot (lane / 32) <-> element
+#pragma unroll
+    for (int kk = 0; kk < TL::NKK; ++kk) {
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const f32x4 kv =
+            *reinterpret_cast<const f32x4*>(ks + TL::k_off(row, 4 * kk + 2 * hh + half));
+        const u32x4 q = qf[2 * kk + half];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          s = __builtin_amdgcn_mfma_f32_32x32x2f32(kv[e], __uint_as_float(q[e]), s, 0, 0, 0);
+      }
+    }
+  }
+  return s;
+}
+
 template <typename T, int D, bool CAUSAL>
 __global__ __launch_bounds__(256, (sizeof(T) == 4 && D == 128) ? 1 : 2) void attn_kernel(AttnArgs a) {
   using TL = Tile<T, D>;
-  using M = Mfma<T>;
+  constexpr int NQF = TL::E == 2 ? TL::NKK : 2 * TL::NKK;  // 16-byte Q fragments
   __shared__ __align__(16) char smem[2 * TL::STAGE];
 
   const int tid = threadIdx.x;
@@ -197,18 +197,25 @@ __global__ __launch_bounds__(256, (sizeof(T) == 4 && D == 128) ? 1 : 2) void att
   const bool qvalid = qrow < a.N;
   const bool wave_partial = wrow0 + 32 > a.N;
 
-  // Q fragment: row qrow, d = 16 kk + 8 hh + [0, 8)
-  typename M::Frag qf[TL::NKK];
+  // Q fragments: row qrow, d = 16 kk + 8 hh + [0, 8) (fp32: two 16 B halves)
+  u32x4 qf[NQF];
 #pragma unroll
-  for (int kk = 0; kk < TL::NKK; ++kk)
-    qf[kk] = qvalid ? M::load(qbase + (int64_t)qrow * row_bytes + (16 * kk + 8 * hh) * TL::E)
-                    : M::zero();
+  for (int f = 0; f < NQF; ++f) {
+    const int byte =
+        TL::E == 2 ? (16 * f + 8 * hh) * 2 : (16 * (f >> 1) + 8 * hh + 4 * (f & 1)) * 4;
+    qf[f] = qvalid ? *reinterpret_cast<const u32x4*>(qbase + (int64_t)qrow * row_bytes + byte)
+                   : u32x4{0u, 0u, 0u, 0u};
+  }
 
   int cnt = a.kept_cnt[wg];
   cnt = cnt < 0 ? 0 : (cnt > a.nkb ? a.nkb : cnt);
   const int32_t* lst = a.kept_idx + (size_t)wg * a.nkb;
   // an entry outside [0, NKB) is an empty tile: its keys start at N
   auto key_start = [&](int j) { return (unsigned)j < (unsigned)a.nkb ? j * 64 : a.N; };
+  // list entries travel 64 at a time in one VGPR (lane e holds entry
+  // base + e) and are picked with readlane; the next chunk is prefetched
+  int lvec = lane < cnt ? lst[lane] : 0;
+  int nvec = 64 + lane < cnt ? lst[64 + lane] : 0;
   uint32_t* skip_out =
       a.skip_bits ? a.skip_bits + ((size_t)wg * 4 + w) * a.skip_words : nullptr;
 
@@ -221,29 +228,33 @@ __global__ __launch_bounds__(256, (sizeof(T) == 4 && D == 128) ? 1 : 2) void att
   float l = 0.f;        // this lane's share of the running sum
   uint32_t skip_word = 0;
 
+  // V^T transpose reads: this lane's source key (within a 16-key chunk, +8
+  // for the second read) and d offset (within a 32-wide d tile)
+  const int g16 = lane >> 4, s16 = lane & 15;
+  const int tr_key = 4 * (g16 >> 1) + (s16 >> 2);
+  const int tr_d = 16 * (g16 & 1) + 4 * (s16 & 3);
+
   Stager<T, D> st;
+  st.init(kbase, vbase, (uint32_t)row_bytes,
+          (uint32_t)((int64_t)(a.N - 1) * row_bytes + D * TL::E));
   if (cnt > 0) {
-    st.load(kbase, vbase, row_bytes, key_start(lst[0]), a.N, tid);
+    st.load((uint32_t)key_start(__builtin_amdgcn_readlane(lvec, 0)) * (uint32_t)row_bytes, tid);
     st.store(smem, tid);
   }
   __syncthreads();
 
   for (int t = 0; t < cnt; ++t) {
-    const int key0 = key_start(lst[t]);
+    const int key0 = key_start(__builtin_amdgcn_readlane(lvec, t & 63));
     const char* stage = smem + (t & 1) * TL::STAGE;
-    if (t + 1 < cnt) st.load(kbase, vbase, row_bytes, key_start(lst[t + 1]), a.N, tid);
-
-    // S^T = K Q^T: two 32-key sub-tiles
-    f32x16 s[2];
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s[kt][r] = 0.f;
-      const char* krow = stage + (32 * kt + l32) * TL::KS + 8 * hh * TL::E;
-#pragma unroll
-      for (int kk = 0; kk < TL::NKK; ++kk)
-        s[kt] = M::mma(M::load(krow + 16 * kk * TL::E), qf[kk], s[kt]);
+    if (t + 1 < cnt) {
+      const int jn = ((t + 1) & 63) ? __builtin_amdgcn_readlane(lvec, (t + 1) & 63)
+                                    : __builtin_amdgcn_readlane(nvec, 0);
+      st.load((uint32_t)key_start(jn) * (uint32_t)row_bytes, tid);
     }
+
+    f32x16 s[2];
+    s[0] = qk_sub<T, D>(stage, qf, 0, l32, hh);
+    s[1] = qk_sub<T, D>(stage, qf, 1, l32, hh);
 
     // masking: keys past N, rows past N, future keys under causality
     const bool need_mask = (key0 + 64 > a.N) || wave_partial || (CAUSAL && key0 + 63 > wrow0);
@@ -263,14 +274,11 @@ __global__ __launch_bounds__(256, (sizeof(T) == 4 && D == 128) ? 1 : 2) void att
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mloc = fmaxf(mloc, s[kt][r]);
-    mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
+    mloc = xhalf_max(mloc);
     const float mloc2 = mloc * a.c2;
     const float mnew = fmaxf(m, mloc2);
     bool do_pv = true;
-    if (!a.lam_off) {
-      const bool raises = (mloc2 != -INFINITY) && (mloc2 - mnew >= a.lam2);
-      do_pv = __any(raises);
-    }
+    if (!a.lam_off) do_pv = __any((mloc2 != -INFINITY) && (mloc2 - mnew >= a.lam2));
     const float alpha = (mnew == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m - mnew);
     const float negm = (mnew == -INFINITY) ? 0.f : -mnew;
     float psum = 0.f;
@@ -292,40 +300,47 @@ __global__ __launch_bounds__(256, (sizeof(T) == 4 && D == 128) ? 1 : 2) void att
     }
 
     if (do_pv) {
-      // O^T += V^T P^T; chunk c of 16 keys uses p values [8 (c & 1), +8) of
-      // sub-tile c >> 1: lane half hh holds keys 32 kt + 16 (c & 1) +
-      // 8 (e / 4) + 4 hh + e % 4 for e in [0, 8).
-      const char* vst = stage + TL::KBYTES;
+      // O^T += V^T P^T.  Chunk c of 16 keys uses p values [8 (c & 1), +8) of
+      // sub-tile c >> 1: lane half hh holds keys 16 c + 8 (e / 4) + 4 hh +
+      // e % 4 for e in [0, 8).
+      const char* vst = stage + TL::TBYTES;
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         const int kt = c >> 1, half = c & 1;
-        const int kbase_c = 32 * kt + 16 * half + 4 * hh;
         if constexpr (TL::E == 2) {
           u32x4 pb;
 #pragma unroll
           for (int e = 0; e < 4; ++e)
-            pb[e] = pack_bf16x2(s[kt][8 * half + 2 * e], s[kt][8 * half + 2 * e + 1]);
+            pb[e] = pack2(s[kt][8 * half + 2 * e], s[kt][8 * half + 2 * e + 1]);
 #pragma unroll
           for (int dt = 0; dt < TL::NDT; ++dt) {
-            const char* vr = vst + (32 * dt + l32) * TL::VS + kbase_c * 2;
-            const u32x2 v0 = *reinterpret_cast<const u32x2*>(vr);
-            const u32x2 v1 = *reinterpret_cast<const u32x2*>(vr + 16);
-            const u32x4 va{v0[0], v0[1], v1[0], v1[1]};
+            // source: key 16 c + tr_key (+ 8), d = 32 dt + tr_d .. + 3
+            const int d = 32 * dt + tr_d;
+            const int k0 = 16 * c + tr_key;
+            const int cd = d >> 3, hb = (d & 7) * 2;
+            const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_s16x4*)(vst + TL::v_off(k0, cd) + hb));
+            const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_s16x4*)(vst + TL::v_off(k0 + 8, cd) + hb));
+            const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+            const u32x4 va{l2[0], l2[1], h2[0], h2[1]};
             acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
                 __builtin_bit_cast(bf16x8, va), __builtin_bit_cast(bf16x8, pb), acc[dt], 0, 0, 0);
           }
         } else {
+          // fp32: V^T element (d = 32 dt + l32, key) is one 4-byte read of
+          // row `key`; eight k=2 MFMAs per chunk
 #pragma unroll
           for (int dt = 0; dt < TL::NDT; ++dt) {
-            const char* vr = vst + (32 * dt + l32) * TL::VS + kbase_c * 4;
-            const f32x4 v0 = *reinterpret_cast<const f32x4*>(vr);
-            const f32x4 v1 = *reinterpret_cast<const f32x4*>(vr + 32);
+            const int d = 32 * dt + l32;
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-              acc[dt] = __builtin_amdgcn_mfma_f32_32x32x2f32(v0[e], s[kt][8 * half + e], acc[dt], 0, 0, 0);
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-              acc[dt] = __builtin_amdgcn_mfma_f32_32x32x2f32(v1[e], s[kt][8 * half + 4 + e], acc[dt], 0, 0, 0);
+            for (int e = 0; e < 8; ++e) {
+              const int key = 16 * c + 8 * (e >> 2) + 4 * hh + (e & 3);
+              const float vv =
+                  *reinterpret_cast<const float*>(vst + TL::v_off(key, d >> 2) + (d & 3) * 4);
+              acc[dt] =
+                  __builtin_amdgcn_mfma_f32_32x32x2f32(vv, s[kt][8 * half + e], acc[dt], 0, 0, 0);
+            }
           }
         }
       }
@@ -340,11 +355,15 @@ __global__ __launch_bounds__(256, (sizeof(T) == 4 && D == 128) ? 1 : 2) void att
     }
 
     if (t + 1 < cnt) st.store(smem + ((t + 1) & 1) * TL::STAGE, tid);
+    if (((t + 1) & 63) == 0) {
+      lvec = nvec;
+      nvec = t + 65 + lane < cnt ? lst[t + 65 + lane] : 0;
+    }
     __syncthreads();
   }
 
   // epilogue: O = acc / l; lse = (m + log2 l) ln 2
-  l += __shfl_xor(l, 32, 64);
+  l = xhalf_sum(l);
   if (qvalid) {
     const float inv = l > 0.f ? 1.f / l : 0.f;
     const int oe = a.o_fp32 ? 4 : 2;  // bytes per O element
@@ -360,8 +379,7 @@ __global__ __launch_bounds__(256, (sizeof(T) == 4 && D == 128) ? 1 : 2) void att
         if (a.o_fp32) {
           *reinterpret_cast<f32x4*>(orow + d * 4) = f32x4{o0, o1, o2, o3};
         } else {
-          u32x2 pk{pack_bf16x2(o0, o1), pack_bf16x2(o2, o3)};
-          *reinterpret_cast<u32x2*>(orow + d * 2) = pk;
+          *reinterpret_cast<u32x2*>(orow + d * 2) = u32x2{pack2(o0, o1), pack2(o2, o3)};
         }
       }
     if (a.lse && hh == 0) {

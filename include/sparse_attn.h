@@ -43,7 +43,8 @@
  *   ABI.  NaN/Inf inside Q, K, V are not checked and propagate.
  * - An empty problem (B, H or N equal to 0) is valid and enqueues nothing.
  * - Supported: D in {64, 128}; block_q = 128, block_k = 64; lambda group of
- *   32 rows (one wavefront's rows); N <= 262144 (4096 key blocks).  The
+ *   32 rows (one wavefront's rows); N <= 262144 (4096 key blocks); one
+ *   head's rows (N + 64) * stride_n elements under 2 GiB.  The
  *   quantised variant needs dtype = SA_BF16 and D = 128.  Anything else
  *   returns SA_ERR_UNSUPPORTED.
  */
