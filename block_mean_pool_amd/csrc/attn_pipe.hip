@@ -1,0 +1,453 @@
+// K3 for bf16 inputs: block-sparse flash attention with the per-wavefront
+// softmax-aware skip, software-pipelined so that the matrix cores and the
+// vector ALU of each wavefront work at the same time.
+//
+// Same method, tile shapes, operand layouts and results as the generic
+// kernel in attn.hip (see there for the reading of the SpargeAttn abstract's
+// stage two); what differs is the schedule:
+//
+//   iteration t (tile = t-th kept key block, in list order):
+//     DMA   K of tile t+NST and V of tile t+NST-2, global -> LDS directly
+//           (buffer_load ... lds, no staging registers), into the stages
+//           whose previous contents iteration t-1 finished reading;
+//     scalar part of the softmax of tile t: masking (edge tiles only),
+//           row max, lambda ballot, running max;
+//     one region: the 16 MFMAs of P.V for tile t-1 (skipped when tile t-1
+//           was skipped) and the 16 MFMAs of Q.K^T for tile t+1, next to
+//           the 32 exp2/FMA/add of tile t's softmax and its bf16 packing
+//           (optionally woven by sched_group_barrier);
+//     wait until this wave's DMA for the next iteration has landed, barrier.
+//
+// LDS: NST stages of K and of V (2 with two workgroups per CU, 4 with one),
+// each stage its own array so the compiler sees that DMA into one does not
+// alias reads of another; the loop is unrolled NST times so every stage
+// choice, and every LDS read offset, is a compile-time constant plus a
+// per-lane base.  DMA is issued every iteration (rows past N read as zero),
+// so the number of loads still in flight at each wait is a constant.
+// The exponent offset is a lazily raised running max: P = exp2(c S - mu)
+// with mu <= m; acc and l are rescaled only when m - mu would exceed 8, so
+// P < 2^8 in bf16 and the 64-register rescale almost never runs.  The
+// lambda test always uses the exact running max m.
+#include <type_traits>
+
+#include "attn_common.h"
+
+namespace sa {
+namespace {
+
+using namespace attn;
+
+constexpr float kLazyMax = 8.0f;  // log2 units
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+struct Soft {
+  float m;        // exact running max (log2 units)
+  float mu;       // exponent offset, mu <= m
+  float l;        // this lane's share of sum exp2(c S - mu)
+  float rescale;  // pending factor for acc
+};
+
+template <int I>
+using Int = std::integral_constant<int, I>;
+
+// NST: LDS stages per tensor; WAVES: waves per SIMD targeted (2: two
+// workgroups per CU); WEAVE: order the MFMA / DS / VALU groups explicitly.
+template <int D, bool CAUSAL, int NST, int WAVES, bool WEAVE>
+__global__ __launch_bounds__(256, WAVES) void attn_pipe_kernel(AttnArgs a) {
+  using TL = Tile<__bf16, D>;
+  constexpr int RB = TL::RB, TB = TL::TBYTES;
+  constexpr int NI = TB / 4096;  // DMA wave-instructions per tile per wave
+  constexpr int NKK = D / 16, NDT = D / 32;
+  constexpr int ROWS_PER_4K = 4096 / RB;
+  constexpr int XB = NST > 2 ? TB : 16;  // stages 2, 3 exist only for NST = 4
+  static_assert(NST == 2 || NST == 4, "two or four stages");
+  __shared__ __align__(16) char k0[TB];
+  __shared__ __align__(16) char k1[TB];
+  __shared__ __align__(16) char k2[XB];
+  __shared__ __align__(16) char k3[XB];
+  __shared__ __align__(16) char v0[TB];
+  __shared__ __align__(16) char v1[TB];
+  __shared__ __align__(16) char v2[XB];
+  __shared__ __align__(16) char v3[XB];
+  auto kst = [&](auto s) -> char* {
+    constexpr int S = decltype(s)::value % NST;
+    if constexpr (S == 0) return k0;
+    else if constexpr (S == 1) return k1;
+    else if constexpr (S == 2) return k2;
+    else return k3;
+  };
+  auto vst = [&](auto s) -> char* {
+    constexpr int S = decltype(s)::value % NST;
+    if constexpr (S == 0) return v0;
+    else if constexpr (S == 1) return v1;
+    else if constexpr (S == 2) return v2;
+    else return v3;
+  };
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31, hh = lane >> 5;
+  const int wg = xcd_remap(blockIdx.x, a.nwg);
+  const int bh = wg / a.nqb;
+  const int i = wg - bh * a.nqb;
+  const int b = bh / a.H, h = bh - b * a.H;
+  const int64_t head_off = ((int64_t)b * a.sb + (int64_t)h * a.sh) * 2;
+  const int64_t row_bytes = a.sn * 2;
+  const uint32_t rbg = (uint32_t)row_bytes;
+  const char* qbase = static_cast<const char*>(a.q) + head_off;
+
+  const int wrow0 = i * 128 + 32 * w;
+  const int qrow = wrow0 + l32;
+  const bool qvalid = qrow < a.N;
+  const bool wave_partial = wrow0 + 32 > a.N;
+
+  u32x4 qf[NKK];  // d = 16 kk + 8 hh + [0, 8) of row qrow
+#pragma unroll
+  for (int kk = 0; kk < NKK; ++kk)
+    qf[kk] = qvalid ? *reinterpret_cast<const u32x4*>(qbase + (int64_t)qrow * row_bytes +
+                                                      (16 * kk + 8 * hh) * 2)
+                    : u32x4{0u, 0u, 0u, 0u};
+
+  int cnt = a.kept_cnt[wg];
+  cnt = cnt < 0 ? 0 : (cnt > a.nkb ? a.nkb : cnt);
+  const int32_t* lst = a.kept_idx + (size_t)wg * a.nkb;
+  auto key_of = [&](int j) { return (unsigned)j < (unsigned)a.nkb ? j * 64 : a.N; };
+  // list window: lane e of `win` holds entry wbase + e, `nxt` the next 64
+  int wbase = 0;
+  int win = lane < cnt ? lst[lane] : 0;
+  int nxt = 64 + lane < cnt ? lst[64 + lane] : 0;
+  auto entry_key = [&](int e) {  // key of entry e < wbase + 64, or N past the list
+    return e < cnt ? key_of(__builtin_amdgcn_readlane(win, e - wbase)) : a.N;
+  };
+  uint32_t* skip_out =
+      a.skip_bits ? a.skip_bits + ((size_t)wg * 4 + w) * a.skip_words : nullptr;
+  uint32_t skip_word = 0;
+
+  // buffer resources for K and V of this head (rows >= N read as zero)
+  const uint32_t span = (uint32_t)((int64_t)(a.N - 1) * row_bytes + D * 2);
+  const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<char*>(static_cast<const char*>(a.k) + head_off), (short)0, (int)span, 0x00020000);
+  const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<char*>(static_cast<const char*>(a.v) + head_off), (short)0, (int)span, 0x00020000);
+
+  // DMA: wave-instruction n of wave w fills LDS bytes [(4 n + w) KiB, +1 KiB)
+  // of a tile, lane e the 16 bytes at e * 16: LDS row r, position p holds the
+  // global chunk p ^ swizzle(r) of key row r.  Instruction n covers rows
+  // n * 4096 / RB further on, which leaves both swizzles unchanged, so one
+  // per-lane offset per tensor serves every n.
+  uint32_t dk0, dv0;
+  {
+    const int pos = w * 1024 + lane * 16;
+    const int r = pos / RB, pch = (pos % RB) >> 4;
+    dk0 = (uint32_t)r * rbg + (uint32_t)((pch ^ TL::swz_k(r)) << 4);
+    dv0 = (uint32_t)r * rbg + (uint32_t)((pch ^ TL::swz_v(r)) << 4);
+  }
+  // LDS read bases: K row l32 (+ 32 kt), chunk 2 kk + hh; V^T transpose
+  // reads from key 16 c + 8 half + tr_key, d = 32 dt + tr_d
+  uint32_t kro[NKK];
+#pragma unroll
+  for (int kk = 0; kk < NKK; ++kk) kro[kk] = (uint32_t)TL::k_off(l32, 2 * kk + hh);
+  const int g16 = lane >> 4, s16 = lane & 15;
+  const int tr_key = 4 * (g16 >> 1) + (s16 >> 2);
+  const int tr_d = 16 * (g16 & 1) + 4 * (s16 & 3);
+  uint32_t vro[NDT];
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt) {
+    const int d = 32 * dt + tr_d;
+    vro[dt] = (uint32_t)(TL::v_off(tr_key, d >> 3) + (d & 7) * 2);
+  }
+
+  auto dma = [&](const __amdgpu_buffer_rsrc_t& rs, uint32_t lane_off, char* dst, int key0) {
+    const uint32_t base = (uint32_t)key0 * rbg + lane_off;
+#pragma unroll
+    for (int n = 0; n < NI; ++n)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(dst + (4 * n + w) * 1024), 16,
+                                               base + n * ROWS_PER_4K * rbg, 0, 0, 0);
+  };
+  auto qk_mfma = [&](const char* kb, int kt, int kk, f32x16 acc_s) {
+    const u32x4 kv = *reinterpret_cast<const u32x4*>(kb + kro[kk] + 32 * kt * RB);
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kv),
+                                                   __builtin_bit_cast(bf16x8, qf[kk]), acc_s, 0, 0,
+                                                   0);
+  };
+  auto pv_mfma = [&](const char* vb, int c, int dt, const u32x4& pb, f32x16 acc_o) {
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_s16x4*)(vb + vro[dt] + 16 * c * RB));
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_s16x4*)(vb + vro[dt] + (16 * c + 8) * RB));
+    const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+    const u32x4 va{l2[0], l2[1], h2[0], h2[1]};
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, va),
+                                                   __builtin_bit_cast(bf16x8, pb), acc_o, 0, 0, 0);
+  };
+  // wait for this wave's DMA that the next iteration reads (all but the
+  // loads issued in the last NST - 2 iterations), then barrier
+  auto sync_stage = [&]() {
+    if constexpr (NST == 2) {
+      __syncthreads();
+    } else {
+      asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"((NST - 2) * 2 * NI) : "memory");
+    }
+  };
+
+  f32x16 acc[NDT];
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[dt][r] = 0.f;
+  f32x16 sA[2], sB[2];
+  u32x4 pf[4];  // P of the previous tile, bf16, as the P.V B operand
+#pragma unroll
+  for (int c = 0; c < 4; ++c) pf[c] = u32x4{0u, 0u, 0u, 0u};
+  Soft ss{-INFINITY, -INFINITY, 0.f, 1.f};
+  bool pv_prev = false;
+
+  // keys of entries t .. t + NST - 1 (kq[0] = tile t)
+  int kq[NST];
+#pragma unroll
+  for (int e = 0; e < NST; ++e) kq[e] = entry_key(e);
+
+  // prologue: K of entries 0 .. NST-1, V of entries 0 .. NST-3, S of entry 0
+  dma(krs, dk0, kst(Int<0>{}), kq[0]);
+  dma(krs, dk0, kst(Int<1>{}), kq[1]);
+  if constexpr (NST == 4) {
+    dma(krs, dk0, kst(Int<2>{}), kq[2]);
+    dma(krs, dk0, kst(Int<3>{}), kq[3]);
+    dma(vrs, dv0, vst(Int<0>{}), kq[0]);
+    dma(vrs, dv0, vst(Int<1>{}), kq[1]);
+  }
+  __syncthreads();
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sA[kt][r] = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) sA[kt] = qk_mfma(kst(Int<0>{}), kt, kk, sA[kt]);
+  }
+  __syncthreads();  // stage 0 of K is refilled in iteration 0
+
+  // one pipeline step for entry t with phase PH = t % NST
+  auto step = [&](auto ph, int t, f32x16(&sc)[2], f32x16(&sn)[2]) {
+    constexpr int PH = decltype(ph)::value;
+    char* k_next = kst(Int<PH + 1>{});        // K of entry t + 1
+    char* k_free = kst(Int<PH>{});            // K of entry t (read) -> entry t + NST
+    char* v_prev = vst(Int<PH + NST - 1>{});  // V of entry t - 1
+    char* v_free = vst(Int<PH + NST - 2>{});  // V of entry t - 2 (read) -> entry t + NST - 2
+
+    if (t + NST - wbase >= 64) {  // slide the list window
+      win = nxt;
+      wbase += 64;
+      nxt = wbase + 64 + lane < cnt ? lst[wbase + 64 + lane] : 0;
+    }
+    const int key_far = entry_key(t + NST);
+    dma(krs, dk0, k_free, key_far);
+    dma(vrs, dv0, v_free, kq[NST - 2]);
+    const int key_cur = kq[0];
+
+    if (__any(ss.rescale != 1.f)) {  // the exponent offset moved at t - 1
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[dt][r] *= ss.rescale;
+      ss.rescale = 1.f;
+    }
+
+    // softmax, scalar part: masking, row max, lambda ballot, running max
+    const bool need_mask =
+        (key_cur + 64 > a.N) || wave_partial || (CAUSAL && key_cur + 63 > wrow0);
+    if (need_mask) {
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = key_cur + 32 * kt + 8 * (r >> 2) + 4 * hh + (r & 3);
+          const bool ok = qvalid && key < a.N && (!CAUSAL || key <= qrow);
+          if (!ok) sc[kt][r] = -INFINITY;
+        }
+    }
+    float mloc = -INFINITY;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mloc = fmaxf(mloc, sc[kt][r]);
+    mloc = xhalf_max(mloc) * a.c2;
+    const float mnew = fmaxf(ss.m, mloc);
+    bool do_pv = true;
+    if (!a.lam_off) do_pv = __any((mloc != -INFINITY) && (mloc - mnew >= a.lam2));
+    ss.m = mnew;
+    if (__any(mnew - ss.mu > kLazyMax)) {
+      const float mu_new = fmaxf(ss.mu, mnew);
+      const float f = (mu_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(ss.mu - mu_new);
+      ss.l *= f;
+      ss.rescale *= f;
+      ss.mu = mu_new;
+    }
+    const float negm = (ss.mu == -INFINITY) ? 0.f : -ss.mu;
+    const float c2 = a.c2;
+
+    // region: [P.V of t-1] + Q.K^T of t+1 + exp/sum/pack of t
+    u32x4 pn[4];
+    float psum = 0.f;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sn[kt][r] = 0.f;
+    auto softmax_part = [&]() {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int kt = c >> 1, half = c & 1;
+        float pv[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          pv[e] = __builtin_amdgcn_exp2f(fmaf(sc[kt][8 * half + e], c2, negm));
+          psum += pv[e];
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) pn[c][e] = pack2(pv[2 * e], pv[2 * e + 1]);
+      }
+    };
+    if (pv_prev) {
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk) {
+        sn[0] = qk_mfma(k_next, 0, kk, sn[0]);
+        sn[1] = qk_mfma(k_next, 1, kk, sn[1]);
+      }
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) acc[dt] = pv_mfma(v_prev, c, dt, pf[c], acc[dt]);
+      softmax_part();
+      if constexpr (WEAVE) {
+#pragma unroll
+        for (int g = 0; g < 2 * NKK + 4 * NDT; ++g) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // DS read
+          __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // VALU
+        }
+      }
+    } else {
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk) {
+        sn[0] = qk_mfma(k_next, 0, kk, sn[0]);
+        sn[1] = qk_mfma(k_next, 1, kk, sn[1]);
+      }
+      softmax_part();
+      if constexpr (WEAVE) {
+#pragma unroll
+        for (int g = 0; g < 2 * NKK; ++g) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+          __builtin_amdgcn_sched_group_barrier(0x002, 7, 0);  // VALU
+        }
+      }
+    }
+    ss.l += psum;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) pf[c] = pn[c];
+
+    if (skip_out) {
+      skip_word |= (do_pv ? 0u : 1u) << (t & 31);
+      if ((t & 31) == 31 || t + 1 == cnt) {
+        if (lane == 0) skip_out[t >> 5] = skip_word;
+        skip_word = 0;
+      }
+    }
+    pv_prev = do_pv;
+#pragma unroll
+    for (int e = 0; e + 1 < NST; ++e) kq[e] = kq[e + 1];
+    kq[NST - 1] = key_far;
+    sync_stage();
+  };
+
+  int t = 0;
+  for (; t + NST <= cnt; t += NST) {
+    step(Int<0>{}, t, sA, sB);
+    step(Int<1>{}, t + 1, sB, sA);
+    if constexpr (NST == 4) {
+      step(Int<2>{}, t + 2, sA, sB);
+      step(Int<3>{}, t + 3, sB, sA);
+    }
+  }
+  if (t < cnt) step(Int<0>{}, t, sA, sB);
+  if constexpr (NST == 4) {
+    if (t + 1 < cnt) step(Int<1>{}, t + 1, sB, sA);
+    if (t + 2 < cnt) step(Int<2>{}, t + 2, sA, sB);
+  }
+
+  if (cnt > 0) {
+    if (__any(ss.rescale != 1.f)) {
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[dt][r] *= ss.rescale;
+    }
+    if (pv_prev) {  // P.V of the last entry, V in stage (cnt - 1) % NST
+      auto last_pv = [&](const char* vlast) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+#pragma unroll
+          for (int dt = 0; dt < NDT; ++dt) acc[dt] = pv_mfma(vlast, c, dt, pf[c], acc[dt]);
+      };
+      const int ls = (cnt - 1) % NST;
+      if (ls == 0) last_pv(vst(Int<0>{}));
+      else if (ls == 1) last_pv(vst(Int<1>{}));
+      else if (ls == 2) last_pv(vst(Int<2>{}));
+      else last_pv(vst(Int<3>{}));
+    }
+  }
+
+  // epilogue: O = acc / l; lse = (mu + log2 l) ln 2
+  const float l = xhalf_sum(ss.l);
+  if (qvalid) {
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+    const int oe = a.o_fp32 ? 4 : 2;
+    char* orow = static_cast<char*>(a.o) +
+                 ((int64_t)b * a.sb + (int64_t)h * a.sh + (int64_t)qrow * a.sn) * oe;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int d = 32 * dt + 8 * g4 + 4 * hh;
+        const float o0 = acc[dt][4 * g4] * inv, o1 = acc[dt][4 * g4 + 1] * inv;
+        const float o2 = acc[dt][4 * g4 + 2] * inv, o3 = acc[dt][4 * g4 + 3] * inv;
+        if (a.o_fp32)
+          *reinterpret_cast<f32x4*>(orow + d * 4) = f32x4{o0, o1, o2, o3};
+        else
+          *reinterpret_cast<u32x2*>(orow + d * 2) = u32x2{pack2(o0, o1), pack2(o2, o3)};
+      }
+    if (a.lse && hh == 0)
+      a.lse[(int64_t)bh * a.N + qrow] = l > 0.f ? (ss.mu + __log2f(l)) * kLn2 : -INFINITY;
+  }
+}
+
+#ifndef SA_PIPE_NST
+#define SA_PIPE_NST 2
+#endif
+#ifndef SA_PIPE_WAVES
+#define SA_PIPE_WAVES 2
+#endif
+#ifndef SA_PIPE_WEAVE
+#define SA_PIPE_WEAVE 0
+#endif
+
+template <int D>
+hipError_t launch_pipe_t(const ForwardLaunch& f, hipStream_t s) {
+  const AttnArgs a = make_args(f);
+  constexpr int NST = SA_PIPE_NST, W = SA_PIPE_WAVES;
+  constexpr bool WV = SA_PIPE_WEAVE != 0;
+  if (f.causal)
+    hipLaunchKernelGGL((attn_pipe_kernel<D, true, NST, W, WV>), dim3(a.nwg), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL((attn_pipe_kernel<D, false, NST, W, WV>), dim3(a.nwg), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_attn_pipe(const ForwardLaunch& f, hipStream_t s) {
+  return f.g.D == 128 ? launch_pipe_t<128>(f, s) : launch_pipe_t<64>(f, s);
+}
+
+}  // namespace sa

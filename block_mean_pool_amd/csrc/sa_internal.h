@@ -54,6 +54,7 @@ struct ForwardLaunch {
 hipError_t launch_pool(const PredictLaunch& a, hipStream_t s);
 hipError_t launch_mask(const PredictLaunch& a, hipStream_t s);
 hipError_t launch_attn(const ForwardLaunch& a, hipStream_t s);
+hipError_t launch_attn_pipe(const ForwardLaunch& a, hipStream_t s);
 hipError_t launch_quant(const ForwardLaunch& a, hipStream_t s);
 hipError_t launch_attn_q(const ForwardLaunch& a, hipStream_t s);
 
