@@ -34,11 +34,17 @@ sys.path.insert(0, ROOT)
 METRIC = "dense-equiv attention TFLOPS + sparsity at fixed rel-L1, N=32760 H=40 d=128"
 # HBM traffic of the forward kernel per launch, from two rocprofv3 --pmc
 # passes (FETCH_SIZE x 2.000, WRITE_SIZE x 1.000, the factors a 1 GiB copy
-# reads on the same counters), keyed by the hash of the kernel source it was
+# reads on the same counters), keyed by the hash of the kernel sources it was
 # measured on: a changed kernel reports null until it is measured again.
 MEASURED_TRAFFIC = {
     # workload -> (source hash, bytes read, bytes written)
-    "wan_video": ("f0b088297c15b8de", 112_250_245_000, 335_462_400),
+    "wan_video": ("e85a8cea0b356e89", 111_854_964_736, 345_953_382),
+}
+# the forward kernel that dominates each kind of workload, and its sources
+FORWARD_KERNELS = {
+    "bf16": ("attn_pipe_kernel (sparse_attn_forward)", ("attn_pipe.hip", "attn_common.h")),
+    "f32": ("attn_kernel (sparse_attn_forward)", ("attn.hip", "attn_common.h")),
+    "i8fp8": ("attn_q_kernel (sparse_attn_forward)", ("attn_q.hip",)),
 }
 PEAK_BF16_TFLOPS = 2500.0
 PEAK_I8FP8_TOPS = 5000.0
@@ -53,7 +59,9 @@ def parse():
     ap.add_argument("--workload", default="wan_video")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-sweep", action="store_true")
-    ap.add_argument("--cpu-blocks", type=int, default=128,
+    ap.add_argument("--no-peaks", action="store_true",
+                    help="skip the GEMM / copy reference measurements")
+    ap.add_argument("--cpu-blocks", type=int, default=256,
                     help="query blocks of head 0 in the CPU oracle sample")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after the run, launch a plain copy kernel (torch.neg on "
@@ -62,11 +70,47 @@ def parse():
     return ap.parse_args()
 
 
-def kernel_source_hash():
+def forward_kind(w):
+    return "i8fp8" if w.prec == "i8fp8" else w.dtype
+
+
+def kernel_source_hash(kind):
     import hashlib
-    h = hashlib.sha256(open(os.path.join(ROOT, "block_mean_pool_amd", "csrc", "attn.hip"),
-                            "rb").read())
+    h = hashlib.sha256()
+    for name in FORWARD_KERNELS[kind][1]:
+        h.update(open(os.path.join(ROOT, "block_mean_pool_amd", "csrc", name), "rb").read())
     return h.hexdigest()[:16]
+
+
+def measured_peaks(torch, dev):
+    """What this GPU reaches on a plain bf16 GEMM (torch.matmul, 8192^3) and
+    a plain 1 GiB fp32 copy: context for the roofline fractions, which are
+    taken against the published peaks."""
+    n = 8192
+    a = torch.randn(n, n, device=dev, dtype=torch.bfloat16)
+    b = torch.randn(n, n, device=dev, dtype=torch.bfloat16)
+    for _ in range(3):
+        torch.matmul(a, b)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(10):
+        torch.matmul(a, b)
+    e1.record()
+    torch.cuda.synchronize()
+    gemm = 2.0 * n ** 3 * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e12
+    del a, b
+    x = torch.ones(1 << 28, device=dev, dtype=torch.float32)
+    y = torch.empty_like(x)
+    y.copy_(x)
+    e0.record()
+    for _ in range(10):
+        y.copy_(x)
+    e1.record()
+    torch.cuda.synchronize()
+    copy = 2.0 * x.numel() * 4 * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del x, y
+    return {"bf16_gemm_8192_tflops": round(gemm, 1), "copy_1gib_gbps": round(copy, 1),
+            "published": {"bf16_dense_tflops": PEAK_BF16_TFLOPS, "hbm_gbps": 8000.0}}
 
 
 def gen_inputs(w, threads=16):
@@ -267,9 +311,12 @@ def main():
         print("[bench] timing the CPU oracle sample", file=sys.stderr, flush=True)
         cpu = cpu_baseline(w, Q, K, V, w.tau, args.cpu_blocks)
 
+    peaks = None if args.no_peaks else measured_peaks(torch, dev)
+
+    kind = forward_kind(w)
     traffic = None
     mt = MEASURED_TRAFFIC.get(w.name)
-    if mt and mt[0] == kernel_source_hash() and w.prec == "native":
+    if mt and mt[0] == kernel_source_hash(kind):
         traffic = {"read_bytes": mt[1], "written_bytes": mt[2], "total_bytes": mt[1] + mt[2],
                    "source": "rocprofv3 FETCH_SIZE/WRITE_SIZE, copy-calibrated"}
     out = {
@@ -297,8 +344,10 @@ def main():
         "forward_ms": round(m["forward_ms"], 4),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": traffic,
-                     "kernel": "attn_kernel (sparse_attn_forward)",
-                     "executed_flops_per_launch": m["exec_flops"]},
+                     "kernel": FORWARD_KERNELS[kind][0],
+                     "kernel_source_hash": kernel_source_hash(kind),
+                     "executed_flops_per_launch": m["exec_flops"],
+                     "measured_peaks": peaks},
         "tau_sweep": sweep,
         "cpu_baseline": cpu,
     }

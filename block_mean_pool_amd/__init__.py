@@ -63,6 +63,12 @@ def _load():
         raise ImportError(
             f"{LIB_PATH} is missing: build the HIP library first "
             "(python block_mean_pool_amd/build.py); there is no fallback path")
+    # torch ships its own HIP runtime under the same soname
+    # (libamdhip64.so.7) as the ROCm one this library is linked against.
+    # Importing torch first makes the library's dependency resolve to the
+    # runtime torch already loaded, so the process holds one HIP runtime
+    # (two would each open the device, and the second finds none).
+    import torch  # noqa: F401
     lib = ctypes.CDLL(LIB_PATH)
     P = ctypes.POINTER
     vp = ctypes.c_void_p

@@ -7,23 +7,22 @@
 // stage two); what differs is the schedule:
 //
 //   iteration t (tile = t-th kept key block, in list order):
-//     DMA   K of tile t+NST and V of tile t+NST-2, global -> LDS directly
+//     DMA   K of tile t+2 and V of tile t, global -> LDS directly
 //           (buffer_load ... lds, no staging registers), into the stages
 //           whose previous contents iteration t-1 finished reading;
 //     scalar part of the softmax of tile t: masking (edge tiles only),
 //           row max, lambda ballot, running max;
-//     one region: the 16 MFMAs of P.V for tile t-1 (skipped when tile t-1
-//           was skipped) and the 16 MFMAs of Q.K^T for tile t+1, next to
-//           the 32 exp2/FMA/add of tile t's softmax and its bf16 packing
-//           (optionally woven by sched_group_barrier);
-//     wait until this wave's DMA for the next iteration has landed, barrier.
+//     one region, in four chunks of 16 keys: the 4 MFMAs of P.V for tile
+//           t-1 (not issued when tile t-1 was skipped), 4 MFMAs of Q.K^T
+//           for tile t+1, and 8 exp2/FMA/add plus bf16 packing of tile t's
+//           softmax;
+//     wait until this wave's DMA has landed, barrier.
 //
-// LDS: NST stages of K and of V (2 with two workgroups per CU, 4 with one),
-// each stage its own array so the compiler sees that DMA into one does not
-// alias reads of another; the loop is unrolled NST times so every stage
-// choice, and every LDS read offset, is a compile-time constant plus a
-// per-lane base.  DMA is issued every iteration (rows past N read as zero),
-// so the number of loads still in flight at each wait is a constant.
+// LDS: two stages of K and of V (64 KiB, two workgroups per CU), each stage
+// its own array so the compiler sees that DMA into one does not alias reads
+// of another; the loop is unrolled twice so every stage choice, and every
+// LDS read offset, is a compile-time constant plus a per-lane base.  DMA is
+// issued every iteration (rows past N read as zero).
 // The exponent offset is a lazily raised running max: P = exp2(c S - mu)
 // with mu <= m; acc and l are rescaled only when m - mu would exceed 8, so
 // P < 2^8 in bf16 and the 64-register rescale almost never runs.  The
@@ -51,38 +50,25 @@ struct Soft {
 template <int I>
 using Int = std::integral_constant<int, I>;
 
-// NST: LDS stages per tensor; WAVES: waves per SIMD targeted (2: two
-// workgroups per CU); WEAVE: order the MFMA / DS / VALU groups explicitly.
-template <int D, bool CAUSAL, int NST, int WAVES, bool WEAVE>
-__global__ __launch_bounds__(256, WAVES) void attn_pipe_kernel(AttnArgs a) {
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(256, 2) void attn_pipe_kernel(AttnArgs a) {
   using TL = Tile<__bf16, D>;
   constexpr int RB = TL::RB, TB = TL::TBYTES;
   constexpr int NI = TB / 4096;  // DMA wave-instructions per tile per wave
   constexpr int NKK = D / 16, NDT = D / 32;
   constexpr int ROWS_PER_4K = 4096 / RB;
-  constexpr int XB = NST > 2 ? TB : 16;  // stages 2, 3 exist only for NST = 4
-  static_assert(NST == 2 || NST == 4, "two or four stages");
+  static_assert(NKK % 4 == 0, "the region splits the d chunks in quarters");
   __shared__ __align__(16) char k0[TB];
   __shared__ __align__(16) char k1[TB];
-  __shared__ __align__(16) char k2[XB];
-  __shared__ __align__(16) char k3[XB];
   __shared__ __align__(16) char v0[TB];
   __shared__ __align__(16) char v1[TB];
-  __shared__ __align__(16) char v2[XB];
-  __shared__ __align__(16) char v3[XB];
   auto kst = [&](auto s) -> char* {
-    constexpr int S = decltype(s)::value % NST;
-    if constexpr (S == 0) return k0;
-    else if constexpr (S == 1) return k1;
-    else if constexpr (S == 2) return k2;
-    else return k3;
+    if constexpr (decltype(s)::value % 2 == 0) return k0;
+    else return k1;
   };
   auto vst = [&](auto s) -> char* {
-    constexpr int S = decltype(s)::value % NST;
-    if constexpr (S == 0) return v0;
-    else if constexpr (S == 1) return v1;
-    else if constexpr (S == 2) return v2;
-    else return v3;
+    if constexpr (decltype(s)::value % 2 == 0) return v0;
+    else return v1;
   };
 
   const int tid = threadIdx.x;
@@ -182,15 +168,6 @@ __global__ __launch_bounds__(256, WAVES) void attn_pipe_kernel(AttnArgs a) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, va),
                                                    __builtin_bit_cast(bf16x8, pb), acc_o, 0, 0, 0);
   };
-  // wait for this wave's DMA that the next iteration reads (all but the
-  // loads issued in the last NST - 2 iterations), then barrier
-  auto sync_stage = [&]() {
-    if constexpr (NST == 2) {
-      __syncthreads();
-    } else {
-      asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"((NST - 2) * 2 * NI) : "memory");
-    }
-  };
 
   f32x16 acc[NDT];
 #pragma unroll
@@ -204,20 +181,11 @@ __global__ __launch_bounds__(256, WAVES) void attn_pipe_kernel(AttnArgs a) {
   Soft ss{-INFINITY, -INFINITY, 0.f, 1.f};
   bool pv_prev = false;
 
-  // keys of entries t .. t + NST - 1 (kq[0] = tile t)
-  int kq[NST];
-#pragma unroll
-  for (int e = 0; e < NST; ++e) kq[e] = entry_key(e);
+  int kq0 = entry_key(0), kq1 = entry_key(1);  // keys of entries t, t + 1
 
-  // prologue: K of entries 0 .. NST-1, V of entries 0 .. NST-3, S of entry 0
-  dma(krs, dk0, kst(Int<0>{}), kq[0]);
-  dma(krs, dk0, kst(Int<1>{}), kq[1]);
-  if constexpr (NST == 4) {
-    dma(krs, dk0, kst(Int<2>{}), kq[2]);
-    dma(krs, dk0, kst(Int<3>{}), kq[3]);
-    dma(vrs, dv0, vst(Int<0>{}), kq[0]);
-    dma(vrs, dv0, vst(Int<1>{}), kq[1]);
-  }
+  // prologue: K of entries 0 and 1, S of entry 0
+  dma(krs, dk0, kst(Int<0>{}), kq0);
+  dma(krs, dk0, kst(Int<1>{}), kq1);
   __syncthreads();
 #pragma unroll
   for (int kt = 0; kt < 2; ++kt) {
@@ -228,23 +196,23 @@ __global__ __launch_bounds__(256, WAVES) void attn_pipe_kernel(AttnArgs a) {
   }
   __syncthreads();  // stage 0 of K is refilled in iteration 0
 
-  // one pipeline step for entry t with phase PH = t % NST
+  // one pipeline step for entry t with phase PH = t % 2
   auto step = [&](auto ph, int t, f32x16(&sc)[2], f32x16(&sn)[2]) {
     constexpr int PH = decltype(ph)::value;
-    char* k_next = kst(Int<PH + 1>{});        // K of entry t + 1
-    char* k_free = kst(Int<PH>{});            // K of entry t (read) -> entry t + NST
-    char* v_prev = vst(Int<PH + NST - 1>{});  // V of entry t - 1
-    char* v_free = vst(Int<PH + NST - 2>{});  // V of entry t - 2 (read) -> entry t + NST - 2
+    char* k_next = kst(Int<PH + 1>{});  // K of entry t + 1
+    char* k_free = kst(Int<PH>{});      // K of entry t (read) -> entry t + 2
+    char* v_prev = vst(Int<PH + 1>{});  // V of entry t - 1
+    char* v_free = vst(Int<PH>{});      // V of entry t - 2 (read) -> entry t
 
-    if (t + NST - wbase >= 64) {  // slide the list window
+    if (t + 2 - wbase >= 64) {  // slide the list window
       win = nxt;
       wbase += 64;
       nxt = wbase + 64 + lane < cnt ? lst[wbase + 64 + lane] : 0;
     }
-    const int key_far = entry_key(t + NST);
+    const int key_far = entry_key(t + 2);
     dma(krs, dk0, k_free, key_far);
-    dma(vrs, dv0, v_free, kq[NST - 2]);
-    const int key_cur = kq[0];
+    dma(vrs, dv0, v_free, kq0);
+    const int key_cur = kq0;
 
     if (__any(ss.rescale != 1.f)) {  // the exponent offset moved at t - 1
 #pragma unroll
@@ -287,60 +255,49 @@ __global__ __launch_bounds__(256, WAVES) void attn_pipe_kernel(AttnArgs a) {
     const float negm = (ss.mu == -INFINITY) ? 0.f : -ss.mu;
     const float c2 = a.c2;
 
-    // region: [P.V of t-1] + Q.K^T of t+1 + exp/sum/pack of t
+    // region: [P.V of t-1] + Q.K^T of t+1 + exp/sum/pack of t.  Chunk c:
+    // P.V MFMAs of key chunk c of tile t-1, Q.K^T MFMAs for the c-th quarter
+    // of the d chunks kk (both key halves), softmax of this lane's 8 scores
+    // 8 half + [0, 8) of key half kt = c / 2 of tile t.
     u32x4 pn[4];
     float psum = 0.f;
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) sn[kt][r] = 0.f;
-    auto softmax_part = [&]() {
+    auto chunk_qk = [&](int c) {
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const int kt = c >> 1, half = c & 1;
-        float pv[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          pv[e] = __builtin_amdgcn_exp2f(fmaf(sc[kt][8 * half + e], c2, negm));
-          psum += pv[e];
-        }
-#pragma unroll
-        for (int e = 0; e < 4; ++e) pn[c][e] = pack2(pv[2 * e], pv[2 * e + 1]);
+      for (int kk = c * (NKK / 4); kk < (c + 1) * (NKK / 4); ++kk) {
+        sn[0] = qk_mfma(k_next, 0, kk, sn[0]);
+        sn[1] = qk_mfma(k_next, 1, kk, sn[1]);
       }
+    };
+    auto chunk_pv = [&](int c) {
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) acc[dt] = pv_mfma(v_prev, c, dt, pf[c], acc[dt]);
+    };
+    auto chunk_soft = [&](int c) {
+      const int kt = c >> 1, half = c & 1;
+      float pv[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        pv[e] = __builtin_amdgcn_exp2f(fmaf(sc[kt][8 * half + e], c2, negm));
+      psum += ((pv[0] + pv[1]) + (pv[2] + pv[3])) + ((pv[4] + pv[5]) + (pv[6] + pv[7]));
+#pragma unroll
+      for (int e = 0; e < 4; ++e) pn[c][e] = pack2(pv[2 * e], pv[2 * e + 1]);
     };
     if (pv_prev) {
 #pragma unroll
-      for (int kk = 0; kk < NKK; ++kk) {
-        sn[0] = qk_mfma(k_next, 0, kk, sn[0]);
-        sn[1] = qk_mfma(k_next, 1, kk, sn[1]);
-      }
-#pragma unroll
-      for (int c = 0; c < 4; ++c)
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) acc[dt] = pv_mfma(v_prev, c, dt, pf[c], acc[dt]);
-      softmax_part();
-      if constexpr (WEAVE) {
-#pragma unroll
-        for (int g = 0; g < 2 * NKK + 4 * NDT; ++g) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // DS read
-          __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // VALU
-        }
+      for (int c = 0; c < 4; ++c) {
+        chunk_pv(c);
+        chunk_qk(c);
+        chunk_soft(c);
       }
     } else {
 #pragma unroll
-      for (int kk = 0; kk < NKK; ++kk) {
-        sn[0] = qk_mfma(k_next, 0, kk, sn[0]);
-        sn[1] = qk_mfma(k_next, 1, kk, sn[1]);
-      }
-      softmax_part();
-      if constexpr (WEAVE) {
-#pragma unroll
-        for (int g = 0; g < 2 * NKK; ++g) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
-          __builtin_amdgcn_sched_group_barrier(0x002, 7, 0);  // VALU
-        }
+      for (int c = 0; c < 4; ++c) {
+        chunk_qk(c);
+        chunk_soft(c);
       }
     }
     ss.l += psum;
@@ -355,26 +312,18 @@ __global__ __launch_bounds__(256, WAVES) void attn_pipe_kernel(AttnArgs a) {
       }
     }
     pv_prev = do_pv;
-#pragma unroll
-    for (int e = 0; e + 1 < NST; ++e) kq[e] = kq[e + 1];
-    kq[NST - 1] = key_far;
-    sync_stage();
+    kq0 = kq1;
+    kq1 = key_far;
+    // the DMA issued above is what iteration t + 1 reads
+    __syncthreads();
   };
 
   int t = 0;
-  for (; t + NST <= cnt; t += NST) {
+  for (; t + 2 <= cnt; t += 2) {
     step(Int<0>{}, t, sA, sB);
     step(Int<1>{}, t + 1, sB, sA);
-    if constexpr (NST == 4) {
-      step(Int<2>{}, t + 2, sA, sB);
-      step(Int<3>{}, t + 3, sB, sA);
-    }
   }
   if (t < cnt) step(Int<0>{}, t, sA, sB);
-  if constexpr (NST == 4) {
-    if (t + 1 < cnt) step(Int<1>{}, t + 1, sB, sA);
-    if (t + 2 < cnt) step(Int<2>{}, t + 2, sA, sB);
-  }
 
   if (cnt > 0) {
     if (__any(ss.rescale != 1.f)) {
@@ -383,18 +332,12 @@ __global__ __launch_bounds__(256, WAVES) void attn_pipe_kernel(AttnArgs a) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[dt][r] *= ss.rescale;
     }
-    if (pv_prev) {  // P.V of the last entry, V in stage (cnt - 1) % NST
-      auto last_pv = [&](const char* vlast) {
+    if (pv_prev) {  // P.V of the last entry, V in stage (cnt - 1) % 2
+      const char* vlast = ((cnt - 1) & 1) ? v1 : v0;
 #pragma unroll
-        for (int c = 0; c < 4; ++c)
+      for (int c = 0; c < 4; ++c)
 #pragma unroll
-          for (int dt = 0; dt < NDT; ++dt) acc[dt] = pv_mfma(vlast, c, dt, pf[c], acc[dt]);
-      };
-      const int ls = (cnt - 1) % NST;
-      if (ls == 0) last_pv(vst(Int<0>{}));
-      else if (ls == 1) last_pv(vst(Int<1>{}));
-      else if (ls == 2) last_pv(vst(Int<2>{}));
-      else last_pv(vst(Int<3>{}));
+        for (int dt = 0; dt < NDT; ++dt) acc[dt] = pv_mfma(vlast, c, dt, pf[c], acc[dt]);
     }
   }
 
@@ -422,25 +365,13 @@ __global__ __launch_bounds__(256, WAVES) void attn_pipe_kernel(AttnArgs a) {
   }
 }
 
-#ifndef SA_PIPE_NST
-#define SA_PIPE_NST 2
-#endif
-#ifndef SA_PIPE_WAVES
-#define SA_PIPE_WAVES 2
-#endif
-#ifndef SA_PIPE_WEAVE
-#define SA_PIPE_WEAVE 0
-#endif
-
 template <int D>
 hipError_t launch_pipe_t(const ForwardLaunch& f, hipStream_t s) {
   const AttnArgs a = make_args(f);
-  constexpr int NST = SA_PIPE_NST, W = SA_PIPE_WAVES;
-  constexpr bool WV = SA_PIPE_WEAVE != 0;
   if (f.causal)
-    hipLaunchKernelGGL((attn_pipe_kernel<D, true, NST, W, WV>), dim3(a.nwg), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((attn_pipe_kernel<D, true>), dim3(a.nwg), dim3(256), 0, s, a);
   else
-    hipLaunchKernelGGL((attn_pipe_kernel<D, false, NST, W, WV>), dim3(a.nwg), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((attn_pipe_kernel<D, false>), dim3(a.nwg), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
