@@ -113,6 +113,20 @@ def measured_peaks(torch, dev):
             "published": {"bf16_dense_tflops": PEAK_BF16_TFLOPS, "hbm_gbps": 8000.0}}
 
 
+def data_description(w):
+    what = {
+        "field": "smoothed-field Q/K on a %s latent grid%s, Gaussian V; stands in for the "
+                 "pages' video DiT self-attention" % (
+                     "x".join(map(str, w.grid)) if w.grid else "1-D",
+                     f" plus {w.n_text} Gaussian text tokens" if w.n_text else ""),
+        "lm": "AR(1) rho=0.95 Q/K with an attention sink on tokens 0-3, Gaussian V; stands "
+              "in for LM prefill",
+        "centroid": "Q/K around 8 centroids in runs of 64, Gaussian V",
+        "gauss": "Gaussian Q/K/V",
+    }[w.structure]
+    return f"synthetic, seeded ({what})"
+
+
 def gen_inputs(w, threads=16):
     with ThreadPoolExecutor(threads) as ex:
         heads = list(ex.map(lambda bh: w.head(bh // w.H, bh % w.H), range(w.B * w.H)))
@@ -331,8 +345,7 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "i8/fp8" if w.prec == "i8fp8" else w.dtype,
-        "data": "synthetic (seeded smoothed-field Q/K, Gaussian V; stands in for the "
-                "pages' Wan video DiT workloads)",
+        "data": data_description(w),
         "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "D": w.D,
                    "causal": w.causal, "tau": w.tau, "lambda": w.lam, "rule": w.rule,
                    "block_q": 128, "block_k": 64, "lambda_group_rows": 32},
