@@ -16,9 +16,9 @@
 // attn_q_kernel: the same tiling, online softmax and per-wavefront lambda
 // test as the bf16 kernel, with v_mfma_i32_32x32x32_i8 for S^T = K Q^T and
 // v_mfma_f32_32x32x16_fp8_fp8 for O^T += V^T P^T.
-#include "sa_device.h"
-#include "sa_internal.h"
-#include "../../include/sparse_attn.h"
+#include <type_traits>
+
+#include "attn_common.h"
 
 namespace sa {
 namespace {
@@ -104,18 +104,22 @@ __global__ __launch_bounds__(256) void quant_kernel(ForwardLaunch f) {
   } else {
     const float scale = amax > 0.f ? __fdiv_rn(amax, 448.0f) : 1.0f;
     if (tid == 0) f.sv[bh * g.nkb + blk] = scale;
-    // rows ro + 16 it (it < 4) of this key block; transposed into LDS
+    // rows ro + 16 it (it < 4) of this key block; transposed into LDS,
+    // key k = 32 t + 8 g + 4 h + e at position 32 h + 16 t + 4 g + e: the
+    // order of a 32x32 MFMA accumulator lane's keys, so that a lane's 32 P
+    // codes and the 32 V codes it multiplies are both contiguous
 #pragma unroll
     for (int it = 0; it < 4; ++it) {
       const int rr = ro + 16 * it;  // key within block
+      const int pos = 32 * ((rr >> 2) & 1) + 16 * (rr >> 5) + 4 * ((rr >> 3) & 3) + (rr & 3);
 #pragma unroll
       for (int e = 0; e < 8; e += 2) {
         const uint32_t w = buf[it][e >> 1];
         const float x0 = __fdiv_rn(bf16_lo(w), scale);
         const float x1 = __fdiv_rn(bf16_hi(w), scale);
         const int pk = __builtin_amdgcn_cvt_pk_fp8_f32(x0, x1, 0, false);
-        vt_tile[(c * 8 + e) * 64 + rr] = (uint8_t)(pk & 0xff);
-        vt_tile[(c * 8 + e + 1) * 64 + rr] = (uint8_t)((pk >> 8) & 0xff);
+        vt_tile[(c * 8 + e) * 64 + pos] = (uint8_t)(pk & 0xff);
+        vt_tile[(c * 8 + e + 1) * 64 + pos] = (uint8_t)((pk >> 8) & 0xff);
       }
     }
     __syncthreads();
@@ -148,199 +152,270 @@ struct AttnQArgs {
   int o_fp32;
 };
 
-constexpr int KS = D + 16;  // int8 K row stride (bytes)
-constexpr int VS = 64 + 4;  // e4m3 V^T row stride (bytes)
-constexpr int KBYTES = 64 * KS;
-constexpr int VBYTES = D * VS;
-constexpr int STAGE = KBYTES + VBYTES;
+typedef __attribute__((address_space(3))) void lds_void_q;
+typedef int i32x8 __attribute__((ext_vector_type(8)));
 
-struct StagerQ {
-  u32x4 kr[2];  // 64 rows x 8 chunks = 512 chunks
-  u32x4 vr[2];  // 128 d rows x 4 chunks = 512 chunks
-  __device__ void load(const int8_t* kc, const uint8_t* vt_blocks, int j, int N, int tid) {
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      const int id = tid + 256 * s;
-      const int r = id >> 3, c = id & 7;
-      const int key = j * 64 + r;
-      kr[s] = key < N ? *reinterpret_cast<const u32x4*>(kc + (int64_t)key * D + c * 16)
-                      : u32x4{0u, 0u, 0u, 0u};
-      vr[s] = *reinterpret_cast<const u32x4*>(vt_blocks + (size_t)j * D * 64 + id * 16);
-    }
-  }
-  __device__ void store(char* stage, int tid) {
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      const int id = tid + 256 * s;
-      const int r = id >> 3, c = id & 7;
-      *reinterpret_cast<u32x4*>(stage + r * KS + c * 16) = kr[s];
-      const int d = id >> 2, cv = id & 3;
-      uint32_t* vp = reinterpret_cast<uint32_t*>(stage + KBYTES + d * VS + cv * 16);
-      vp[0] = vr[s][0];
-      vp[1] = vr[s][1];
-      vp[2] = vr[s][2];
-      vp[3] = vr[s][3];
-    }
-  }
-};
-
+// Stage two in INT8 / FP8, software-pipelined like the bf16 kernel
+// (attn_pipe.hip): K codes (64 rows x 128 B) and V^T codes (128 rows x 64 B)
+// are DMA'd global -> LDS in two stages each, 16-byte chunks XOR-permuted
+// per row so that the operand reads are free of bank conflicts; iteration t
+// holds, in one region, the FP8 P.V MFMAs of tile t-1, the INT8 Q.K^T MFMAs
+// of tile t+1 and the softmax of tile t.  Unlike the bf16 kernel the
+// exponent offset is the exact running max m (P codes are e4m3(2^8 P) with
+// P <= 1, as the reading fixes), so acc is rescaled whenever m grows.  The
+// factor 2^8 is folded into the exponent and into l: O = acc / l and lse are
+// unchanged.  P.V uses v_mfma_f32_32x32x64_f8f6f4 (all 64 keys of a tile in
+// one MFMA per 32 d-rows); each tile's product is added as acc += s_v * tmp.
 template <bool CAUSAL>
 __global__ __launch_bounds__(256, 2) void attn_q_kernel(AttnQArgs a) {
-  __shared__ __align__(16) char smem[2 * STAGE];
+  constexpr int TK = 64 * D;  // K codes of a tile, 8 KiB
+  constexpr int TV = D * 64;  // V^T codes of a tile, 8 KiB
+  __shared__ __align__(16) char k0[TK];
+  __shared__ __align__(16) char k1[TK];
+  __shared__ __align__(16) char v0[TV];
+  __shared__ __align__(16) char v1[TV];
+
   const int tid = threadIdx.x;
-  const int lane = tid & 63, w = tid >> 6;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hh = lane >> 5;
   const int wg = xcd_remap(blockIdx.x, a.nwg);
   const int bh = wg / a.nqb;
   const int i = wg - bh * a.nqb;
   const int b = bh / a.H, h = bh - b * a.H;
-  const int row0 = i * 128;
-  const int wrow0 = row0 + 32 * w;
+  const int wrow0 = i * 128 + 32 * w;
   const int qrow = wrow0 + l32;
   const bool qvalid = qrow < a.N;
   const bool wave_partial = wrow0 + 32 > a.N;
   const int8_t* qc = a.qc + (size_t)bh * a.N * D;
-  const int8_t* kc = a.kc + (size_t)bh * a.N * D;
-  const uint8_t* vt = a.vt + (size_t)bh * a.nkb * D * 64;
 
-  u32x4 qf[4];  // d = 32 kk + 16 hh + [0, 16)
+  u32x4 qf[4];  // Q codes, d = 32 kk + 16 hh + [0, 16) of row qrow
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk)
     qf[kk] = qvalid ? *reinterpret_cast<const u32x4*>(qc + (int64_t)qrow * D + 32 * kk + 16 * hh)
                     : u32x4{0u, 0u, 0u, 0u};
   const float cq = a.c2 * a.sq[wg];
+  const float* skp = a.sk + (size_t)bh * a.nkb;
+  const float* svp = a.sv + (size_t)bh * a.nkb;
 
   int cnt = a.kept_cnt[wg];
   cnt = cnt < 0 ? 0 : (cnt > a.nkb ? a.nkb : cnt);
   const int32_t* lst = a.kept_idx + (size_t)wg * a.nkb;
+  int wbase = 0;
+  int win = lane < cnt ? lst[lane] : 0;
+  int nxt = 64 + lane < cnt ? lst[64 + lane] : 0;
+  // block of entry e (< wbase + 64), or nkb (an empty tile) past the list
+  auto entry_blk = [&](int e) {
+    if (e >= cnt) return a.nkb;
+    const int j = __builtin_amdgcn_readlane(win, e - wbase);
+    return (unsigned)j < (unsigned)a.nkb ? j : a.nkb;
+  };
   uint32_t* skip_out =
       a.skip_bits ? a.skip_bits + ((size_t)wg * 4 + w) * a.skip_words : nullptr;
+  uint32_t skip_word = 0;
+
+  // K codes of the head: rows >= N read as zero; V^T codes: block nkb (an
+  // empty tile) reads as zero
+  const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<int8_t*>(a.kc + (size_t)bh * a.N * D), (short)0, (int)(a.N * D), 0x00020000);
+  const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(a.vt + (size_t)bh * a.nkb * TV), (short)0, (int)(a.nkb * TV),
+      0x00020000);
+
+  // DMA: wave-instruction n (0, 1) of wave w fills bytes [(4 n + w) KiB,
+  // +1 KiB) of a tile, lane e 16 bytes at e * 16.  K: LDS row r (128 B),
+  // position p holds global chunk p ^ swk(r), swk(r) = (r >> 1) & 7; V^T:
+  // LDS row d (64 B), position p holds chunk p ^ swv(d), swv(d) = (d >> 2) & 3.
+  // Instruction n is 32 K rows / 64 V rows further on, which leaves both
+  // permutations unchanged.
+  auto swk = [](int r) { return (r >> 1) & 7; };
+  auto swv = [](int d) { return (d >> 2) & 3; };
+  uint32_t dk0, dv0;
+  {
+    const int pos = w * 1024 + lane * 16;
+    const int r = pos >> 7, pk = (pos & 127) >> 4;
+    dk0 = (uint32_t)(r * D + ((pk ^ swk(r)) << 4));
+    const int d = pos >> 6, pv = (pos & 63) >> 4;
+    dv0 = (uint32_t)(d * 64 + ((pv ^ swv(d)) << 4));
+  }
+  // LDS read bases: K row l32 (+32 kt), chunk 2 kk + hh; V^T row l32
+  // (+32 dt), chunks 2 hh and 2 hh + 1
+  uint32_t kro[4];
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) kro[kk] = (uint32_t)(l32 * D + (((2 * kk + hh) ^ swk(l32)) << 4));
+  const uint32_t vro0 = (uint32_t)(l32 * 64 + (((2 * hh) ^ swv(l32)) << 4));
+  const uint32_t vro1 = (uint32_t)(l32 * 64 + (((2 * hh + 1) ^ swv(l32)) << 4));
+
+  // K(blk) into kdst, V(vblk) into vdst (a block index of nkb is an empty
+  // tile and reads as zero)
+  auto dma = [&](char* kdst, int blk, char* vdst, int vblk) {
+    const uint32_t kb = (uint32_t)blk * 64u * D + dk0;
+    const uint32_t vb = (uint32_t)vblk * TV + dv0;
+#pragma unroll
+    for (int n = 0; n < 2; ++n) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_void_q*)(kdst + (4 * n + w) * 1024), 16,
+                                               kb + n * 4096, 0, 0, 0);
+      if (vdst)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void_q*)(vdst + (4 * n + w) * 1024),
+                                                 16, vb + n * 4096, 0, 0, 0);
+    }
+  };
+  auto qk_mfma = [&](const char* kbuf, int kt, int kk, i32x16 acc_s) {
+    const u32x4 kv = *reinterpret_cast<const u32x4*>(kbuf + kro[kk] + 32 * kt * D);
+    return __builtin_amdgcn_mfma_i32_32x32x32_i8(__builtin_bit_cast(i32x4, kv),
+                                                 __builtin_bit_cast(i32x4, qf[kk]), acc_s, 0, 0, 0);
+  };
+  auto pv_mfma = [&](const char* vbuf, int dt, const i32x8& pb) {
+    const u32x4 lo = *reinterpret_cast<const u32x4*>(vbuf + vro0 + 32 * dt * 64);
+    const u32x4 hi = *reinterpret_cast<const u32x4*>(vbuf + vro1 + 32 * dt * 64);
+    const i32x8 va{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                   (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+    f32x16 z;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) z[r] = 0.f;
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va, pb, z, 0, 0, 0, 0, 0, 0);
+  };
 
   f32x16 acc[4];
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[dt][r] = 0.f;
-  float m = -INFINITY, l = 0.f;
-  uint32_t skip_word = 0;
+  i32x16 sA[2], sB[2];
+  i32x8 pf;  // e4m3(2^8 P) of the previous tile, byte j = key 32 kt + ... (S^T order)
+#pragma unroll
+  for (int e = 0; e < 8; ++e) pf[e] = 0;
+  float m = -INFINITY, l = 0.f, rescale = 1.f, vsc_prev = 0.f;
+  bool pv_prev = false;
 
-  StagerQ st;
-  auto valid_block = [&](int j) { return (unsigned)j < (unsigned)a.nkb ? j : -1; };
-  if (cnt > 0) {
-    const int j0 = valid_block(lst[0]);
-    if (j0 >= 0) {
-      st.load(kc, vt, j0, a.N, tid);
-      st.store(smem, tid);
-    }
+  int jq0 = entry_blk(0), jq1 = entry_blk(1);  // blocks of entries t, t + 1
+
+  // prologue: K of entries 0 and 1, S of entry 0
+  dma(k0, jq0, nullptr, 0);
+  dma(k1, jq1, nullptr, 0);
+  __syncthreads();
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sA[kt][r] = 0;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) sA[kt] = qk_mfma(k0, kt, kk, sA[kt]);
   }
   __syncthreads();
 
-  for (int t = 0; t < cnt; ++t) {
-    const int j = valid_block(lst[t]);
-    const char* stage = smem + (t & 1) * STAGE;
-    if (t + 1 < cnt) {
-      const int jn = valid_block(lst[t + 1]);
-      if (jn >= 0) st.load(kc, vt, jn, a.N, tid);
-    }
-    const int key0 = j >= 0 ? j * 64 : a.N;  // an invalid entry is an empty tile
-    const float csc = j >= 0 ? cq * a.sk[(size_t)bh * a.nkb + j] : 0.f;
-    const float vsc = j >= 0 ? a.sv[(size_t)bh * a.nkb + j] * (1.0f / 256.0f) : 0.f;
+  auto step = [&](auto ph, int t, i32x16(&sc)[2], i32x16(&sn)[2]) {
+    constexpr int PH = decltype(ph)::value;
+    char* k_next = PH ? k0 : k1;  // K of entry t + 1
+    char* k_free = PH ? k1 : k0;  // K of entry t (read) -> entry t + 2
+    char* v_prev = PH ? v0 : v1;  // V of entry t - 1
+    char* v_free = PH ? v1 : v0;  // V of entry t - 2 (read) -> entry t
 
-    f32x16 s[2];
+    if (t + 2 - wbase >= 64) {
+      win = nxt;
+      wbase += 64;
+      nxt = wbase + 64 + lane < cnt ? lst[wbase + 64 + lane] : 0;
+    }
+    const int j_far = entry_blk(t + 2);
+    // K(t+2) into the stage of K(t); V(t) into the stage of V(t-2)
+    dma(k_free, j_far, v_free, jq0);
+    const int j_cur = jq0;
+    const int key_cur = j_cur < a.nkb ? j_cur * 64 : a.N;
+    const float csc = j_cur < a.nkb ? cq * skp[j_cur] : 0.f;
+    const float vsc = j_cur < a.nkb ? svp[j_cur] : 0.f;
+
+    if (__any(rescale != 1.f)) {  // m grew at t - 1
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-      i32x16 si;
+      for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) si[r] = 0;
-      const char* krow = stage + (32 * kt + l32) * KS + 16 * hh;
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const u32x4 kv = *reinterpret_cast<const u32x4*>(krow + 32 * kk);
-        si = __builtin_amdgcn_mfma_i32_32x32x32_i8(__builtin_bit_cast(i32x4, kv),
-                                                   __builtin_bit_cast(i32x4, qf[kk]), si, 0, 0, 0);
-      }
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s[kt][r] = (float)si[r];
+        for (int r = 0; r < 16; ++r) acc[dt][r] *= rescale;
+      rescale = 1.f;
     }
 
-    const bool need_mask = (key0 + 64 > a.N) || wave_partial || (CAUSAL && key0 + 63 > wrow0);
+    // integer scores Q~.K~ of tile t (exact in fp32: |Q~.K~| < 2^22); masked -inf
+    f32x16 x[2];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) x[kt][r] = (float)sc[kt][r];
+    const bool need_mask =
+        (key_cur + 64 > a.N) || wave_partial || (CAUSAL && key_cur + 63 > wrow0);
     if (need_mask) {
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int key = key0 + 32 * kt + 8 * (r >> 2) + 4 * hh + (r & 3);
+          const int key = key_cur + 32 * kt + 8 * (r >> 2) + 4 * hh + (r & 3);
           const bool ok = qvalid && key < a.N && (!CAUSAL || key <= qrow);
-          if (!ok) s[kt][r] = -INFINITY;
+          if (!ok) x[kt][r] = -INFINITY;
         }
     }
-    // logits in log2 units: s * (sm log2e sq sk); max taken on scaled values
-    float mloc = -INFINITY;
+    float xmax = -INFINITY;
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        s[kt][r] *= csc;
-        mloc = fmaxf(mloc, s[kt][r]);
-      }
-    mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
+      for (int r = 0; r < 16; ++r) xmax = fmaxf(xmax, x[kt][r]);
+    xmax = attn::xhalf_max(xmax);
+    // logits in log2 units: csc * x, csc = sm log2(e) sq sk > 0
+    const float mloc = xmax * csc;
     const float mnew = fmaxf(m, mloc);
     bool do_pv = true;
     if (!a.lam_off) do_pv = __any((mloc != -INFINITY) && (mloc - mnew >= a.lam2));
-    const float alpha = (mnew == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m - mnew);
-    const float negm = (mnew == -INFINITY) ? 0.f : -mnew;
+    if (mnew != m) {
+      const float f = (m == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m - mnew);
+      l *= f;
+      rescale = f;
+      m = mnew;
+    }
+    // 2^8 P = exp2(csc * x + cb), cb = 8 - m
+    const float cb = (m == -INFINITY) ? 0.f : 8.f - m;
+
+    i32x8 pn;
     float psum = 0.f;
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float p = __builtin_amdgcn_exp2f(s[kt][r] + negm);
-        s[kt][r] = p;
-        psum += p;
-      }
-    l = alpha * l + psum;
-    m = mnew;
-    if (__any(alpha != 1.f)) {
+      for (int r = 0; r < 16; ++r) sn[kt][r] = 0;
+    // chunk c: P.V of tile t-1 for d rows 32c..32c+31, Q.K^T of tile t+1 for
+    // kk = c (both key halves), softmax of this lane's scores 8c .. 8c+7
+    auto chunk_pv = [&](int c) {
+      const f32x16 tmp = pv_mfma(v_prev, c, pf);
 #pragma unroll
-      for (int dt = 0; dt < 4; ++dt)
+      for (int r = 0; r < 16; ++r) acc[c][r] = fmaf(vsc_prev, tmp[r], acc[c][r]);
+    };
+    auto chunk_qk = [&](int c) {
+      sn[0] = qk_mfma(k_next, 0, c, sn[0]);
+      sn[1] = qk_mfma(k_next, 1, c, sn[1]);
+    };
+    auto chunk_soft = [&](int c) {
+      const int kt = c >> 1, r0 = 8 * (c & 1);
+      float p[8];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc[dt][r] *= alpha;
-    }
-
-    if (do_pv) {
-      // P codes: chunk c holds p[kt][8 half + e], e in [0, 8), as e4m3(256 p)
-      uint64_t pc[4];
+      for (int e = 0; e < 8; ++e) p[e] = __builtin_amdgcn_exp2f(fmaf(x[kt][r0 + e], csc, cb));
+      psum += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+      int lo = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
+      lo = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], lo, true);
+      int hi = __builtin_amdgcn_cvt_pk_fp8_f32(p[4], p[5], 0, false);
+      hi = __builtin_amdgcn_cvt_pk_fp8_f32(p[6], p[7], hi, true);
+      pn[2 * c] = lo;
+      pn[2 * c + 1] = hi;
+    };
+    if (pv_prev) {
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        const int kt = c >> 1, half = c & 1;
-        float pp[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) pp[e] = s[kt][8 * half + e];
-        int lo = __builtin_amdgcn_cvt_pk_fp8_f32(pp[0] * 256.f, pp[1] * 256.f, 0, false);
-        lo = __builtin_amdgcn_cvt_pk_fp8_f32(pp[2] * 256.f, pp[3] * 256.f, lo, true);
-        int hi = __builtin_amdgcn_cvt_pk_fp8_f32(pp[4] * 256.f, pp[5] * 256.f, 0, false);
-        hi = __builtin_amdgcn_cvt_pk_fp8_f32(pp[6] * 256.f, pp[7] * 256.f, hi, true);
-        pc[c] = (uint64_t)(uint32_t)lo | ((uint64_t)(uint32_t)hi << 32);
+        chunk_pv(c);
+        chunk_qk(c);
+        chunk_soft(c);
       }
-      const char* vst = stage + KBYTES;
+    } else {
 #pragma unroll
-      for (int dt = 0; dt < 4; ++dt) {
-        f32x16 tmp;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) tmp[r] = 0.f;
-        const char* vr = vst + (32 * dt + l32) * VS + 4 * hh;
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const int kb = 16 * c;  // = 32 kt + 16 half
-          const uint32_t v0 = *reinterpret_cast<const uint32_t*>(vr + kb);
-          const uint32_t v1 = *reinterpret_cast<const uint32_t*>(vr + kb + 8);
-          const uint64_t va = (uint64_t)v0 | ((uint64_t)v1 << 32);
-          tmp = __builtin_amdgcn_mfma_f32_32x32x16_fp8_fp8((long)va, (long)pc[c], tmp, 0, 0, 0);
-        }
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[dt][r] = fmaf(vsc, tmp[r], acc[dt][r]);
+      for (int c = 0; c < 4; ++c) {
+        chunk_qk(c);
+        chunk_soft(c);
       }
     }
+    l += psum;
+    pf = pn;
+    vsc_prev = vsc;
 
     if (skip_out) {
       skip_word |= (do_pv ? 0u : 1u) << (t & 31);
@@ -349,11 +424,39 @@ __global__ __launch_bounds__(256, 2) void attn_q_kernel(AttnQArgs a) {
         skip_word = 0;
       }
     }
-    if (t + 1 < cnt) st.store(smem + ((t + 1) & 1) * STAGE, tid);
+    pv_prev = do_pv;
+    jq0 = jq1;
+    jq1 = j_far;
     __syncthreads();
+  };
+
+  int t = 0;
+  for (; t + 2 <= cnt; t += 2) {
+    step(std::integral_constant<int, 0>{}, t, sA, sB);
+    step(std::integral_constant<int, 1>{}, t + 1, sB, sA);
+  }
+  if (t < cnt) step(std::integral_constant<int, 0>{}, t, sA, sB);
+
+  if (cnt > 0) {
+    if (__any(rescale != 1.f)) {
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[dt][r] *= rescale;
+    }
+    if (pv_prev) {  // P.V of the last entry, V in stage (cnt - 1) % 2
+      const char* vlast = ((cnt - 1) & 1) ? v1 : v0;
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) {
+        const f32x16 tmp = pv_mfma(vlast, dt, pf);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[dt][r] = fmaf(vsc_prev, tmp[r], acc[dt][r]);
+      }
+    }
   }
 
-  l += __shfl_xor(l, 32, 64);
+  // epilogue: O = acc / l (both carry the factor 2^8); lse = (m + log2 l - 8) ln 2
+  l = attn::xhalf_sum(l);
   if (qvalid) {
     const float inv = l > 0.f ? 1.f / l : 0.f;
     const int oe = a.o_fp32 ? 4 : 2;
@@ -374,7 +477,7 @@ __global__ __launch_bounds__(256, 2) void attn_q_kernel(AttnQArgs a) {
         }
       }
     if (a.lse && hh == 0)
-      a.lse[(int64_t)bh * a.N + qrow] = l > 0.f ? (m + __log2f(l)) * kLn2 : -INFINITY;
+      a.lse[(int64_t)bh * a.N + qrow] = l > 0.f ? (m + __log2f(l) - 8.f) * kLn2 : -INFINITY;
   }
 }
 

@@ -130,8 +130,10 @@ SA_API sa_status sparse_attn_mask_shape(const sa_params* p, int64_t* nqb, int64_
  *   predict: qbar float [B,H,NQB,D], then kbar float [B,H,NKB,D] -- the
  *            block means, left in place after the call.
  *   forward, SA_PREC_I8_FP8: Q codes int8 [B,H,N,D], K codes int8 [B,H,N,D],
- *            V codes e4m3 [B,H,NKB,D,64] (each key block stored transposed:
- *            byte (d, c) holds key j*64 + c), then float scales
+ *            V codes e4m3 [B,H,NKB,D,64] (each key block stored transposed,
+ *            keys permuted: byte (d, p) of block j holds key
+ *            j*64 + 32t + 8g + 4h + e for p = 32h + 16t + 4g + e, with
+ *            h, t in {0,1} and g, e in {0..3}), then float scales
  *            sq [B,H,NQB], sk [B,H,NKB], sv [B,H,NKB].
  *   forward, SA_PREC_NATIVE: 0 bytes. */
 SA_API sa_status sparse_attn_workspace_size(const sa_params* p, size_t* predict_ws,

@@ -116,7 +116,14 @@ def check_case(w: Workload, layout="bhnd", check_out=True):
                 codes = np.zeros((r["nkb"] * 64, w.D), dtype=np.uint8)
                 codes[:w.N] = O.e4m3_encode(vq)
                 want = codes.reshape(r["nkb"], 64, w.D).transpose(0, 2, 1)
-                np.testing.assert_array_equal(r["vt"][b, h], want)
+                # key k of a block sits at position 32h + 16t + 4g + e for
+                # k = 32t + 8g + 4h + e (the header's V-code layout)
+                k = np.arange(64)
+                pos = 32 * ((k >> 2) & 1) + 16 * (k >> 5) + 4 * ((k >> 3) & 3) + (k & 3)
+                assert sorted(pos.tolist()) == list(range(64))
+                perm = np.empty_like(want)
+                perm[:, :, pos] = want
+                np.testing.assert_array_equal(r["vt"][b, h], perm)
     log(f"   masks {n_exact}/{n_rows} exact; skips {skip_mis}/{skip_n} near-lambda "
         f"mismatches; max-abs {worst:.3g}")
     return r
