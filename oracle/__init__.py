@@ -41,6 +41,7 @@ from .sparse_attn_oracle import (  # noqa: F401
     processing_order,
     cut_length,
     predict_head,
+    group_skip,
     sparse_attention_head,
     dense_attention_head,
     oracle_head,

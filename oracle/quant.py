@@ -29,7 +29,7 @@ from typing import List, Optional
 
 import numpy as np
 
-from .sparse_attn_oracle import Params, n_blocks
+from .sparse_attn_oracle import Params, group_skip, n_blocks
 
 
 def e4m3_round(x) -> np.ndarray:
@@ -107,11 +107,11 @@ def sparse_attention_quant_head(Q, K, V, kept: List[np.ndarray], p: Params,
     skip rule as the unquantised oracle, with
     S = sm * s_q(i) * s_k(j) * (Qcode . Kcode)  (exact integer dot product) and
     the P.V term  s_v(j) * 2^-8 * sum_c e4m3(2^8 * P) * Vcode.
-    ``deltas`` collects delta_g as in the unquantised oracle.
+    ``deltas`` collects the group statistics and the skip rule (lambda or
+    recall) is applied as in the unquantised oracle.
     Returns (O, lse, skips)."""
     N, d = np.asarray(Q).shape
     sm = p.sm(d)
-    lam = float(p.lam)
     qc, qs = int8_quantize_blocks(Q, p.BQ)
     kc, ks = int8_quantize_blocks(K, p.BK)
     vq, vs = fp8_quantize_v_blocks(V, p.BK)
@@ -127,6 +127,7 @@ def sparse_attention_quant_head(Q, K, V, kept: List[np.ndarray], p: Params,
         m = np.full(nr, -np.inf)
         l = np.zeros(nr)
         acc = np.zeros((nr, d))
+        drop = np.zeros(nr)
         sk = np.zeros((len(lst), n_groups), dtype=bool)
         dl = np.full((len(lst), n_groups), -np.inf)
         for t, j in enumerate(lst):
@@ -142,20 +143,23 @@ def sparse_attention_quant_head(Q, K, V, kept: List[np.ndarray], p: Params,
             alpha[moved] = np.exp(m[moved] - mnew[moved])   # exp(-inf) = 0
             safe = np.where(np.isfinite(mnew), mnew, 0.0)
             P = np.where(np.isfinite(S), np.exp(S - safe[:, None]), 0.0)
-            l = alpha * l + P.sum(axis=1)
+            E = P.sum(axis=1)
+            l = alpha * l + E
+            drop = alpha * drop
             acc = alpha[:, None] * acc
             Pq = e4m3_round(P * 256.0) / 256.0
             delta_r = np.where(np.isfinite(mloc), mloc - safe, -np.inf)
             for g in range(n_groups):
                 gr = slice(g * p.G, min(nr, (g + 1) * p.G))
-                dg = delta_r[gr].max() if gr.start < nr else -np.inf
-                dl[t, g] = dg
-                skip = bool(dg < lam)
+                skip, dl[t, g] = group_skip(p, gr, nr, delta_r, E, l, drop)
                 if force_skip is not None:
                     skip = bool(force_skip[i][t, g])
                 sk[t, g] = skip
-                if not skip and gr.start < nr:
-                    acc[gr] += float(vs[j]) * (Pq[gr] @ vq[cols])
+                if gr.start < nr:
+                    if skip:
+                        drop[gr] += E[gr]
+                    else:
+                        acc[gr] += float(vs[j]) * (Pq[gr] @ vq[cols])
             m = mnew
         skips.append(sk)
         if deltas is not None:

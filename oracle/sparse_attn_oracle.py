@@ -46,6 +46,20 @@ O8 attention     SpargeAttn abstract, stage two (an online softmax-aware
                  when delta_g < lambda (natural-log units, strict).  A
                  skipped tile still updates m and l.  Rows with no visible
                  key in the tile contribute -inf to delta_g.
+O8' recall skip  DynSparse story ("training-free sparse attention based on
+                 cumulative energy filtering": a fixed recall suffices for
+                 accuracy, a static threshold is suboptimal, and the dynamic
+                 threshold comes from the cumulative energy of the selected
+                 tokens, which the flash-attention operator already holds).
+                 Reading (skip_rule = "recall", target recall rho): each row
+                 keeps, next to l, the energy d it has dropped so far, both
+                 relative to the same running max.  For tile t with energy
+                 E_r = sum_c exp(S_rc - m_r) and l_r already updated with it,
+                 row r may drop the tile when d_r + E_r <= (1 - rho) l_r; the
+                 group skips P.V when every row may, and then d_r += E_r.  So
+                 for every row the dropped share of the energy over the kept
+                 tiles stays <= 1 - rho at every step (recall >= rho).  Rows
+                 with no visible key in the tile (E_r = 0) never block a skip.
 O10 dense        Plain softmax(sm * Q K^T [+ causal mask]) V, the exact
                  reference for rel-L1 and for the tau=1, lambda=-inf identity.
 """
@@ -74,6 +88,8 @@ class Params:
     rule: str = "topcdf"           # "topcdf" | "energy"
     keep_prefix_kblocks: int = 0
     G: int = 32                    # rows per skip group
+    skip_rule: str = "lambda"      # "lambda" (O8) | "recall" (O8')
+    recall: float = 1.0            # rho of the recall rule
 
     def sm(self, d: int) -> float:
         return float(self.sm_scale) if self.sm_scale else 1.0 / math.sqrt(d)
@@ -206,6 +222,30 @@ def predict_head(Q: np.ndarray, K: np.ndarray, p: Params) -> dict:
 
 
 # --------------------------------------------------------------------- O8
+def group_skip(p: Params, gr: slice, nr: int, delta_r: np.ndarray, E: np.ndarray,
+               l: np.ndarray, drop: np.ndarray):
+    """The skip decision of one row group for one tile, and its statistic.
+
+    lambda (O8): stat = delta_g = max over the group's rows of
+    (local max - new running max); skip when stat < lambda.
+    recall (O8'): stat = min over the group's rows of the relative slack
+    ((1 - rho) l_r - d_r - E_r) / l_r (+inf for a row with l_r = 0); skip
+    when stat >= 0.  ``drop`` holds d_r, already rescaled to the new max.
+    """
+    if p.skip_rule == "lambda":
+        dg = float(delta_r[gr].max()) if gr.start < nr else -np.inf
+        return bool(dg < float(p.lam)), dg
+    if gr.start >= nr:
+        return True, np.inf
+    if p.skip_rule != "recall":
+        raise ValueError(p.skip_rule)
+    omr = 1.0 - float(p.recall)
+    lg, dg, eg = l[gr], drop[gr], E[gr]
+    slack = np.where(lg > 0, (omr * lg - dg - eg) / np.where(lg > 0, lg, 1.0), np.inf)
+    st = float(slack.min())
+    return bool(st >= 0.0), st
+
+
 def sparse_attention_head(Q, K, V, kept: List[np.ndarray], p: Params,
                           force_skip: Optional[List[np.ndarray]] = None,
                           deltas: Optional[list] = None):
@@ -213,8 +253,9 @@ def sparse_attention_head(Q, K, V, kept: List[np.ndarray], p: Params,
 
     ``kept[i]`` lists key blocks for query block i in processing order.
     ``force_skip[i]`` (bool [len(kept[i]), n_groups]) replaces the skip
-    decision when given.  If ``deltas`` is a list, the group statistics
-    delta_g (float [len(kept[i]), n_groups]) are appended to it.  Returns
+    decision when given (and the recall rule's dropped energy follows the
+    forced decisions).  If ``deltas`` is a list, the group statistics of
+    ``group_skip`` (float [len(kept[i]), n_groups]) are appended to it.  Returns
     (O [N,d], lse [N] natural log, skips: list of bool
     [len(kept[i]), n_groups]).
     """
@@ -223,7 +264,6 @@ def sparse_attention_head(Q, K, V, kept: List[np.ndarray], p: Params,
     V = np.asarray(V, dtype=np.float64)
     N, d = Q.shape
     sm = p.sm(d)
-    lam = float(p.lam)
     n_groups = (p.BQ + p.G - 1) // p.G
     O = np.zeros((N, d))
     lse = np.full(N, -np.inf)
@@ -234,6 +274,7 @@ def sparse_attention_head(Q, K, V, kept: List[np.ndarray], p: Params,
         m = np.full(nr, -np.inf)
         l = np.zeros(nr)
         acc = np.zeros((nr, d))
+        drop = np.zeros(nr)
         sk = np.zeros((len(lst), n_groups), dtype=bool)
         dl = np.full((len(lst), n_groups), -np.inf)
         for t, j in enumerate(lst):
@@ -248,19 +289,22 @@ def sparse_attention_head(Q, K, V, kept: List[np.ndarray], p: Params,
             alpha[moved] = np.exp(m[moved] - mnew[moved])   # exp(-inf) = 0
             safe = np.where(np.isfinite(mnew), mnew, 0.0)
             P = np.where(np.isfinite(S), np.exp(S - safe[:, None]), 0.0)
-            l = alpha * l + P.sum(axis=1)
+            E = P.sum(axis=1)
+            l = alpha * l + E
+            drop = alpha * drop
             acc = alpha[:, None] * acc
             delta_r = np.where(np.isfinite(mloc), mloc - safe, -np.inf)
             for g in range(n_groups):
                 gr = slice(g * p.G, min(nr, (g + 1) * p.G))
-                dg = delta_r[gr].max() if gr.start < nr else -np.inf
-                dl[t, g] = dg
-                skip = bool(dg < lam)
+                skip, dl[t, g] = group_skip(p, gr, nr, delta_r, E, l, drop)
                 if force_skip is not None:
                     skip = bool(force_skip[i][t, g])
                 sk[t, g] = skip
-                if not skip and gr.start < nr:
-                    acc[gr] += P[gr] @ V[cols]
+                if gr.start < nr:
+                    if skip:
+                        drop[gr] += E[gr]
+                    else:
+                        acc[gr] += P[gr] @ V[cols]
             m = mnew
         skips.append(sk)
         if deltas is not None:
