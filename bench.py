@@ -59,6 +59,10 @@ def parse():
     ap.add_argument("--workload", default="wan_video")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-sweep", action="store_true")
+    ap.add_argument("--skip-rule", default="lambda", choices=("lambda", "recall"),
+                    help="stage-two skip rule of the timed configuration")
+    ap.add_argument("--recall", type=float, default=0.95,
+                    help="target recall of the recall skip rule")
     ap.add_argument("--no-peaks", action="store_true",
                     help="skip the GEMM / copy reference measurements")
     ap.add_argument("--cpu-blocks", type=int, default=256,
@@ -137,13 +141,14 @@ def gen_inputs(w, threads=16):
 class Runner:
     """Owns the device buffers of one configuration and runs the two calls."""
 
-    def __init__(self, sa, torch, w, q, k, v, tau):
+    def __init__(self, sa, torch, w, q, k, v, tau, skip_rule="lambda", recall=1.0):
         self.sa, self.torch, self.w = sa, torch, w
         self.q, self.k, self.v = q, k, v
         self.o = torch.empty_like(q)
         self.p = sa.make_params(w.B, w.H, w.N, w.D, dtype=w.dtype, causal=w.causal, tau=tau,
                                 lam=w.lam, rule=w.rule, prec=w.prec,
-                                keep_prefix_kblocks=w.keep_prefix_kblocks)
+                                keep_prefix_kblocks=w.keep_prefix_kblocks,
+                                skip_rule=skip_rule, recall=recall)
         self.nqb, self.nkb = sa.sparse_attn_mask_shape(self.p)
         pws, fws = sa.sparse_attn_workspace_size(self.p)
         dev = q.device
@@ -231,13 +236,14 @@ def rel_l1_sample(w, Q, K, V, O_gpu, oracle):
     return num / den, f"heads {heads}, query blocks {blocks}"
 
 
-def cpu_baseline(w, Q, K, V, tau, blocks):
+def cpu_baseline(w, Q, K, V, tau, blocks, skip_rule="lambda", recall=1.0):
     """The fp64 oracle as it stands, single-threaded, on head 0: stage one
     for the whole head plus stage two for the first `blocks` query blocks."""
     import oracle as O
     from threadpoolctl import threadpool_limits
     p = O.Params(causal=w.causal, tau=float(np.float32(tau)), lam=w.lam, rule=w.rule,
-                 keep_prefix_kblocks=w.keep_prefix_kblocks)
+                 keep_prefix_kblocks=w.keep_prefix_kblocks, skip_rule=skip_rule,
+                 recall=float(np.float32(recall)))
     q, k, v = Q[0, 0], K[0, 0], V[0, 0]
     with threadpool_limits(1):
         t0 = time.perf_counter()
@@ -280,8 +286,10 @@ def main():
     q, k, v = (torch.from_numpy(x).to(tdt).to(dev) for x in (Q, K, V))
     dense = w.dense_flops()
 
-    def measure(tau, steps, warmup):
-        r = Runner(sa, torch, w, q, k, v, tau)
+    def measure(tau, steps, warmup, skip_rule=None, recall=None):
+        r = Runner(sa, torch, w, q, k, v, tau,
+                   skip_rule=skip_rule or args.skip_rule,
+                   recall=args.recall if recall is None else recall)
         ms, pred_ms, fwd_ms, wall = r.time_steps(steps, warmup)
         cnt, skipped = r.decisions()
         adm = admissible_count(w, r.nqb, r.nkb)
@@ -308,6 +316,7 @@ def main():
           flush=True)
 
     sweep = []
+    recall_sweep = []
     if not args.no_sweep and w.name == "wan_video":
         for tau in (0.9, 0.95, 0.99):
             rs, ms_ = measure(tau, max(3, args.steps // 4), 1)
@@ -319,11 +328,25 @@ def main():
                               dense_equiv_tflops=round(dense / (ms_["ms"] * 1e-3) / 1e12, 2)))
             del rs
             print(f"[bench] sweep tau={tau}: {sweep[-1]}", file=sys.stderr, flush=True)
+        # the recall skip rule (dynamic threshold from the cumulative energy)
+        # against the static lambda, at the headline tau
+        for rho in (0.99, 0.95, 0.9):
+            rs, ms_ = measure(w.tau, max(3, args.steps // 4), 1, skip_rule="recall", recall=rho)
+            o_s = rs.o.float().cpu().numpy()[0]
+            rl, _ = rel_l1_sample(w, Q, K, V, o_s, oracle)
+            recall_sweep.append(dict(recall=rho, tau=w.tau, sparsity=round(ms_["sparsity"], 5),
+                                     pv_skip_fraction=round(ms_["skip"], 5),
+                                     rel_l1=round(rl, 6), ms_per_step=round(ms_["ms"], 4),
+                                     dense_equiv_tflops=round(dense / (ms_["ms"] * 1e-3) / 1e12,
+                                                              2)))
+            del rs
+            print(f"[bench] recall rule rho={rho}: {recall_sweep[-1]}", file=sys.stderr,
+                  flush=True)
 
     cpu = None
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle sample", file=sys.stderr, flush=True)
-        cpu = cpu_baseline(w, Q, K, V, w.tau, args.cpu_blocks)
+        cpu = cpu_baseline(w, Q, K, V, w.tau, args.cpu_blocks, args.skip_rule, args.recall)
 
     peaks = None if args.no_peaks else measured_peaks(torch, dev)
 
@@ -348,7 +371,9 @@ def main():
         "data": data_description(w),
         "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "D": w.D,
                    "causal": w.causal, "tau": w.tau, "lambda": w.lam, "rule": w.rule,
-                   "block_q": 128, "block_k": 64, "lambda_group_rows": 32},
+                   "block_q": 128, "block_k": 64, "lambda_group_rows": 32,
+                   "skip_rule": args.skip_rule,
+                   **({"recall": args.recall} if args.skip_rule == "recall" else {})},
         "sparsity": round(m["sparsity"], 5),
         "pv_skip_fraction": round(m["skip"], 5),
         "rel_l1_vs_dense": round(rel, 6),
@@ -362,6 +387,7 @@ def main():
                      "executed_flops_per_launch": m["exec_flops"],
                      "measured_peaks": peaks},
         "tau_sweep": sweep,
+        "recall_rule_sweep": recall_sweep,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

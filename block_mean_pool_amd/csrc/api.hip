@@ -52,6 +52,10 @@ sa_status check_params(const sa_params* p, sa::Geometry* g, bool* empty) {
   if (!(p->tau > 0.f) || std::isnan(p->tau))
     return fail(SA_ERR_INVALID_ARG, "tau=%g (must be in (0, 1]; >= 1 keeps all)", (double)p->tau);
   if (std::isnan(p->lambda)) return fail(SA_ERR_INVALID_ARG, "lambda is NaN");
+  if (p->skip_rule != SA_SKIP_LAMBDA && p->skip_rule != SA_SKIP_RECALL)
+    return fail(SA_ERR_INVALID_ARG, "skip_rule=%d", p->skip_rule);
+  if (p->skip_rule == SA_SKIP_RECALL && !(p->recall > 0.f && p->recall <= 1.f))
+    return fail(SA_ERR_INVALID_ARG, "recall=%g (must be in (0, 1])", (double)p->recall);
   if (!(p->sm_scale >= 0.f) || std::isinf(p->sm_scale))
     return fail(SA_ERR_INVALID_ARG, "sm_scale=%g", (double)p->sm_scale);
   if (p->keep_prefix_kblocks < 0) return fail(SA_ERR_INVALID_ARG, "keep_prefix_kblocks < 0");
@@ -207,6 +211,8 @@ sa_status sparse_attn_forward(const sa_params* p, const void* q, const void* k, 
   a.causal = p->causal;
   a.sm = softmax_scale(p);
   a.lambda = p->lambda;
+  a.recall_on = p->skip_rule == SA_SKIP_RECALL;
+  a.recall = p->recall;
   a.o_fp32 = p->o_fp32 || p->dtype == SA_F32;
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e;

@@ -167,6 +167,7 @@ __global__ __launch_bounds__(256, (sizeof(T) == 4 && D == 128) ? 1 : 2) void att
     for (int r = 0; r < 16; ++r) acc[dt][r] = 0.f;
   float m = -INFINITY;  // running max, log2 units
   float l = 0.f;        // this lane's share of the running sum
+  float drop = 0.f;     // recall rule: energy this row has dropped (row total)
   uint32_t skip_word = 0;
 
   // V^T transpose reads: this lane's source key (within a 16-key chunk, +8
@@ -233,6 +234,12 @@ __global__ __launch_bounds__(256, (sizeof(T) == 4 && D == 128) ? 1 : 2) void att
       }
     l = alpha * l + psum;
     m = mnew;
+    if (a.recall_on) {  // drop the tile if the row's dropped share stays <= 1 - recall
+      drop *= alpha;
+      const float E = xhalf_sum(psum), L = xhalf_sum(l);
+      do_pv = __any(!(drop + E <= a.omr * L));
+      if (!do_pv) drop += E;
+    }
     if (__any(alpha != 1.f)) {
 #pragma unroll
       for (int dt = 0; dt < TL::NDT; ++dt)

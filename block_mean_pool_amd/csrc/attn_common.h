@@ -46,6 +46,8 @@ struct AttnArgs {
   float lam2;   // lambda * log2(e)
   int lam_off;  // lambda == -inf: never skip
   int o_fp32;   // O stored as fp32
+  int recall_on;  // recall skip rule instead of lambda
+  float omr;      // 1 - recall
 };
 
 template <typename T, int D>
@@ -94,6 +96,9 @@ inline AttnArgs make_args(const ForwardLaunch& f) {
   a.lam_off = f.lambda == -INFINITY;
   a.lam2 = a.lam_off ? 0.f : f.lambda * kLog2e;
   a.o_fp32 = f.o_fp32;
+  a.recall_on = f.recall_on;
+  a.omr = 1.0f - f.recall;
+  if (a.recall_on) a.lam_off = 1;
   return a;
 }
 

@@ -11,7 +11,8 @@
 //           (buffer_load ... lds, no staging registers), into the stages
 //           whose previous contents iteration t-1 finished reading;
 //     scalar part of the softmax of tile t: masking (edge tiles only),
-//           row max, lambda ballot, running max;
+//           row max, lambda ballot, running max (the recall rule decides
+//           after the region, once tile t's energy is summed);
 //     one region, in four chunks of 16 keys: the 4 MFMAs of P.V for tile
 //           t-1 (not issued when tile t-1 was skipped), 4 MFMAs of Q.K^T
 //           for tile t+1, and 8 exp2/FMA/add plus bf16 packing of tile t's
@@ -45,6 +46,7 @@ struct Soft {
   float mu;       // exponent offset, mu <= m
   float l;        // this lane's share of sum exp2(c S - mu)
   float rescale;  // pending factor for acc
+  float drop;     // recall rule: energy the row has dropped, same offset as l
 };
 
 template <int I>
@@ -178,7 +180,7 @@ __global__ __launch_bounds__(256, 2) void attn_pipe_kernel(AttnArgs a) {
   u32x4 pf[4];  // P of the previous tile, bf16, as the P.V B operand
 #pragma unroll
   for (int c = 0; c < 4; ++c) pf[c] = u32x4{0u, 0u, 0u, 0u};
-  Soft ss{-INFINITY, -INFINITY, 0.f, 1.f};
+  Soft ss{-INFINITY, -INFINITY, 0.f, 1.f, 0.f};
   bool pv_prev = false;
 
   int kq0 = entry_key(0), kq1 = entry_key(1);  // keys of entries t, t + 1
@@ -249,6 +251,7 @@ __global__ __launch_bounds__(256, 2) void attn_pipe_kernel(AttnArgs a) {
       const float mu_new = fmaxf(ss.mu, mnew);
       const float f = (mu_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(ss.mu - mu_new);
       ss.l *= f;
+      ss.drop *= f;
       ss.rescale *= f;
       ss.mu = mu_new;
     }
@@ -303,6 +306,11 @@ __global__ __launch_bounds__(256, 2) void attn_pipe_kernel(AttnArgs a) {
     ss.l += psum;
 #pragma unroll
     for (int c = 0; c < 4; ++c) pf[c] = pn[c];
+    if (a.recall_on) {  // drop the tile if every row's dropped share stays <= 1 - recall
+      const float E = xhalf_sum(psum), L = xhalf_sum(ss.l);
+      do_pv = __any(!(ss.drop + E <= a.omr * L));
+      if (!do_pv) ss.drop += E;
+    }
 
     if (skip_out) {
       skip_word |= (do_pv ? 0u : 1u) << (t & 31);

@@ -150,6 +150,8 @@ struct AttnQArgs {
   float c2, lam2;
   int lam_off;
   int o_fp32;
+  int recall_on;  // recall skip rule instead of lambda
+  float omr;      // 1 - recall
 };
 
 typedef __attribute__((address_space(3))) void lds_void_q;
@@ -286,6 +288,7 @@ __global__ __launch_bounds__(256, 2) void attn_q_kernel(AttnQArgs a) {
 #pragma unroll
   for (int e = 0; e < 8; ++e) pf[e] = 0;
   float m = -INFINITY, l = 0.f, rescale = 1.f, vsc_prev = 0.f;
+  float drop = 0.f;  // recall rule: energy the row has dropped, same scale as l
   bool pv_prev = false;
 
   int jq0 = entry_blk(0), jq1 = entry_blk(1);  // blocks of entries t, t + 1
@@ -363,6 +366,7 @@ __global__ __launch_bounds__(256, 2) void attn_q_kernel(AttnQArgs a) {
     if (mnew != m) {
       const float f = (m == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m - mnew);
       l *= f;
+      drop *= f;
       rescale = f;
       m = mnew;
     }
@@ -416,6 +420,11 @@ __global__ __launch_bounds__(256, 2) void attn_q_kernel(AttnQArgs a) {
     l += psum;
     pf = pn;
     vsc_prev = vsc;
+    if (a.recall_on) {  // drop the tile if every row's dropped share stays <= 1 - recall
+      const float E = attn::xhalf_sum(psum), L = attn::xhalf_sum(l);
+      do_pv = __any(!(drop + E <= a.omr * L));
+      if (!do_pv) drop += E;
+    }
 
     if (skip_out) {
       skip_word |= (do_pv ? 0u : 1u) << (t & 31);
@@ -517,6 +526,9 @@ hipError_t launch_attn_q(const ForwardLaunch& f, hipStream_t s) {
   a.lam_off = f.lambda == -INFINITY;
   a.lam2 = a.lam_off ? 0.f : f.lambda * kLog2e;
   a.o_fp32 = f.o_fp32;
+  a.recall_on = f.recall_on;
+  a.omr = 1.0f - f.recall;
+  if (a.recall_on) a.lam_off = 1;
   if (f.causal)
     hipLaunchKernelGGL((attn_q_kernel<true>), dim3(a.nwg), dim3(256), 0, s, a);
   else

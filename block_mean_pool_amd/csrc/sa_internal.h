@@ -42,6 +42,8 @@ struct ForwardLaunch {
   int o_fp32;                // O stored as fp32 (else bf16)
   float sm;
   float lambda;
+  int recall_on;             // skip rule: 0 lambda, 1 recall
+  float recall;              // target recall rho (recall rule)
   // quantised variant: workspace buffers
   int8_t* qc;                // [B,H,N,D]
   int8_t* kc;                // [B,H,N,D]

@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define SPARSE_ATTN_VERSION 1
+#define SPARSE_ATTN_VERSION 2
 
 #if defined(__GNUC__)
 #define SA_API __attribute__((visibility("default")))
@@ -85,6 +85,13 @@ enum { SA_PREC_NATIVE = 0, SA_PREC_I8_FP8 = 1 };
  * n_j * exp(s_j), n_j the number of keys in block j (a cumulative-energy
  * target; equal to TOPCDF when every block is full). */
 enum { SA_RULE_TOPCDF = 0, SA_RULE_ENERGY = 1 };
+/* Skip rule of stage two (see sparse_attn_forward).  LAMBDA: the static
+ * threshold `lambda` on (tile max - running max), the SpargeAttn abstract's
+ * stage-two filter.  RECALL: a dynamic threshold from the cumulative energy
+ * the online softmax already holds, keeping at least a share `recall` of
+ * each row's energy over the kept tiles (the DynSparse story's "cumulative
+ * energy filtering" with a fixed recall). */
+enum { SA_SKIP_LAMBDA = 0, SA_SKIP_RECALL = 1 };
 
 typedef struct sa_params {
   int32_t B, H, N, D;          /* batch, heads, tokens, head dimension         */
@@ -105,6 +112,9 @@ typedef struct sa_params {
                                /* 0: O has `dtype` (bf16 O = the fp32 result  */
                                /* rounded to nearest even)                    */
   int64_t stride_b, stride_h, stride_n;  /* element strides; 0 -> packed       */
+  int32_t skip_rule;           /* SA_SKIP_LAMBDA | SA_SKIP_RECALL              */
+  float recall;                /* SA_SKIP_RECALL: target share rho in (0, 1]   */
+                               /* of each row's energy; ignored otherwise      */
 } sa_params;
 
 /* The mask: output of predict, input of forward.  Caller-allocated; sizes
@@ -157,9 +167,16 @@ SA_API sa_status sparse_attn_predict(const sa_params* p, const void* q, const vo
 
 /* Stage two.  For each query block, processes mask->kept_idx in list order
  * with an online softmax (running max m, running sum l).  For each group of
- * 32 consecutive rows (one wavefront), delta = max over the group's rows of
- * (tile max - new running max); when delta < lambda the group skips the
- * tile's P.V product (m and l are still updated).  Writes
+ * 32 consecutive rows (one wavefront) and each tile:
+ *   SA_SKIP_LAMBDA: delta = max over the group's rows of (tile max - new
+ *     running max); when delta < lambda the group skips the tile's P.V
+ *     product;
+ *   SA_SKIP_RECALL: each row also keeps d, the energy it has dropped so far
+ *     (rescaled with l when m moves); with E the row's energy in the tile
+ *     (sum of exp(S - m)) and l already including it, the group skips when
+ *     d + E <= (1 - recall) * l for every row, and each row then adds E to
+ *     d.  So every row drops at most a share 1 - recall of its energy.
+ * m and l are updated either way.  Writes
  *   o          [B,H,N,D] dtype (fp32 if o_fp32): acc / l;
  *   lse        optional float [B,H,N]: m + log(l) in natural-log units;
  *   skip_bits  optional uint32 [B,H,NQB,4,ceil(NKB/32)]: bit (t % 32) of

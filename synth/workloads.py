@@ -164,6 +164,8 @@ class Workload:
     structure: str = "field"
     grid: Optional[Tuple[int, int, int]] = None
     n_text: int = 0
+    skip_rule: str = "lambda"  # "lambda" or "recall" (stage-two skip rule)
+    recall: float = 1.0        # target recall of the "recall" rule
 
     def head(self, b: int, h: int, n: Optional[int] = None):
         """(Q, K, V) float32 arrays [N, D] for one (b, h), rounded to the

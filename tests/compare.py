@@ -77,6 +77,28 @@ def compare_masks(gpu_kept, preds, tau):
     return n, exact, fails
 
 
+def compare_recall_skips(gpu_skips, stats, tol):
+    """Recall rule.  ``stats`` are the oracle's group statistics (relative
+    slack) computed along the GPU's own skip history (the oracle run with
+    force_skip = the GPU's bits), so an earlier near-threshold difference
+    does not cascade; the oracle would skip where stat >= 0.  A differing bit
+    is excused when |stat| <= tol."""
+    n = mism = 0
+    fails = []
+    for i, (g, st) in enumerate(zip(gpu_skips, stats)):
+        ng = st.shape[1]
+        gg = g[:, :ng]
+        n += gg.size
+        diff = gg != (st >= 0)
+        if diff.any():
+            mism += int(diff.sum())
+            bad = diff & ~(np.abs(st) <= tol)
+            if bad.any():
+                t, gi = np.argwhere(bad)[0]
+                fails.append((i, int(t), int(gi), float(st[t, gi])))
+    return n, mism, fails
+
+
 def compare_skips(gpu_skips, oracle_skips, oracle_deltas, lam, tol):
     """All lists are per query block: bool/float [cnt, n_groups]."""
     n = mism = 0

@@ -31,10 +31,19 @@ def test_binding_exposes_the_same_names():
 
 
 def test_struct_layout_matches_header():
-    # 10 int32 + 3 float + 3 int32 = 64 bytes, + 3 int64
-    assert ctypes.sizeof(sa.SaParams) == 88
+    # 10 int32 + 3 float + 3 int32 = 64 bytes, + 3 int64, + int32 + float
+    assert ctypes.sizeof(sa.SaParams) == 96
     assert sa.SaParams.stride_b.offset == 64
+    assert sa.SaParams.skip_rule.offset == 88
+    assert sa.SaParams.recall.offset == 92
     assert ctypes.sizeof(sa.SaMask) == 24
+    # field order and names as declared in the header
+    text = open(sa.HEADER).read()
+    body = text[text.index("typedef struct sa_params {"):text.index("} sa_params;")]
+    body = re.sub(r"/\*.*?\*/", "", body, flags=re.S)
+    declared = re.findall(r"\b(\w+)\s*[,;]", body.split("{", 1)[1])
+    ctypes_names = [f[0] for f in sa.SaParams._fields_]
+    assert [n.replace("lambda", "lam") if n == "lambda" else n for n in declared] == ctypes_names
 
 
 def test_shapes_and_workspace():
@@ -47,7 +56,7 @@ def test_shapes_and_workspace():
     _, fw = sa.sparse_attn_workspace_size(q)
     bh = 16
     assert fw == 2 * bh * 65536 * 128 + bh * 1024 * 128 * 64 + bh * 512 * 4 + 2 * bh * 1024 * 4
-    assert sa.sparse_attn_info() == (32, 1)
+    assert sa.sparse_attn_info() == (32, 2)
     assert sa.sparse_attn_status_str(3) == "SA_ERR_WORKSPACE"
     assert sa.sparse_attn_status_str(99) == "SA_ERR_UNKNOWN"
     p = sa.make_params(2, 3, 0, 64)
@@ -68,6 +77,10 @@ def test_shapes_and_workspace():
     (dict(N=300000), sa.SA_ERR_UNSUPPORTED),
     (dict(strides=(0, 0, 100)), sa.SA_ERR_INVALID_ARG),
     (dict(strides=(0, 0, 130)), sa.SA_ERR_INVALID_ARG),
+    (dict(skip_rule=2), sa.SA_ERR_INVALID_ARG),
+    (dict(skip_rule="recall", recall=0.0), sa.SA_ERR_INVALID_ARG),
+    (dict(skip_rule="recall", recall=1.5), sa.SA_ERR_INVALID_ARG),
+    (dict(skip_rule="recall", recall=float("nan")), sa.SA_ERR_INVALID_ARG),
 ])
 def test_invalid_params_rejected_before_launch(kw, code):
     base = dict(B=1, H=2, N=1000, D=128)

@@ -12,6 +12,7 @@ The oracle cannot redo whole workloads in seconds, so:
     output against the oracle run under the GPU's own mask and skip bits,
     and the bf16 output as that result rounded.
 """
+import dataclasses
 import math
 import sys
 import time
@@ -52,15 +53,17 @@ def decode_skips(bits, cnt):
     return ((bits[:, t // 32] >> (t % 32).astype(np.uint32)) & 1).T.astype(bool)
 
 
-@pytest.mark.parametrize("name,heads,nblocks", [
-    ("tiny_fp32", None, None),
-    ("wan_video", [0, 23], 5),
-    ("hunyuan_video", [7], 4),
-    ("lm_causal", [0, 31], 5),
-    ("quant_long", [5], 4),
+@pytest.mark.parametrize("name,heads,nblocks,over", [
+    ("tiny_fp32", None, None, {}),
+    ("wan_video", [0, 23], 5, {}),
+    ("hunyuan_video", [7], 4, {}),
+    ("lm_causal", [0, 31], 5, {}),
+    ("quant_long", [5], 4, {}),
+    ("wan_video", [11], 4, dict(skip_rule="recall", recall=0.95)),
+    ("lm_causal", [9], 4, dict(skip_rule="recall", recall=0.9)),
 ])
-def test_fullsize_parity(name, heads, nblocks):
-    w = make_workload(name)
+def test_fullsize_parity(name, heads, nblocks, over):
+    w = dataclasses.replace(make_workload(name), **over)
     t0 = time.perf_counter()
     Q, K, V = generate(w)
     log(f"[fullsize] {name} B={w.B} H={w.H} N={w.N} D={w.D} generated in "
@@ -69,7 +72,8 @@ def test_fullsize_parity(name, heads, nblocks):
     dev = torch.device("cuda:0")
     q, k, v = (torch.from_numpy(x).to(tdt).to(dev) for x in (Q, K, V))
     kw = dict(dtype=w.dtype, causal=w.causal, tau=w.tau, lam=w.lam, rule=w.rule, prec=w.prec,
-              keep_prefix_kblocks=w.keep_prefix_kblocks)
+              keep_prefix_kblocks=w.keep_prefix_kblocks, skip_rule=w.skip_rule,
+              recall=w.recall)
     p = sa.make_params(w.B, w.H, w.N, w.D, **kw)
     p32 = sa.make_params(w.B, w.H, w.N, w.D, o_fp32=True, **kw)
     nqb, nkb = sa.sparse_attn_mask_shape(p)
@@ -119,7 +123,8 @@ def test_fullsize_parity(name, heads, nblocks):
     lam32 = float(np.float32(w.lam))
     op = O.Params(causal=w.causal, tau=tau32, lam=lam32, rule=w.rule,
                   keep_prefix_kblocks=w.keep_prefix_kblocks,
-                  sm_scale=float(np.float32(1.0 / math.sqrt(w.D))))
+                  sm_scale=float(np.float32(1.0 / math.sqrt(w.D))),
+                  skip_rule=w.skip_rule, recall=float(np.float32(w.recall)))
     mode = w.prec if w.prec == "i8fp8" else w.dtype
     if heads is None:
         heads = list(range(w.H))
@@ -142,11 +147,17 @@ def test_fullsize_parity(name, heads, nblocks):
               else np.zeros((0, 4), dtype=bool) for i in range(nqb)]
         deltas = []
         fn = O.sparse_attention_quant_head if w.prec == "i8fp8" else O.sparse_attention_head
-        _, _, osk = fn(qh, kh, vh, sub_kept, op, deltas=deltas)
-        ns, mis, sf = compare.compare_skips([gs[i] for i in blocks], [osk[i] for i in blocks],
-                                            [deltas[i] for i in blocks], lam32, SKIP_TOL[mode])
+        if w.skip_rule == "recall":
+            Oref, _, _ = fn(qh, kh, vh, sub_kept, op, force_skip=gs, deltas=deltas)
+            ns, mis, sf = compare.compare_recall_skips([gs[i] for i in blocks],
+                                                       [deltas[i] for i in blocks], 1e-4)
+        else:
+            _, _, osk = fn(qh, kh, vh, sub_kept, op, deltas=deltas)
+            ns, mis, sf = compare.compare_skips([gs[i] for i in blocks], [osk[i] for i in blocks],
+                                                [deltas[i] for i in blocks], lam32,
+                                                SKIP_TOL[mode])
+            Oref, _, _ = fn(qh, kh, vh, sub_kept, op, force_skip=gs)
         assert not sf, f"{name} head {h}: skip mismatch {sf[:3]}"
-        Oref, _, _ = fn(qh, kh, vh, sub_kept, op, force_skip=gs)
         rows = np.concatenate([np.arange(i * 128, min(w.N, (i + 1) * 128)) for i in blocks])
         og = o32[0, h].cpu().numpy()
         err = float(np.abs(og[rows] - Oref[rows]).max())

@@ -35,6 +35,7 @@ import gpu_harness  # noqa: E402
 
 OUT_TOL = {"bf16": 1e-2, "f32": 1e-2, "i8fp8": 5e-2}
 SKIP_TOL = {"bf16": 1e-3, "f32": 1e-4, "i8fp8": 1e-3}
+RECALL_TOL = 1e-4  # relative slack of the recall rule (fp32 sums vs fp64)
 
 
 def log(*a):
@@ -53,20 +54,21 @@ def stacked(w: Workload):
 def check_case(w: Workload, layout="bhnd", check_out=True):
     log(f"[case] {w.name} B={w.B} H={w.H} N={w.N} D={w.D} {w.dtype} causal={w.causal} "
         f"tau={w.tau} lam={w.lam} rule={w.rule} prec={w.prec} kp={w.keep_prefix_kblocks} "
-        f"layout={layout}")
+        f"skip={w.skip_rule}/{w.recall} layout={layout}")
     Q, K, V = stacked(w)
     tau32 = float(np.float32(w.tau))
     lam32 = float(np.float32(w.lam))
     r = gpu_harness.run(Q, K, V, dtype=w.dtype, causal=w.causal, tau=w.tau, lam=w.lam,
                         rule=w.rule, prec=w.prec, keep_prefix_kblocks=w.keep_prefix_kblocks,
-                        layout=layout)
+                        layout=layout, skip_rule=w.skip_rule, recall=w.recall)
     p = O.Params(BQ=128, BK=64, causal=w.causal, tau=tau32, lam=lam32, rule=w.rule,
                  keep_prefix_kblocks=w.keep_prefix_kblocks, G=32,
-                 sm_scale=float(np.float32(1.0 / math.sqrt(w.D))))
+                 sm_scale=float(np.float32(1.0 / math.sqrt(w.D))),
+                 skip_rule=w.skip_rule, recall=float(np.float32(w.recall)))
     mode = w.prec if w.prec == "i8fp8" else w.dtype
     worst = 0.0
     n_rows = n_exact = 0
-    skip_n = skip_mis = 0
+    skip_n = skip_mis = n_skipped = 0
     for b in range(w.B):
         for h in range(w.H):
             hid = b * w.H + h
@@ -82,20 +84,23 @@ def check_case(w: Workload, layout="bhnd", check_out=True):
             if not check_out:
                 continue
             gk = r["kept"][hid]
-            deltas = []
-            if w.prec == "i8fp8":
-                _, _, osk = O.sparse_attention_quant_head(q, k, v, gk, p, deltas=deltas)
-            else:
-                _, _, osk = O.sparse_attention_head(q, k, v, gk, p, deltas=deltas)
             gs = r["skips"][hid]
-            n, mis, sf = compare.compare_skips(gs, osk, deltas, lam32, SKIP_TOL[mode])
+            fn = O.sparse_attention_quant_head if w.prec == "i8fp8" else O.sparse_attention_head
+            if w.skip_rule == "recall":
+                # the rule's state follows the skips taken: evaluate the
+                # oracle's decisions along the GPU's own history
+                stats = []
+                Oref, lse_ref, _ = fn(q, k, v, gk, p, force_skip=gs, deltas=stats)
+                n, mis, sf = compare.compare_recall_skips(gs, stats, RECALL_TOL)
+            else:
+                deltas = []
+                _, _, osk = fn(q, k, v, gk, p, deltas=deltas)
+                n, mis, sf = compare.compare_skips(gs, osk, deltas, lam32, SKIP_TOL[mode])
+                Oref, lse_ref, _ = fn(q, k, v, gk, p, force_skip=gs)
             assert not sf, f"skip mismatch head {hid}: {sf[:3]}"
             skip_n += n
             skip_mis += mis
-            if w.prec == "i8fp8":
-                Oref, lse_ref, _ = O.sparse_attention_quant_head(q, k, v, gk, p, force_skip=gs)
-            else:
-                Oref, lse_ref, _ = O.sparse_attention_head(q, k, v, gk, p, force_skip=gs)
+            n_skipped += int(sum(int(s.sum()) for s in gs))
             err = float(np.abs(r["O"][b, h] - Oref).max())
             worst = max(worst, err)
             assert err <= OUT_TOL[mode], f"head {hid}: max-abs {err}"
@@ -124,8 +129,10 @@ def check_case(w: Workload, layout="bhnd", check_out=True):
                 perm = np.empty_like(want)
                 perm[:, :, pos] = want
                 np.testing.assert_array_equal(r["vt"][b, h], perm)
-    log(f"   masks {n_exact}/{n_rows} exact; skips {skip_mis}/{skip_n} near-lambda "
-        f"mismatches; max-abs {worst:.3g}")
+    log(f"   masks {n_exact}/{n_rows} exact; {n_skipped}/{skip_n} group-tiles skipped, "
+        f"{skip_mis} near-threshold mismatches; max-abs {worst:.3g}")
+    if check_out and w.skip_rule == "recall" and w.recall < 1.0:
+        assert n_skipped > 0, "the case does not exercise the recall rule"
     return r
 
 
@@ -148,6 +155,19 @@ CASES = [
        rule="energy", prec="i8fp8"),
     wl("quant_causal", 108, 1, 1, 700, 128, structure="lm", causal=True, tau=0.9,
        lam=-5.0, prec="i8fp8"),
+    # recall skip rule (dynamic threshold from the cumulative energy)
+    wl("recall_field", 113, 2, 2, 1000, 128, grid=(10, 10, 10), tau=0.95,
+       skip_rule="recall", recall=0.95),
+    wl("recall_causal", 114, 1, 2, 777, 128, structure="lm", causal=True, tau=0.95,
+       keep_prefix_kblocks=2, skip_rule="recall", recall=0.9),
+    wl("recall_d64", 115, 1, 2, 515, 64, grid=(5, 103, 1), tau=0.9, skip_rule="recall",
+       recall=0.8),
+    wl("recall_fp32", 116, 1, 2, 333, 128, dtype="f32", structure="lm", causal=True,
+       tau=0.9, skip_rule="recall", recall=0.9),
+    wl("recall_quant", 117, 1, 2, 1000, 128, grid=(10, 10, 10), tau=0.95, rule="energy",
+       prec="i8fp8", skip_rule="recall", recall=0.95),
+    wl("recall_one", 118, 1, 2, 640, 128, grid=(4, 10, 16), tau=1.0, skip_rule="recall",
+       recall=1.0),
 ]
 
 
