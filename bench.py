@@ -236,6 +236,71 @@ def rel_l1_sample(w, Q, K, V, O_gpu, oracle):
     return num / den, f"heads {heads}, query blocks {blocks}"
 
 
+def reuse_sweep(sa, torch, w, oracle, n_steps=6, ks=(1, 3, 6), dtheta=0.05, threads=16):
+    """Mask reuse across calls (sparse_attn_step): a seeded drifting
+    sequence of n_steps inputs (synth Workload.drift_head, a stand-in for
+    successive denoising steps), run with refresh_every = k for each k; per
+    k: mean time per call (stage one amortised), mean and worst rel-L1 vs
+    dense fp64 attention on sampled rows, and the number of refreshes."""
+    dev = torch.device("cuda:0")
+    shape = (n_steps, 3, 1, w.H, w.N, w.D)
+    xs = torch.empty(shape, dtype=torch.bfloat16, device=dev)
+    sample_heads = sorted({0, w.H // 2, w.H - 1})
+    host = {}
+
+    def gen(h):
+        return h, w.drift_head(0, h, n_steps, dtheta)
+
+    with ThreadPoolExecutor(threads) as ex:
+        for h, seq in ex.map(gen, range(w.H)):
+            for s in range(n_steps):
+                for t in range(3):
+                    xs[s, t, 0, h].copy_(torch.from_numpy(seq[s][t]))
+            if h in sample_heads:
+                host[h] = seq
+    p = sa.make_params(w.B, w.H, w.N, w.D, dtype=w.dtype, causal=w.causal, tau=w.tau,
+                       lam=w.lam, rule=w.rule, prec=w.prec,
+                       keep_prefix_kblocks=w.keep_prefix_kblocks)
+    nqb, nkb = sa.sparse_attn_mask_shape(p)
+    pws, fws = sa.sparse_attn_workspace_size(p)
+    idx = torch.empty((1, w.H, nqb, nkb), dtype=torch.int32, device=dev)
+    cnt = torch.empty((1, w.H, nqb), dtype=torch.int32, device=dev)
+    mask = sa.make_mask(idx, cnt)
+    ws_p = torch.empty(max(pws, 1), dtype=torch.uint8, device=dev)
+    ws_f = torch.empty(max(fws, 1), dtype=torch.uint8, device=dev)
+    o = torch.empty((1, w.H, w.N, w.D), dtype=torch.bfloat16, device=dev)
+    blocks = sorted({0, nqb // 2, nqb - 1})
+    rows = np.concatenate([np.arange(i * 128, min(w.N, (i + 1) * 128)) for i in blocks])
+    sm = 1.0 / math.sqrt(w.D)
+    dense = {}
+    for h in sample_heads:
+        for s in range(n_steps):
+            dense[h, s], _ = oracle.dense_attention_head(*host[h][s], sm, w.causal, rows=rows)
+    out = []
+    for k in ks:
+        sched = sa.make_schedule(k, 0)
+        times, rels, refreshes = [], [], 0
+        for s in range(n_steps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            sa.sparse_attn_step(p, sched, xs[s, 0], xs[s, 1], xs[s, 2], mask, o,
+                                predict_ws=ws_p, forward_ws=ws_f)
+            e1.record()
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1))
+            refreshes += sched.refreshed
+            og = o.float().cpu().numpy()[0]
+            num = sum(float(np.abs(og[h][rows] - dense[h, s]).sum()) for h in sample_heads)
+            den = sum(float(np.abs(dense[h, s]).sum()) for h in sample_heads)
+            rels.append(num / den)
+        out.append(dict(refresh_every=k, steps=n_steps, refreshes=refreshes,
+                        ms_per_call=round(float(np.mean(times)), 4),
+                        rel_l1_mean=round(float(np.mean(rels)), 6),
+                        rel_l1_max=round(float(np.max(rels)), 6)))
+    del xs
+    return out
+
+
 def cpu_baseline(w, Q, K, V, tau, blocks, skip_rule="lambda", recall=1.0):
     """The fp64 oracle as it stands, single-threaded, on head 0: stage one
     for the whole head plus stage two for the first `blocks` query blocks."""
@@ -343,6 +408,13 @@ def main():
             print(f"[bench] recall rule rho={rho}: {recall_sweep[-1]}", file=sys.stderr,
                   flush=True)
 
+    reuse = []
+    if not args.no_sweep and w.name == "wan_video":
+        print("[bench] mask reuse across a drifting sequence", file=sys.stderr, flush=True)
+        reuse = reuse_sweep(sa, torch, w, oracle)
+        for r_ in reuse:
+            print(f"[bench] reuse {r_}", file=sys.stderr, flush=True)
+
     cpu = None
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle sample", file=sys.stderr, flush=True)
@@ -388,6 +460,8 @@ def main():
                      "measured_peaks": peaks},
         "tau_sweep": sweep,
         "recall_rule_sweep": recall_sweep,
+        "mask_reuse": {"sequence": "6 calls, inputs cos(0.05 s) A + sin(0.05 s) B (seeded)",
+                       "by_refresh_every": reuse},
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

@@ -13,6 +13,8 @@ Entry points have the C names:
     sparse_attn_predict(params, q, k, mask, ws, stream=None)
     sparse_attn_forward(params, q, k, v, mask, o, lse=None, skip_bits=None,
                         ws=None, stream=None)
+    sparse_attn_step(params, schedule, q, k, v, mask, o, lse=None,
+                     skip_bits=None, predict_ws=None, forward_ws=None, stream=None)
     sparse_attn_info() -> (default_group_rows, version)
     sparse_attn_status_str(code) -> str
     sparse_attn_last_error() -> str
@@ -54,6 +56,11 @@ class SaMask(ctypes.Structure):
                 ("block_prob", ctypes.c_void_p)]
 
 
+class SaSchedule(ctypes.Structure):
+    _fields_ = [("refresh_every", ctypes.c_int32), ("dense_steps", ctypes.c_int32),
+                ("step", ctypes.c_int32), ("refreshed", ctypes.c_int32)]
+
+
 class SparseAttnError(RuntimeError):
     def __init__(self, code: int, where: str, msg: str):
         super().__init__(f"{where}: {status_name(code)}: {msg}")
@@ -81,6 +88,8 @@ def _load():
         "sparse_attn_forward": [P(SaParams), vp, vp, vp, P(SaMask), vp, vp, vp, vp,
                                 ctypes.c_size_t, vp],
         "sparse_attn_info": [P(ctypes.c_int32), P(ctypes.c_int32)],
+        "sparse_attn_step": [P(SaParams), P(SaSchedule), vp, vp, vp, P(SaMask), vp, vp, vp, vp,
+                             ctypes.c_size_t, vp, ctypes.c_size_t, vp],
     }
     for name, args in sig.items():
         f = getattr(lib, name)
@@ -194,6 +203,24 @@ def sparse_attn_forward(p: SaParams, q, k, v, mask: SaMask, o, lse=None, skip_bi
     _check(lib.sparse_attn_forward(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v),
                                    ctypes.byref(mask), _ptr(o), _ptr(lse), _ptr(skip_bits),
                                    _ptr(ws), nb, _stream(stream)), "sparse_attn_forward")
+
+
+def make_schedule(refresh_every=1, dense_steps=0) -> SaSchedule:
+    """A mask-reuse schedule for sparse_attn_step, at step 0."""
+    return SaSchedule(int(refresh_every), int(dense_steps), 0, 0)
+
+
+def sparse_attn_step(p: SaParams, sched: SaSchedule, q, k, v, mask: SaMask, o, lse=None,
+                     skip_bits=None, predict_ws=None, forward_ws=None, stream=None,
+                     predict_ws_bytes=None, forward_ws_bytes=None):
+    """One call of a sequence: stage one when ``sched`` says so, then stage
+    two.  Updates ``sched`` (step, refreshed)."""
+    pb = _nbytes(predict_ws) if predict_ws_bytes is None else predict_ws_bytes
+    fb = _nbytes(forward_ws) if forward_ws_bytes is None else forward_ws_bytes
+    _check(lib.sparse_attn_step(ctypes.byref(p), ctypes.byref(sched), _ptr(q), _ptr(k), _ptr(v),
+                                ctypes.byref(mask), _ptr(o), _ptr(lse), _ptr(skip_bits),
+                                _ptr(predict_ws), pb, _ptr(forward_ws), fb, _stream(stream)),
+           "sparse_attn_step")
 
 
 __all__ = [

@@ -144,8 +144,14 @@ sa_status sparse_attn_workspace_size(const sa_params* p, size_t* predict_ws, siz
   return ok();
 }
 
-sa_status sparse_attn_predict(const sa_params* p, const void* q, const void* k, const sa_mask* out,
-                              void* ws, size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// predict / forward with a dry-run mode that validates everything and
+// enqueues nothing (so a composite call can check all of its parts first)
+sa_status predict_impl(const sa_params* p, const void* q, const void* k, const sa_mask* out,
+                       void* ws, size_t ws_bytes, void* stream, bool dry) {
   sa::Geometry g;
   bool empty;
   sa_status st = check_params(p, &g, &empty);
@@ -173,6 +179,7 @@ sa_status sparse_attn_predict(const sa_params* p, const void* q, const void* k, 
   a.keep_prefix = p->keep_prefix_kblocks;
   a.sm = softmax_scale(p);
   a.tau = p->tau;
+  if (dry) return ok();
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = sa::launch_pool(a, s);
   if (e != hipSuccess) return fail(SA_ERR_HIP, "pool launch: %s", hipGetErrorString(e));
@@ -181,9 +188,9 @@ sa_status sparse_attn_predict(const sa_params* p, const void* q, const void* k, 
   return ok();
 }
 
-sa_status sparse_attn_forward(const sa_params* p, const void* q, const void* k, const void* v,
-                              const sa_mask* mask, void* o, float* lse, uint32_t* skip_bits,
-                              void* ws, size_t ws_bytes, void* stream) {
+sa_status forward_impl(const sa_params* p, const void* q, const void* k, const void* v,
+                       const sa_mask* mask, void* o, float* lse, uint32_t* skip_bits, void* ws,
+                       size_t ws_bytes, void* stream, bool dry) {
   sa::Geometry g;
   bool empty;
   sa_status st = check_params(p, &g, &empty);
@@ -214,6 +221,7 @@ sa_status sparse_attn_forward(const sa_params* p, const void* q, const void* k, 
   a.recall_on = p->skip_rule == SA_SKIP_RECALL;
   a.recall = p->recall;
   a.o_fp32 = p->o_fp32 || p->dtype == SA_F32;
+  if (dry) return ok();
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e;
   if (p->prec == SA_PREC_I8_FP8) {
@@ -232,6 +240,59 @@ sa_status sparse_attn_forward(const sa_params* p, const void* q, const void* k, 
     e = sa::launch_attn(a, s);
     if (e != hipSuccess) return fail(SA_ERR_HIP, "attention launch: %s", hipGetErrorString(e));
   }
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+sa_status sparse_attn_predict(const sa_params* p, const void* q, const void* k, const sa_mask* out,
+                              void* ws, size_t ws_bytes, void* stream) {
+  return predict_impl(p, q, k, out, ws, ws_bytes, stream, false);
+}
+
+sa_status sparse_attn_forward(const sa_params* p, const void* q, const void* k, const void* v,
+                              const sa_mask* mask, void* o, float* lse, uint32_t* skip_bits,
+                              void* ws, size_t ws_bytes, void* stream) {
+  return forward_impl(p, q, k, v, mask, o, lse, skip_bits, ws, ws_bytes, stream, false);
+}
+
+sa_status sparse_attn_step(const sa_params* p, sa_schedule* sched, const void* q, const void* k,
+                           const void* v, const sa_mask* mask, void* o, float* lse,
+                           uint32_t* skip_bits, void* predict_ws, size_t predict_ws_bytes,
+                           void* forward_ws, size_t forward_ws_bytes, void* stream) {
+  if (!p) return fail(SA_ERR_INVALID_ARG, "params is NULL");
+  if (!sched) return fail(SA_ERR_INVALID_ARG, "schedule is NULL");
+  if (sched->refresh_every < 1 || sched->dense_steps < 0 || sched->step < 0)
+    return fail(SA_ERR_INVALID_ARG, "schedule refresh_every=%d dense_steps=%d step=%d",
+                sched->refresh_every, sched->dense_steps, sched->step);
+  // the call's parameters: a dense step keeps every admissible block and
+  // skips nothing; a sparse step predicts on its first call and every
+  // refresh_every-th call after, and otherwise reuses the caller's mask
+  sa_params run = *p;
+  bool refresh;
+  if (sched->step < sched->dense_steps) {
+    run.tau = 1.0f;
+    run.skip_rule = SA_SKIP_LAMBDA;
+    run.lambda = -INFINITY;
+    refresh = true;
+  } else {
+    refresh = (sched->step - sched->dense_steps) % sched->refresh_every == 0;
+  }
+  sa_status st = SA_OK;
+  if (refresh) st = predict_impl(&run, q, k, mask, predict_ws, predict_ws_bytes, stream, true);
+  if (st) return st;
+  st = forward_impl(&run, q, k, v, mask, o, lse, skip_bits, forward_ws, forward_ws_bytes, stream,
+                    true);
+  if (st) return st;
+  if (refresh) st = predict_impl(&run, q, k, mask, predict_ws, predict_ws_bytes, stream, false);
+  if (st) return st;
+  st = forward_impl(&run, q, k, v, mask, o, lse, skip_bits, forward_ws, forward_ws_bytes, stream,
+                    false);
+  if (st) return st;
+  sched->refreshed = refresh ? 1 : 0;
+  sched->step += 1;
   return ok();
 }
 

@@ -24,10 +24,12 @@
 // of another; the loop is unrolled twice so every stage choice, and every
 // LDS read offset, is a compile-time constant plus a per-lane base.  DMA is
 // issued every iteration (rows past N read as zero).
-// The exponent offset is a lazily raised running max: P = exp2(c S - mu)
-// with mu <= m; acc and l are rescaled only when m - mu would exceed 8, so
-// P < 2^8 in bf16 and the 64-register rescale almost never runs.  The
-// lambda test always uses the exact running max m.
+// The exponent offset is the exact running max m: P = exp2(c S - m) <= 1,
+// so the key holding a row's maximum has P = 1, exact in bf16 (a lazily
+// raised offset would leave that dominant weight with up to 2^-8 relative
+// rounding, which alone can move O by 1e-2).  l is rescaled at once when m
+// grows; acc one step later, before the P.V of the tile that set the new m
+// (in score order m grows on about 2 % of a wavefront's tiles).
 #include <type_traits>
 
 #include "attn_common.h"
@@ -37,14 +39,11 @@ namespace {
 
 using namespace attn;
 
-constexpr float kLazyMax = 8.0f;  // log2 units
-
 typedef __attribute__((address_space(3))) void lds_void;
 
 struct Soft {
-  float m;        // exact running max (log2 units)
-  float mu;       // exponent offset, mu <= m
-  float l;        // this lane's share of sum exp2(c S - mu)
+  float m;        // running max (log2 units), the exponent offset
+  float l;        // this lane's share of sum exp2(c S - m)
   float rescale;  // pending factor for acc
   float drop;     // recall rule: energy the row has dropped, same offset as l
 };
@@ -180,7 +179,7 @@ __global__ __launch_bounds__(256, 2) void attn_pipe_kernel(AttnArgs a) {
   u32x4 pf[4];  // P of the previous tile, bf16, as the P.V B operand
 #pragma unroll
   for (int c = 0; c < 4; ++c) pf[c] = u32x4{0u, 0u, 0u, 0u};
-  Soft ss{-INFINITY, -INFINITY, 0.f, 1.f, 0.f};
+  Soft ss{-INFINITY, 0.f, 1.f, 0.f};
   bool pv_prev = false;
 
   int kq0 = entry_key(0), kq1 = entry_key(1);  // keys of entries t, t + 1
@@ -216,7 +215,7 @@ __global__ __launch_bounds__(256, 2) void attn_pipe_kernel(AttnArgs a) {
     dma(vrs, dv0, v_free, kq0);
     const int key_cur = kq0;
 
-    if (__any(ss.rescale != 1.f)) {  // the exponent offset moved at t - 1
+    if (__any(ss.rescale != 1.f)) {  // m grew at t - 1
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
@@ -246,16 +245,15 @@ __global__ __launch_bounds__(256, 2) void attn_pipe_kernel(AttnArgs a) {
     const float mnew = fmaxf(ss.m, mloc);
     bool do_pv = true;
     if (!a.lam_off) do_pv = __any((mloc != -INFINITY) && (mloc - mnew >= a.lam2));
-    ss.m = mnew;
-    if (__any(mnew - ss.mu > kLazyMax)) {
-      const float mu_new = fmaxf(ss.mu, mnew);
-      const float f = (mu_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(ss.mu - mu_new);
+    if (__any(mnew != ss.m)) {
+      // 0 when m was -inf (nothing accumulated yet), 1 where m did not move
+      const float f = (mnew == ss.m) ? 1.f : __builtin_amdgcn_exp2f(ss.m - mnew);
       ss.l *= f;
       ss.drop *= f;
       ss.rescale *= f;
-      ss.mu = mu_new;
+      ss.m = mnew;
     }
-    const float negm = (ss.mu == -INFINITY) ? 0.f : -ss.mu;
+    const float negm = (ss.m == -INFINITY) ? 0.f : -ss.m;
     const float c2 = a.c2;
 
     // region: [P.V of t-1] + Q.K^T of t+1 + exp/sum/pack of t.  Chunk c:
@@ -349,7 +347,7 @@ __global__ __launch_bounds__(256, 2) void attn_pipe_kernel(AttnArgs a) {
     }
   }
 
-  // epilogue: O = acc / l; lse = (mu + log2 l) ln 2
+  // epilogue: O = acc / l; lse = (m + log2 l) ln 2
   const float l = xhalf_sum(ss.l);
   if (qvalid) {
     const float inv = l > 0.f ? 1.f / l : 0.f;
@@ -369,7 +367,7 @@ __global__ __launch_bounds__(256, 2) void attn_pipe_kernel(AttnArgs a) {
           *reinterpret_cast<u32x2*>(orow + d * 2) = u32x2{pack2(o0, o1), pack2(o2, o3)};
       }
     if (a.lse && hh == 0)
-      a.lse[(int64_t)bh * a.N + qrow] = l > 0.f ? (ss.mu + __log2f(l)) * kLn2 : -INFINITY;
+      a.lse[(int64_t)bh * a.N + qrow] = l > 0.f ? (ss.m + __log2f(l)) * kLn2 : -INFINITY;
   }
 }
 

@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define SPARSE_ATTN_VERSION 2
+#define SPARSE_ATTN_VERSION 3
 
 #if defined(__GNUC__)
 #define SA_API __attribute__((visibility("default")))
@@ -190,6 +190,39 @@ SA_API sa_status sparse_attn_forward(const sa_params* p, const void* q, const vo
                               const void* v, const sa_mask* mask, void* o,
                               float* lse, uint32_t* skip_bits, void* ws,
                               size_t ws_bytes, void* stream);
+
+/* Mask reuse across a sequence of calls (e.g. the denoising steps of a
+ * diffusion model), for sparse_attn_step.  The pages note that attention
+ * patterns stay similar across denoising steps and can be precomputed once
+ * and reused (SparseD and LiteAttention abstracts on the search page; the
+ * DynSparse story: combinable with pre-computed masks), and that early steps
+ * are critical (SparseD runs them dense).  Caller-owned; set step = 0 to
+ * start a sequence. */
+typedef struct sa_schedule {
+  int32_t refresh_every;  /* >= 1: sparse calls predict a new mask on their   */
+                          /* first call and every refresh_every-th after, and */
+                          /* reuse the caller's mask in between              */
+  int32_t dense_steps;    /* >= 0: the first dense_steps calls keep every     */
+                          /* admissible block and skip nothing (exact up to   */
+                          /* rounding)                                        */
+  int32_t step;           /* calls made so far; incremented on success        */
+  int32_t refreshed;      /* out: 1 if this call ran stage one                */
+} sa_schedule;
+
+/* One call of a sequence: stage one when the schedule says so (writing
+ * *mask), then stage two with *mask.  Call number s = sched->step runs
+ *   s <  dense_steps: predict and forward with tau = 1 and no skip;
+ *   s >= dense_steps: predict iff (s - dense_steps) % refresh_every == 0,
+ *                     then forward, with *p as given.
+ * A reused mask must come from a call with the same shapes and causality
+ * (every entry admissible), which the sequence guarantees when the caller
+ * keeps `mask` between calls.  Every argument is validated before anything
+ * is enqueued.  Workspaces as for sparse_attn_predict / sparse_attn_forward. */
+SA_API sa_status sparse_attn_step(const sa_params* p, sa_schedule* sched, const void* q,
+                           const void* k, const void* v, const sa_mask* mask, void* o,
+                           float* lse, uint32_t* skip_bits, void* predict_ws,
+                           size_t predict_ws_bytes, void* forward_ws,
+                           size_t forward_ws_bytes, void* stream);
 
 /* Host.  Library defaults and version (either pointer may be NULL). */
 SA_API sa_status sparse_attn_info(int32_t* default_group_rows, int32_t* version);

@@ -53,6 +53,7 @@ from .quant import (  # noqa: F401
     fp8_quantize_v_blocks,
     sparse_attention_quant_head,
 )
+from .schedule import step_plan, sequence_head  # noqa: F401
 from .metrics import (  # noqa: F401
     rel_l1,
     block_sparsity,

@@ -210,6 +210,25 @@ class Workload:
         return (np.stack(qs).reshape(shape), np.stack(ks).reshape(shape),
                 np.stack(vs).reshape(shape))
 
+    def drift_head(self, b: int, h: int, n_steps: int, dtheta: float = 0.05):
+        """A sequence of n_steps inputs for one (b, h) that drift slowly, a
+        stand-in for successive denoising steps: step s mixes this head's
+        draw A with an independent draw B of the same structure (seed index
+        + 1000) as cos(s dtheta) A + sin(s dtheta) B, which keeps the
+        per-element variance, then rounds to the storage dtype."""
+        a = self.head(b, h)
+        partner = dataclasses.replace(self, index=self.index + 1000, dtype="f32")
+        bb = partner.head(b, h)
+        out = []
+        for s in range(n_steps):
+            c, sn = np.cos(s * dtheta), np.sin(s * dtheta)
+            step = []
+            for x, y in zip(a, bb):
+                z = (c * x.astype(np.float64) + sn * y.astype(np.float64)).astype(np.float32)
+                step.append(round_to_bf16(z) if self.dtype == "bf16" else z)
+            out.append(tuple(step))
+        return out
+
     def dense_flops(self) -> float:
         f = 4.0 * self.B * self.H * self.N * self.N * self.D
         return f / 2.0 if self.causal else f

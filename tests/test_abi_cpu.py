@@ -56,7 +56,7 @@ def test_shapes_and_workspace():
     _, fw = sa.sparse_attn_workspace_size(q)
     bh = 16
     assert fw == 2 * bh * 65536 * 128 + bh * 1024 * 128 * 64 + bh * 512 * 4 + 2 * bh * 1024 * 4
-    assert sa.sparse_attn_info() == (32, 2)
+    assert sa.sparse_attn_info() == (32, 3)
     assert sa.sparse_attn_status_str(3) == "SA_ERR_WORKSPACE"
     assert sa.sparse_attn_status_str(99) == "SA_ERR_UNKNOWN"
     p = sa.make_params(2, 3, 0, 64)
@@ -97,6 +97,33 @@ def test_invalid_params_rejected_before_launch(kw, code):
         sa.sparse_attn_forward(p, fake, fake, fake, mask, fake, ws=fake, ws_bytes=1 << 40,
                                stream=0)
     assert e.value.code == code
+
+
+def test_step_schedule_validated_before_launch():
+    assert ctypes.sizeof(sa.SaSchedule) == 16
+    p = sa.make_params(1, 2, 1000, 128, tau=0.9)
+    fake = 1 << 20  # never dereferenced: validation fails first
+    mask = sa.make_mask(fake, fake)
+    for sched in (sa.make_schedule(0, 0), sa.make_schedule(2, -1), sa.SaSchedule(1, 0, -3, 0)):
+        with pytest.raises(sa.SparseAttnError) as e:
+            sa.sparse_attn_step(p, sched, fake, fake, fake, mask, fake, predict_ws=fake,
+                                forward_ws=fake, predict_ws_bytes=1 << 40,
+                                forward_ws_bytes=1 << 40, stream=0)
+        assert e.value.code == sa.SA_ERR_INVALID_ARG
+    # a bad part of the forward half is caught before the predict half runs,
+    # and the schedule does not advance
+    sched = sa.make_schedule(3, 1)
+    for bad in (dict(v=None), dict(forward_ws_bytes=0, forward_ws=None)):
+        args = dict(q=fake, k=fake, v=fake, o=fake, predict_ws=fake, forward_ws=fake,
+                    predict_ws_bytes=1 << 40, forward_ws_bytes=1 << 40)
+        args.update(bad)
+        q8 = sa.make_params(1, 2, 1000, 128, tau=0.9, prec="i8fp8")
+        with pytest.raises(sa.SparseAttnError):
+            sa.sparse_attn_step(q8, sched, args["q"], args["k"], args["v"], mask, args["o"],
+                                predict_ws=args["predict_ws"], forward_ws=args["forward_ws"],
+                                predict_ws_bytes=args["predict_ws_bytes"],
+                                forward_ws_bytes=args["forward_ws_bytes"], stream=0)
+        assert sched.step == 0
 
 
 def test_null_and_workspace_errors():

@@ -32,7 +32,6 @@ import oracle as O  # noqa: E402
 from synth import make_workload, round_to_bf16  # noqa: E402
 import compare  # noqa: E402
 
-OUT_TOL = {"bf16": 1e-2, "f32": 1e-2, "i8fp8": 5e-2}
 SKIP_TOL = {"bf16": 1e-3, "f32": 1e-4, "i8fp8": 1e-3}
 
 
@@ -162,7 +161,7 @@ def test_fullsize_parity(name, heads, nblocks, over):
         og = o32[0, h].cpu().numpy()
         err = float(np.abs(og[rows] - Oref[rows]).max())
         worst = max(worst, err)
-        assert err <= OUT_TOL[mode], f"{name} head {h}: max-abs {err}"
+        assert err <= compare.out_tol(mode, vh), f"{name} head {h}: max-abs {err}"
         if w.dtype == "bf16":
             ob = o[0, h].float().cpu().numpy()
             np.testing.assert_array_equal(ob[rows], round_to_bf16(og[rows]))
