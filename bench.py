@@ -141,12 +141,14 @@ def gen_inputs(w, threads=16):
 class Runner:
     """Owns the device buffers of one configuration and runs the two calls."""
 
-    def __init__(self, sa, torch, w, q, k, v, tau, skip_rule="lambda", recall=1.0):
+    def __init__(self, sa, torch, w, q, k, v, tau, skip_rule="lambda", recall=1.0, rule=None,
+                 topk_blocks=0):
         self.sa, self.torch, self.w = sa, torch, w
         self.q, self.k, self.v = q, k, v
         self.o = torch.empty_like(q)
         self.p = sa.make_params(w.B, w.H, w.N, w.D, dtype=w.dtype, causal=w.causal, tau=tau,
-                                lam=w.lam, rule=w.rule, prec=w.prec,
+                                lam=w.lam, rule=rule or w.rule, prec=w.prec,
+                                topk_blocks=topk_blocks,
                                 keep_prefix_kblocks=w.keep_prefix_kblocks,
                                 skip_rule=skip_rule, recall=recall)
         self.nqb, self.nkb = sa.sparse_attn_mask_shape(self.p)
@@ -351,10 +353,11 @@ def main():
     q, k, v = (torch.from_numpy(x).to(tdt).to(dev) for x in (Q, K, V))
     dense = w.dense_flops()
 
-    def measure(tau, steps, warmup, skip_rule=None, recall=None):
+    def measure(tau, steps, warmup, skip_rule=None, recall=None, rule=None, topk_blocks=0):
         r = Runner(sa, torch, w, q, k, v, tau,
                    skip_rule=skip_rule or args.skip_rule,
-                   recall=args.recall if recall is None else recall)
+                   recall=args.recall if recall is None else recall, rule=rule,
+                   topk_blocks=topk_blocks)
         ms, pred_ms, fwd_ms, wall = r.time_steps(steps, warmup)
         cnt, skipped = r.decisions()
         adm = admissible_count(w, r.nqb, r.nkb)
@@ -408,6 +411,23 @@ def main():
             print(f"[bench] recall rule rho={rho}: {recall_sweep[-1]}", file=sys.stderr,
                   flush=True)
 
+    topk_sweep = []
+    if not args.no_sweep and w.name == "wan_video":
+        # the fixed-budget top-k mask against the cumulative-mass cut: the
+        # first budget matches the mean kept count of the headline tau
+        mean_kept = int(round(m["tiles"] / (w.B * w.H * r.nqb)))
+        for kb in (mean_kept, r.nkb // 2, r.nkb // 4):
+            rs, ms_ = measure(w.tau, max(3, args.steps // 4), 1, rule="topk", topk_blocks=kb)
+            o_s = rs.o.float().cpu().numpy()[0]
+            rl, _ = rel_l1_sample(w, Q, K, V, o_s, oracle)
+            topk_sweep.append(dict(topk_blocks=kb, sparsity=round(ms_["sparsity"], 5),
+                                   pv_skip_fraction=round(ms_["skip"], 5), rel_l1=round(rl, 6),
+                                   ms_per_step=round(ms_["ms"], 4),
+                                   dense_equiv_tflops=round(dense / (ms_["ms"] * 1e-3) / 1e12,
+                                                            2)))
+            del rs
+            print(f"[bench] top-k {kb}: {topk_sweep[-1]}", file=sys.stderr, flush=True)
+
     reuse = []
     if not args.no_sweep and w.name == "wan_video":
         print("[bench] mask reuse across a drifting sequence", file=sys.stderr, flush=True)
@@ -460,6 +480,7 @@ def main():
                      "measured_peaks": peaks},
         "tau_sweep": sweep,
         "recall_rule_sweep": recall_sweep,
+        "topk_rule_sweep": topk_sweep,
         "mask_reuse": {"sequence": "6 calls, inputs cos(0.05 s) A + sin(0.05 s) B (seeded)",
                        "by_refresh_every": reuse},
         "cpu_baseline": cpu,

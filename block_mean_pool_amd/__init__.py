@@ -33,7 +33,7 @@ HEADER = os.path.join(os.path.dirname(HERE), "include", "sparse_attn.h")
 SA_OK, SA_ERR_INVALID_ARG, SA_ERR_UNSUPPORTED, SA_ERR_WORKSPACE, SA_ERR_HIP = range(5)
 SA_F32, SA_BF16 = 0, 1
 SA_PREC_NATIVE, SA_PREC_I8_FP8 = 0, 1
-SA_RULE_TOPCDF, SA_RULE_ENERGY = 0, 1
+SA_RULE_TOPCDF, SA_RULE_ENERGY, SA_RULE_TOPK = 0, 1, 2
 SA_SKIP_LAMBDA, SA_SKIP_RECALL = 0, 1
 
 
@@ -48,6 +48,7 @@ class SaParams(ctypes.Structure):
         ("stride_b", ctypes.c_int64),
         ("stride_h", ctypes.c_int64), ("stride_n", ctypes.c_int64),
         ("skip_rule", ctypes.c_int32), ("recall", ctypes.c_float),
+        ("topk_blocks", ctypes.c_int32),
     ]
 
 
@@ -125,7 +126,8 @@ def _check(code: int, where: str):
 def make_params(B, H, N, D, *, dtype="bf16", causal=False, tau=0.95, lam=-math.inf,
                 sm_scale=0.0, rule="topcdf", prec="native", keep_prefix_kblocks=0,
                 block_q=128, block_k=64, lambda_group_rows=0, o_fp32=False,
-                strides=(0, 0, 0), skip_rule="lambda", recall=1.0) -> SaParams:
+                strides=(0, 0, 0), skip_rule="lambda", recall=1.0,
+                topk_blocks=0) -> SaParams:
     """A parameter block; ``strides`` are element strides (b, h, n), 0 =
     packed [B, H, N, D]; ``o_fp32`` writes O as float32; ``skip_rule`` is
     "lambda" (threshold ``lam``) or "recall" (target share ``recall``)."""
@@ -133,13 +135,14 @@ def make_params(B, H, N, D, *, dtype="bf16", causal=False, tau=0.95, lam=-math.i
         B, H, N, D, block_q, block_k, int(bool(causal)),
         {"f32": SA_F32, "bf16": SA_BF16}[dtype] if isinstance(dtype, str) else int(dtype),
         {"native": SA_PREC_NATIVE, "i8fp8": SA_PREC_I8_FP8}[prec] if isinstance(prec, str) else int(prec),
-        {"topcdf": SA_RULE_TOPCDF, "energy": SA_RULE_ENERGY}[rule] if isinstance(rule, str) else int(rule),
+        {"topcdf": SA_RULE_TOPCDF, "energy": SA_RULE_ENERGY, "topk": SA_RULE_TOPK}[rule]
+        if isinstance(rule, str) else int(rule),
         float(tau), float(lam), float(sm_scale), int(keep_prefix_kblocks),
         int(lambda_group_rows), int(bool(o_fp32)), int(strides[0]), int(strides[1]),
         int(strides[2]),
         {"lambda": SA_SKIP_LAMBDA, "recall": SA_SKIP_RECALL}[skip_rule]
         if isinstance(skip_rule, str) else int(skip_rule),
-        float(recall))
+        float(recall), int(topk_blocks))
 
 
 def _ptr(t) -> Optional[int]:

@@ -46,8 +46,10 @@ sa_status check_params(const sa_params* p, sa::Geometry* g, bool* empty) {
     return fail(SA_ERR_INVALID_ARG, "prec=%d", p->prec);
   if (p->prec == SA_PREC_I8_FP8 && (p->dtype != SA_BF16 || p->D != 128))
     return fail(SA_ERR_UNSUPPORTED, "INT8/FP8 variant needs bf16 inputs and D=128");
-  if (p->rule != SA_RULE_TOPCDF && p->rule != SA_RULE_ENERGY)
+  if (p->rule != SA_RULE_TOPCDF && p->rule != SA_RULE_ENERGY && p->rule != SA_RULE_TOPK)
     return fail(SA_ERR_INVALID_ARG, "rule=%d", p->rule);
+  if (p->rule == SA_RULE_TOPK && p->topk_blocks < 1)
+    return fail(SA_ERR_INVALID_ARG, "topk_blocks=%d (must be >= 1)", p->topk_blocks);
   if (p->causal != 0 && p->causal != 1) return fail(SA_ERR_INVALID_ARG, "causal=%d", p->causal);
   if (!(p->tau > 0.f) || std::isnan(p->tau))
     return fail(SA_ERR_INVALID_ARG, "tau=%g (must be in (0, 1]; >= 1 keeps all)", (double)p->tau);
@@ -179,6 +181,7 @@ sa_status predict_impl(const sa_params* p, const void* q, const void* k, const s
   a.keep_prefix = p->keep_prefix_kblocks;
   a.sm = softmax_scale(p);
   a.tau = p->tau;
+  a.topk = p->rule == SA_RULE_TOPK ? p->topk_blocks : 0;
   if (dry) return ok();
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = sa::launch_pool(a, s);

@@ -15,7 +15,8 @@
 //   3. bitonic sort in LDS of the keys (class, s, j): forced blocks first,
 //      then s descending, then j ascending -- a strict total order;
 //   4. P-hat_j = weight_j / sum in place, blocked fp64 prefix sum over the
-//      sorted order, first prefix reaching tau, never below the forced count;
+//      sorted order, first prefix reaching tau, never below the forced count
+//      (the top-k rule keeps a fixed count instead);
 //   5. the kept prefix is written in sorted order with its length.
 // LDS: val[P2] doubles indexed by j (score, then P-hat) and key[P2] packed
 // (class << 16 | j), P2 = max(256, next power of two >= NKB) <= 4096.
@@ -191,7 +192,7 @@ __global__ __launch_bounds__(kThreads) void mask_kernel(PredictLaunch a, int P2)
     __syncthreads();
   }
   const double tau = (double)a.tau;
-  if (tau < 1.0) {
+  if (tau < 1.0 && a.topk == 0) {
     double run = tid ? part[tid - 1] : 0.0;
     for (int e = 0; e < E; ++e) {
       const int t = t0 + e;
@@ -205,7 +206,10 @@ __global__ __launch_bounds__(kThreads) void mask_kernel(PredictLaunch a, int P2)
   }
   __syncthreads();
   int kcount = nA;
-  if (tau < 1.0 && s_kstar != 0x7fffffff) kcount = max(nF, s_kstar);
+  if (a.topk > 0)
+    kcount = min(nA, max(nF, a.topk));  // fixed budget, same processing order
+  else if (tau < 1.0 && s_kstar != 0x7fffffff)
+    kcount = max(nF, s_kstar);
 
   // 5. compaction: the kept prefix in processing order
   int32_t* out = a.kept_idx + (size_t)row * g.nkb;

@@ -26,6 +26,7 @@ struct PredictLaunch {
   int causal, rule, keep_prefix;
   float sm;
   float tau;
+  int topk;                  // > 0: keep this many blocks (top-k rule)
 };
 
 struct ForwardLaunch {

@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define SPARSE_ATTN_VERSION 3
+#define SPARSE_ATTN_VERSION 4
 
 #if defined(__GNUC__)
 #define SA_API __attribute__((visibility("default")))
@@ -83,8 +83,11 @@ enum { SA_PREC_NATIVE = 0, SA_PREC_I8_FP8 = 1 };
 /* Mask rule of stage one.  TOPCDF: P-hat = softmax of the block scores over
  * the admissible key blocks.  ENERGY: P-hat_j proportional to
  * n_j * exp(s_j), n_j the number of keys in block j (a cumulative-energy
- * target; equal to TOPCDF when every block is full). */
-enum { SA_RULE_TOPCDF = 0, SA_RULE_ENERGY = 1 };
+ * target; equal to TOPCDF when every block is full).  TOPK: a fixed budget
+ * of `topk_blocks` key blocks per query block in the same processing order
+ * (the fixed-budget comparator the DynSparse story sets against top-p);
+ * P-hat as for TOPCDF. */
+enum { SA_RULE_TOPCDF = 0, SA_RULE_ENERGY = 1, SA_RULE_TOPK = 2 };
 /* Skip rule of stage two (see sparse_attn_forward).  LAMBDA: the static
  * threshold `lambda` on (tile max - running max), the SpargeAttn abstract's
  * stage-two filter.  RECALL: a dynamic threshold from the cumulative energy
@@ -115,6 +118,9 @@ typedef struct sa_params {
   int32_t skip_rule;           /* SA_SKIP_LAMBDA | SA_SKIP_RECALL              */
   float recall;                /* SA_SKIP_RECALL: target share rho in (0, 1]   */
                                /* of each row's energy; ignored otherwise      */
+  int32_t topk_blocks;         /* SA_RULE_TOPK: key blocks kept per query      */
+                               /* block (>= 1; the forced blocks are kept even */
+                               /* beyond it); ignored otherwise                */
 } sa_params;
 
 /* The mask: output of predict, input of forward.  Caller-allocated; sizes
@@ -159,7 +165,8 @@ SA_API sa_status sparse_attn_workspace_size(const sa_params* p, size_t* predict_
  *   blocks that reach the query block's diagonal;
  *   order: forced first, s descending, j ascending;
  *   cut: the shortest prefix whose fp64 running sum of P-hat reaches tau,
- *   never fewer than |F_i|; tau >= 1 keeps all of A_i.
+ *   never fewer than |F_i|; tau >= 1 keeps all of A_i; under SA_RULE_TOPK
+ *   the first min(|A_i|, max(|F_i|, topk_blocks)) entries instead.
  * `ws` must hold the predict workspace. */
 SA_API sa_status sparse_attn_predict(const sa_params* p, const void* q, const void* k,
                               const sa_mask* out, void* ws, size_t ws_bytes,

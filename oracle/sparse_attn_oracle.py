@@ -37,6 +37,10 @@ O7 cut           DynSparse story (recall target); iCATS abstract (top-p).
                  the forced blocks; tau >= 1, or a prefix that never reaches
                  tau by rounding, keeps every admissible block.  The kept
                  list keeps this order; attention processes it in this order.
+O7' top-k        DynSparse story (top-k fixes a computational budget but
+                 relaxes accuracy, the comparator of top-p).  Reading (rule =
+                 "topk"): keep the first min(|A_i|, max(|F_i|, k)) blocks of
+                 the same processing order; P-hat is the top-cdf softmax.
 O8 attention     SpargeAttn abstract, stage two (an online softmax-aware
                  filter that costs nothing extra and skips more products).
                  Reading: flash-attention online softmax over the kept list;
@@ -85,11 +89,12 @@ class Params:
     tau: float = 0.95
     lam: float = -math.inf
     sm_scale: float = 0.0          # 0 -> 1/sqrt(d)
-    rule: str = "topcdf"           # "topcdf" | "energy"
+    rule: str = "topcdf"           # "topcdf" | "energy" | "topk"
     keep_prefix_kblocks: int = 0
     G: int = 32                    # rows per skip group
     skip_rule: str = "lambda"      # "lambda" (O8) | "recall" (O8')
     recall: float = 1.0            # rho of the recall rule
+    topk_blocks: int = 0           # budget of the "topk" rule
 
     def sm(self, d: int) -> float:
         return float(self.sm_scale) if self.sm_scale else 1.0 / math.sqrt(d)
@@ -140,8 +145,8 @@ def block_scores(qbar: np.ndarray, kbar: np.ndarray, sm: float) -> np.ndarray:
 def block_weights(s: np.ndarray, adm: np.ndarray, rule: str,
                   n_k: np.ndarray) -> np.ndarray:
     """O4: predicted block mass P-hat [NQB, NKB], 0 outside the admissible
-    set.  top-cdf: softmax of s over admissible j.  energy: weights
-    n_j * exp(s_ij - max) normalised."""
+    set.  top-cdf (and top-k, which only changes the cut): softmax of s over
+    admissible j.  energy: weights n_j * exp(s_ij - max) normalised."""
     P = np.zeros_like(s)
     for i in range(s.shape[0]):
         a = adm[i]
@@ -149,7 +154,7 @@ def block_weights(s: np.ndarray, adm: np.ndarray, rule: str,
         w = np.exp(si - si.max())
         if rule == "energy":
             w = w * n_k[a]
-        elif rule != "topcdf":
+        elif rule not in ("topcdf", "topk"):
             raise ValueError(rule)
         P[i, a] = w / w.sum()
     return P
@@ -214,7 +219,10 @@ def predict_head(Q: np.ndarray, K: np.ndarray, p: Params) -> dict:
     orders: List[np.ndarray] = []
     for i in range(s.shape[0]):
         order = processing_order(s[i], adm[i], F[i])
-        k = cut_length(P[i, order], int(F[i].sum()), float(p.tau))
+        if p.rule == "topk":        # O7': a fixed budget in the same order
+            k = min(len(order), max(int(F[i].sum()), int(p.topk_blocks)))
+        else:
+            k = cut_length(P[i, order], int(F[i].sum()), float(p.tau))
         orders.append(order)
         kept.append(order[:k])
     return dict(qbar=qbar, kbar=kbar, s=s, P=P, adm=adm, forced=F,

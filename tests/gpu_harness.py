@@ -19,7 +19,7 @@ def to_device(x: np.ndarray, dtype: str):
 def run(Q, K, V, *, dtype="bf16", causal=False, tau=0.95, lam=-5.0, rule="topcdf",
         prec="native", keep_prefix_kblocks=0, sm_scale=0.0, layout="bhnd",
         block_prob=True, want_lse=True, want_skips=True, forward=True,
-        skip_rule="lambda", recall=1.0):
+        skip_rule="lambda", recall=1.0, topk_blocks=0):
     """Q, K, V: float32 arrays [B, H, N, D] holding dtype-representable values.
     ``layout="bnhd"`` stores the tensors as [B, N, H, D] and passes strides."""
     B, H, N, D = Q.shape
@@ -35,7 +35,7 @@ def run(Q, K, V, *, dtype="bf16", causal=False, tau=0.95, lam=-5.0, rule="topcdf
         views = (q, k, v, o)
     kw = dict(dtype=dtype, causal=causal, tau=tau, lam=lam, rule=rule, prec=prec,
               keep_prefix_kblocks=keep_prefix_kblocks, sm_scale=sm_scale, strides=strides,
-              skip_rule=skip_rule, recall=recall)
+              skip_rule=skip_rule, recall=recall, topk_blocks=topk_blocks)
     p = sa.make_params(B, H, N, D, **kw)
     p32 = sa.make_params(B, H, N, D, o_fp32=True, **kw)
     nqb, nkb = sa.sparse_attn_mask_shape(p)

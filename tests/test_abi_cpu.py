@@ -31,11 +31,13 @@ def test_binding_exposes_the_same_names():
 
 
 def test_struct_layout_matches_header():
-    # 10 int32 + 3 float + 3 int32 = 64 bytes, + 3 int64, + int32 + float
-    assert ctypes.sizeof(sa.SaParams) == 96
+    # 10 int32 + 3 float + 3 int32 = 64 bytes, + 3 int64, + int32 + float + int32,
+    # padded to the 8-byte alignment of the int64 fields
+    assert ctypes.sizeof(sa.SaParams) == 104
     assert sa.SaParams.stride_b.offset == 64
     assert sa.SaParams.skip_rule.offset == 88
     assert sa.SaParams.recall.offset == 92
+    assert sa.SaParams.topk_blocks.offset == 96
     assert ctypes.sizeof(sa.SaMask) == 24
     # field order and names as declared in the header
     text = open(sa.HEADER).read()
@@ -56,7 +58,7 @@ def test_shapes_and_workspace():
     _, fw = sa.sparse_attn_workspace_size(q)
     bh = 16
     assert fw == 2 * bh * 65536 * 128 + bh * 1024 * 128 * 64 + bh * 512 * 4 + 2 * bh * 1024 * 4
-    assert sa.sparse_attn_info() == (32, 3)
+    assert sa.sparse_attn_info() == (32, 4)
     assert sa.sparse_attn_status_str(3) == "SA_ERR_WORKSPACE"
     assert sa.sparse_attn_status_str(99) == "SA_ERR_UNKNOWN"
     p = sa.make_params(2, 3, 0, 64)
@@ -78,6 +80,8 @@ def test_shapes_and_workspace():
     (dict(strides=(0, 0, 100)), sa.SA_ERR_INVALID_ARG),
     (dict(strides=(0, 0, 130)), sa.SA_ERR_INVALID_ARG),
     (dict(skip_rule=2), sa.SA_ERR_INVALID_ARG),
+    (dict(rule="topk", topk_blocks=0), sa.SA_ERR_INVALID_ARG),
+    (dict(rule=3), sa.SA_ERR_INVALID_ARG),
     (dict(skip_rule="recall", recall=0.0), sa.SA_ERR_INVALID_ARG),
     (dict(skip_rule="recall", recall=1.5), sa.SA_ERR_INVALID_ARG),
     (dict(skip_rule="recall", recall=float("nan")), sa.SA_ERR_INVALID_ARG),

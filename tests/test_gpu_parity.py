@@ -60,11 +60,13 @@ def check_case(w: Workload, layout="bhnd", check_out=True):
     lam32 = float(np.float32(w.lam))
     r = gpu_harness.run(Q, K, V, dtype=w.dtype, causal=w.causal, tau=w.tau, lam=w.lam,
                         rule=w.rule, prec=w.prec, keep_prefix_kblocks=w.keep_prefix_kblocks,
-                        layout=layout, skip_rule=w.skip_rule, recall=w.recall)
+                        layout=layout, skip_rule=w.skip_rule, recall=w.recall,
+                        topk_blocks=w.topk_blocks)
     p = O.Params(BQ=128, BK=64, causal=w.causal, tau=tau32, lam=lam32, rule=w.rule,
                  keep_prefix_kblocks=w.keep_prefix_kblocks, G=32,
                  sm_scale=float(np.float32(1.0 / math.sqrt(w.D))),
-                 skip_rule=w.skip_rule, recall=float(np.float32(w.recall)))
+                 skip_rule=w.skip_rule, recall=float(np.float32(w.recall)),
+                 topk_blocks=w.topk_blocks)
     mode = w.prec if w.prec == "i8fp8" else w.dtype
     worst = 0.0
     n_rows = n_exact = 0
@@ -77,7 +79,9 @@ def check_case(w: Workload, layout="bhnd", check_out=True):
             np.testing.assert_allclose(r["qbar"][b, h], pred["qbar"], rtol=1e-5, atol=1e-6)
             np.testing.assert_allclose(r["kbar"][b, h], pred["kbar"], rtol=1e-5, atol=1e-6)
             np.testing.assert_allclose(r["block_prob"][b, h], pred["P"], rtol=0, atol=1e-6)
-            n, ex, fails = compare.compare_masks([r["kept"][hid]], [pred], tau32)
+            # the top-k rule has no mass threshold to be near (tau 2 never is)
+            cut_tau = 2.0 if w.rule == "topk" else tau32
+            n, ex, fails = compare.compare_masks([r["kept"][hid]], [pred], cut_tau)
             assert not fails, f"mask mismatch head {hid}: {fails[:3]}"
             n_rows += n
             n_exact += ex
@@ -168,6 +172,13 @@ CASES = [
        prec="i8fp8", skip_rule="recall", recall=0.95),
     wl("recall_one", 118, 1, 2, 640, 128, grid=(4, 10, 16), tau=1.0, skip_rule="recall",
        recall=1.0),
+    # top-k mask rule (fixed budget per query block)
+    wl("topk_field", 119, 1, 2, 1000, 128, grid=(10, 10, 10), rule="topk", topk_blocks=5,
+       lam=-5.0),
+    wl("topk_causal", 120, 1, 2, 777, 128, structure="lm", causal=True, rule="topk",
+       topk_blocks=3, keep_prefix_kblocks=2, lam=-5.0),
+    wl("topk_quant", 121, 1, 1, 900, 128, grid=(9, 10, 10), rule="topk", topk_blocks=6,
+       prec="i8fp8", lam=-5.0),
 ]
 
 

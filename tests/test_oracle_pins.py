@@ -286,3 +286,37 @@ def test_lambda_zero_keeps_only_max_raising_tiles():
             for g in range(4):
                 assert r["skips"][i][t, g] == (not raises[g * 4:(g + 1) * 4].any())
             m = np.maximum(m, mloc)
+
+
+# ------------------------------------------------------------ top-k rule
+@pytest.mark.parametrize("causal", [False, True])
+def test_topk_rule_keeps_the_k_highest_scores(causal):
+    """The top-k cut against an independent selection: forced blocks, then
+    the k - |F| highest pooled scores (ties by index) via a stable argsort."""
+    q, k, _ = rand_qkv(41, 300, 8, scale=2.0)
+    for kk in (1, 3, 7, 100):
+        p = O.Params(BQ=32, BK=16, causal=causal, rule="topk", topk_blocks=kk,
+                     keep_prefix_kblocks=1)
+        pr = O.predict_head(q, k, p)
+        for i, lst in enumerate(pr["kept"]):
+            adm = np.flatnonzero(pr["adm"][i])
+            F = set(np.flatnonzero(pr["forced"][i]).tolist())
+            want_n = min(len(adm), max(len(F), kk))
+            assert len(lst) == want_n
+            assert set(lst[:len(F)].tolist()) == F
+            rest = [j for j in adm if j not in F]
+            s = pr["s"][i, rest]
+            top = [rest[t] for t in np.argsort(-s, kind="stable")[:want_n - len(F)]]
+            assert lst[len(F):].tolist() == top
+        # P-hat is the top-cdf softmax whatever the budget
+        p2 = O.Params(BQ=32, BK=16, causal=causal, rule="topcdf", keep_prefix_kblocks=1)
+        np.testing.assert_array_equal(pr["P"], O.predict_head(q, k, p2)["P"])
+
+
+def test_topk_budget_covering_everything_is_dense():
+    q, k, v = rand_qkv(42, 200, 8)
+    p = O.Params(BQ=32, BK=16, rule="topk", topk_blocks=1000, lam=-math.inf)
+    pr = O.predict_head(q, k, p)
+    Oo, _, _ = O.sparse_attention_head(q, k, v, pr["kept"], p)
+    od, _ = O.dense_attention_head(q, k, v, 1 / math.sqrt(8), False)
+    np.testing.assert_allclose(Oo, od, atol=1e-12)
