@@ -20,6 +20,10 @@ Sources followed (the method as the pages state it):
 * DynSparse story (embedding.report page): top-p vs top-k selection and a
   threshold built from the cumulative energy of the selected tokens, a
   quantity the flash-attention operator already holds.
+* iCATS abstract again, and the PARO abstract (huggingface-mirror search
+  page): tokens grouped by the query-key interaction (a quadratic form)
+  and reordered so that the attention pattern becomes block-wise, with the
+  tails of irregular clusters merged instead of padded (``cluster.py``).
 
 Every concrete choice the pages leave open (block-mean pooling as the
 grouping, block sizes, the tie order, the cut rule, the lambda test, the
@@ -54,6 +58,20 @@ from .quant import (  # noqa: F401
     sparse_attention_quant_head,
 )
 from .schedule import step_plan, sequence_head  # noqa: F401
+from .cluster import (  # noqa: F401
+    ClusterParams,
+    second_moment,
+    metric_matrix,
+    quad_dist,
+    seeds,
+    assign,
+    update,
+    cluster_tokens,
+    token_order,
+    reorder_perms,
+    reordered_attention_head,
+    reordered_head,
+)
 from .metrics import (  # noqa: F401
     rel_l1,
     block_sparsity,
