@@ -226,19 +226,34 @@ def admissible_count(w, nqb, nkb):
     return w.B * w.H * tot
 
 
+_DENSE_CACHE = {}
+
+
+def sample_blocks(nqb, n=16):
+    """n query blocks evenly spaced over the sequence (first and last
+    included)."""
+    return sorted({int(round(x)) for x in np.linspace(0, nqb - 1, min(n, nqb))})
+
+
 def rel_l1_sample(w, Q, K, V, O_gpu, oracle):
-    """rel-L1 of the GPU output vs dense fp64 attention on sampled rows."""
+    """rel-L1 of the GPU output vs dense fp64 attention on sampled rows: 16
+    evenly spaced query blocks of 3 heads (the dense rows are computed once
+    per workload and reused across calls)."""
     heads = sorted({0, w.H // 2, w.H - 1})
     nqb = (w.N + 127) // 128
-    blocks = sorted({0, nqb // 2, nqb - 1})
+    blocks = sample_blocks(nqb)
     num = den = 0.0
     sm = 1.0 / math.sqrt(w.D)
+    rows = np.concatenate([np.arange(i * 128, min(w.N, (i + 1) * 128)) for i in blocks])
     for h in heads:
-        rows = np.concatenate([np.arange(i * 128, min(w.N, (i + 1) * 128)) for i in blocks])
-        od, _ = oracle.dense_attention_head(Q[0, h], K[0, h], V[0, h], sm, w.causal, rows=rows)
+        key = (w.name, h)
+        if key not in _DENSE_CACHE:
+            _DENSE_CACHE[key] = oracle.dense_attention_head(Q[0, h], K[0, h], V[0, h], sm,
+                                                            w.causal, rows=rows)[0]
+        od = _DENSE_CACHE[key]
         num += float(np.abs(O_gpu[h][rows] - od).sum())
         den += float(np.abs(od).sum())
-    return num / den, f"heads {heads}, query blocks {blocks}"
+    return num / den, f"heads {heads}, {len(blocks)} evenly spaced query blocks {blocks}"
 
 
 def reuse_sweep(sa, torch, w, oracle, n_steps=6, ks=(1, 3, 6), dtheta=0.05, threads=16):
@@ -274,7 +289,7 @@ def reuse_sweep(sa, torch, w, oracle, n_steps=6, ks=(1, 3, 6), dtheta=0.05, thre
     ws_p = torch.empty(max(pws, 1), dtype=torch.uint8, device=dev)
     ws_f = torch.empty(max(fws, 1), dtype=torch.uint8, device=dev)
     o = torch.empty((1, w.H, w.N, w.D), dtype=torch.bfloat16, device=dev)
-    blocks = sorted({0, nqb // 2, nqb - 1})
+    blocks = sample_blocks(nqb, 8)
     rows = np.concatenate([np.arange(i * 128, min(w.N, (i + 1) * 128)) for i in blocks])
     sm = 1.0 / math.sqrt(w.D)
     dense = {}
@@ -303,6 +318,61 @@ def reuse_sweep(sa, torch, w, oracle, n_steps=6, ks=(1, 3, 6), dtheta=0.05, thre
                         rel_l1_mean=round(float(np.mean(rels)), 6),
                         rel_l1_max=round(float(np.max(rels)), 6)))
     del xs
+    return out
+
+
+def reorder_sweep(sa, torch, w, q, k, v, Q, K, V, oracle, measure_on, taus=(0.9, 0.95, 0.98),
+                  iters=4, reps=3):
+    """Token reordering (sparse_attn_cluster + sparse_attn_permute) ahead of
+    the two stages: per metric, the time of the clustering (NQB query and NKB
+    key clusters per head, ``iters`` passes) and of the four row
+    permutations, then per tau the sparsity, P.V skip share, predict +
+    forward time and rel-L1 (dense fp64 on sampled rows, in the original row
+    order) of the pipeline run on the reordered tokens."""
+    p = sa.make_params(w.B, w.H, w.N, w.D, dtype=w.dtype)
+    nqb, nkb = sa.sparse_attn_mask_shape(p)
+    dev = q.device
+    out = []
+    for metric in ("interaction", "feature"):
+        cp = sa.make_cluster_params(nqb, nkb, iters, metric)
+        ws = torch.empty(sa.sparse_attn_cluster_workspace_size(p, cp), dtype=torch.uint8,
+                         device=dev)
+        pq, pk = (torch.empty((w.B, w.H, w.N), dtype=torch.int32, device=dev) for _ in range(2))
+        ro = sa.make_reorder(pq, pk)
+        sa.sparse_attn_cluster(p, cp, q, k, ro, ws)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            sa.sparse_attn_cluster(p, cp, q, k, ro, ws)
+        e1.record()
+        torch.cuda.synchronize()
+        cluster_ms = e0.elapsed_time(e1) / reps
+        del ws
+        qp, kp, vp = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        o_back = torch.empty_like(q)
+        e0.record()
+        sa.sparse_attn_permute(p, q, pq, 0, qp)
+        sa.sparse_attn_permute(p, k, pk, 0, kp)
+        sa.sparse_attn_permute(p, v, pk, 0, vp)
+        sa.sparse_attn_permute(p, q, pq, 1, o_back)   # the size of the O scatter
+        e1.record()
+        torch.cuda.synchronize()
+        permute_ms = e0.elapsed_time(e1)
+        rows = []
+        for tau in taus:
+            r, m = measure_on(qp, kp, vp, tau)
+            sa.sparse_attn_permute(p, r.o, pq, 1, o_back)
+            torch.cuda.synchronize()
+            rl, _ = rel_l1_sample(w, Q, K, V, o_back.float().cpu().numpy()[0], oracle)
+            rows.append(dict(tau=tau, sparsity=round(m["sparsity"], 5),
+                             pv_skip_fraction=round(m["skip"], 5), rel_l1=round(rl, 6),
+                             predict_forward_ms=round(m["ms"], 4)))
+            del r
+        out.append(dict(metric=metric, clusters_q=nqb, clusters_k=nkb, iters=iters,
+                        cluster_ms=round(cluster_ms, 4), permute_ms=round(permute_ms, 4),
+                        by_tau=rows))
+        del qp, kp, vp, o_back
     return out
 
 
@@ -356,8 +426,10 @@ def main():
     q, k, v = (torch.from_numpy(x).to(tdt).to(dev) for x in (Q, K, V))
     dense = w.dense_flops()
 
-    def measure(tau, steps, warmup, skip_rule=None, recall=None, rule=None, topk_blocks=0):
-        r = Runner(sa, torch, w, q, k, v, tau,
+    def measure(tau, steps, warmup, skip_rule=None, recall=None, rule=None, topk_blocks=0,
+                tensors=None):
+        qq, kk, vv = tensors or (q, k, v)
+        r = Runner(sa, torch, w, qq, kk, vv, tau,
                    skip_rule=skip_rule or args.skip_rule,
                    recall=args.recall if recall is None else recall, rule=rule,
                    topk_blocks=topk_blocks)
@@ -438,6 +510,16 @@ def main():
         for r_ in reuse:
             print(f"[bench] reuse {r_}", file=sys.stderr, flush=True)
 
+    reorder = []
+    if not args.no_sweep and w.name == "wan_video":
+        print("[bench] token reordering", file=sys.stderr, flush=True)
+        reorder = reorder_sweep(
+            sa, torch, w, q, k, v, Q, K, V, oracle,
+            lambda qq, kk, vv, tau: measure(tau, max(3, args.steps // 4), 1,
+                                            tensors=(qq, kk, vv)))
+        for r_ in reorder:
+            print(f"[bench] reorder {r_}", file=sys.stderr, flush=True)
+
     cpu = None
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle sample", file=sys.stderr, flush=True)
@@ -486,6 +568,7 @@ def main():
         "topk_rule_sweep": topk_sweep,
         "mask_reuse": {"sequence": "6 calls, inputs cos(0.05 s) A + sin(0.05 s) B (seeded)",
                        "by_refresh_every": reuse},
+        "token_reorder": reorder,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

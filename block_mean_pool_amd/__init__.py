@@ -15,6 +15,9 @@ Entry points have the C names:
                         ws=None, stream=None)
     sparse_attn_step(params, schedule, q, k, v, mask, o, lse=None,
                      skip_bits=None, predict_ws=None, forward_ws=None, stream=None)
+    sparse_attn_cluster_workspace_size(params, cluster_params) -> bytes
+    sparse_attn_cluster(params, cluster_params, q, k, reorder, ws, stream=None)
+    sparse_attn_permute(params, x, perm, inverse, y, stream=None)
     sparse_attn_info() -> (default_group_rows, version)
     sparse_attn_status_str(code) -> str
     sparse_attn_last_error() -> str
@@ -35,6 +38,7 @@ SA_F32, SA_BF16 = 0, 1
 SA_PREC_NATIVE, SA_PREC_I8_FP8 = 0, 1
 SA_RULE_TOPCDF, SA_RULE_ENERGY, SA_RULE_TOPK = 0, 1, 2
 SA_SKIP_LAMBDA, SA_SKIP_RECALL = 0, 1
+SA_METRIC_FEATURE, SA_METRIC_INTERACTION = 0, 1
 
 
 class SaParams(ctypes.Structure):
@@ -60,6 +64,16 @@ class SaMask(ctypes.Structure):
 class SaSchedule(ctypes.Structure):
     _fields_ = [("refresh_every", ctypes.c_int32), ("dense_steps", ctypes.c_int32),
                 ("step", ctypes.c_int32), ("refreshed", ctypes.c_int32)]
+
+
+class SaClusterParams(ctypes.Structure):
+    _fields_ = [("clusters_q", ctypes.c_int32), ("clusters_k", ctypes.c_int32),
+                ("iters", ctypes.c_int32), ("metric", ctypes.c_int32)]
+
+
+class SaReorder(ctypes.Structure):
+    _fields_ = [("perm_q", ctypes.c_void_p), ("perm_k", ctypes.c_void_p),
+                ("labels_q", ctypes.c_void_p), ("labels_k", ctypes.c_void_p)]
 
 
 class SparseAttnError(RuntimeError):
@@ -91,6 +105,11 @@ def _load():
         "sparse_attn_info": [P(ctypes.c_int32), P(ctypes.c_int32)],
         "sparse_attn_step": [P(SaParams), P(SaSchedule), vp, vp, vp, P(SaMask), vp, vp, vp, vp,
                              ctypes.c_size_t, vp, ctypes.c_size_t, vp],
+        "sparse_attn_cluster_workspace_size": [P(SaParams), P(SaClusterParams),
+                                               P(ctypes.c_size_t)],
+        "sparse_attn_cluster": [P(SaParams), P(SaClusterParams), vp, vp, P(SaReorder), vp,
+                                ctypes.c_size_t, vp],
+        "sparse_attn_permute": [P(SaParams), vp, vp, ctypes.c_int32, ctypes.c_int32, vp, vp],
     }
     for name, args in sig.items():
         f = getattr(lib, name)
@@ -226,9 +245,50 @@ def sparse_attn_step(p: SaParams, sched: SaSchedule, q, k, v, mask: SaMask, o, l
            "sparse_attn_step")
 
 
+def make_cluster_params(clusters_q, clusters_k, iters=4, metric="interaction") -> SaClusterParams:
+    """Token clustering parameters; ``metric`` is "interaction" or "feature"."""
+    m = {"feature": SA_METRIC_FEATURE, "interaction": SA_METRIC_INTERACTION}[metric] \
+        if isinstance(metric, str) else int(metric)
+    return SaClusterParams(int(clusters_q), int(clusters_k), int(iters), m)
+
+
+def make_reorder(perm_q, perm_k, labels_q=None, labels_k=None) -> SaReorder:
+    return SaReorder(_ptr(perm_q), _ptr(perm_k), _ptr(labels_q), _ptr(labels_k))
+
+
+def sparse_attn_cluster_workspace_size(p: SaParams, cp: SaClusterParams) -> int:
+    n = ctypes.c_size_t()
+    _check(lib.sparse_attn_cluster_workspace_size(ctypes.byref(p), ctypes.byref(cp),
+                                                  ctypes.byref(n)),
+           "sparse_attn_cluster_workspace_size")
+    return n.value
+
+
+def sparse_attn_cluster(p: SaParams, cp: SaClusterParams, q, k, out: SaReorder, ws,
+                        stream=None, ws_bytes=None):
+    """Clusters query and key tokens; writes the orders (and labels) of
+    ``out`` (SaReorder over device int32 [B, H, N] buffers)."""
+    nb = _nbytes(ws) if ws_bytes is None else ws_bytes
+    _check(lib.sparse_attn_cluster(ctypes.byref(p), ctypes.byref(cp), _ptr(q), _ptr(k),
+                                   ctypes.byref(out), _ptr(ws), nb, _stream(stream)),
+           "sparse_attn_cluster")
+
+
+def sparse_attn_permute(p: SaParams, x, perm, inverse, y, stream=None, elem_bytes=None):
+    """Row gather (inverse=0: y[r] = x[perm[r]]) or scatter (inverse=1:
+    y[perm[r]] = x[r]) of [B, H, N, D] tensors; ``elem_bytes`` defaults to
+    x's element size."""
+    eb = x.element_size() if elem_bytes is None else int(elem_bytes)
+    _check(lib.sparse_attn_permute(ctypes.byref(p), _ptr(x), _ptr(perm), int(inverse), eb,
+                                   _ptr(y), _stream(stream)), "sparse_attn_permute")
+
+
 __all__ = [
     "SaParams", "SaMask", "SparseAttnError", "make_params", "make_mask",
     "sparse_attn_mask_shape", "sparse_attn_workspace_size", "sparse_attn_predict",
     "sparse_attn_forward", "sparse_attn_info", "sparse_attn_status_str",
+    "SaClusterParams", "SaReorder", "make_cluster_params", "make_reorder",
+    "sparse_attn_cluster_workspace_size", "sparse_attn_cluster", "sparse_attn_permute",
+    "SaSchedule", "make_schedule", "sparse_attn_step",
     "sparse_attn_last_error", "lib", "LIB_PATH", "HEADER",
 ]

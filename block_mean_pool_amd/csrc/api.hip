@@ -299,6 +299,171 @@ sa_status sparse_attn_step(const sa_params* p, sa_schedule* sched, const void* q
   return ok();
 }
 
+}  // extern "C"
+
+namespace {
+
+struct ClusterLayout {
+  size_t M, mpart, cent, ghi, glo, bvec, labels, perm, hist, seg, cnt, total;
+  int nch, nchm, mspan, cmax;
+};
+
+ClusterLayout cluster_layout(const sa::Geometry& g, const sa_cluster_params* cp) {
+  ClusterLayout L{};
+  const size_t z2 = 2 * (size_t)g.B * g.H;
+  const bool inter = cp->metric == SA_METRIC_INTERACTION;
+  L.cmax = cp->clusters_q > cp->clusters_k ? cp->clusters_q : cp->clusters_k;
+  L.nch = (g.N + 255) / 256;
+  L.nchm = 0;
+  L.mspan = 0;
+  if (inter) {
+    const int want = (g.N + 2047) / 2048;
+    L.nchm = want < 1 ? 1 : (want > 16 ? 16 : want);
+    const int per = (g.N + L.nchm - 1) / L.nchm;
+    L.mspan = (per + 63) / 64 * 64;
+  }
+  const size_t D = g.D, C = L.cmax, N = g.N;
+  size_t o = 0;
+  L.M = o;
+  o += inter ? round_up(z2 * D * D * 4) : 0;
+  L.mpart = o;
+  o += inter ? round_up(z2 * L.nchm * D * D * 4) : 0;
+  L.cent = o;
+  o += round_up(z2 * C * D * 4);
+  L.ghi = o;
+  o += round_up(z2 * C * D * 2);
+  L.glo = o;
+  o += round_up(z2 * C * D * 2);
+  L.bvec = o;
+  o += round_up(z2 * C * 4);
+  L.labels = o;
+  o += round_up(z2 * N * 4);
+  L.perm = o;
+  o += round_up(z2 * N * 4);
+  L.hist = o;
+  o += round_up(z2 * L.nch * C * 4);
+  L.seg = o;
+  o += round_up(z2 * C * 4);
+  L.cnt = o;
+  o += round_up(z2 * C * 4);
+  L.total = o;
+  return L;
+}
+
+sa_status check_cluster(const sa_params* p, const sa_cluster_params* cp, sa::Geometry* g,
+                        bool* empty) {
+  sa_status st = check_params(p, g, empty);
+  if (st) return st;
+  if (!cp) return fail(SA_ERR_INVALID_ARG, "cluster params is NULL");
+  if (p->dtype != SA_BF16) return fail(SA_ERR_UNSUPPORTED, "token clustering needs bf16 Q and K");
+  if (p->causal)
+    return fail(SA_ERR_INVALID_ARG, "token reordering is defined for non-causal attention only");
+  if (cp->metric != SA_METRIC_FEATURE && cp->metric != SA_METRIC_INTERACTION)
+    return fail(SA_ERR_INVALID_ARG, "metric=%d", cp->metric);
+  if (cp->iters < 1 || cp->iters > 64)
+    return fail(SA_ERR_INVALID_ARG, "iters=%d (must be in [1, 64])", cp->iters);
+  const int cap = p->N < sa::kMaxClusters ? p->N : sa::kMaxClusters;
+  if (!*empty && (cp->clusters_q < 1 || cp->clusters_q > cap || cp->clusters_k < 1 ||
+                  cp->clusters_k > cap))
+    return fail(SA_ERR_INVALID_ARG, "clusters_q=%d clusters_k=%d (must be in [1, min(N, %d)])",
+                cp->clusters_q, cp->clusters_k, sa::kMaxClusters);
+  if (2LL * p->B * p->H > 65535)
+    return fail(SA_ERR_UNSUPPORTED, "B*H=%lld > 32767 for token clustering",
+                (long long)p->B * p->H);
+  return SA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+sa_status sparse_attn_cluster_workspace_size(const sa_params* p, const sa_cluster_params* cp,
+                                             size_t* ws) {
+  sa::Geometry g;
+  bool empty;
+  sa_status st = check_cluster(p, cp, &g, &empty);
+  if (st) return st;
+  if (ws) *ws = empty ? 0 : cluster_layout(g, cp).total;
+  return ok();
+}
+
+sa_status sparse_attn_cluster(const sa_params* p, const sa_cluster_params* cp, const void* q,
+                              const void* k, const sa_reorder* out, void* ws, size_t ws_bytes,
+                              void* stream) {
+  sa::Geometry g;
+  bool empty;
+  sa_status st = check_cluster(p, cp, &g, &empty);
+  if (st) return st;
+  if (empty) return ok();
+  if (!q || !k) return fail(SA_ERR_INVALID_ARG, "q or k is NULL");
+  if (!aligned16(q) || !aligned16(k)) return fail(SA_ERR_INVALID_ARG, "q/k not 16-byte aligned");
+  if (!out || !out->perm_q || !out->perm_k)
+    return fail(SA_ERR_INVALID_ARG, "reorder output (perm_q, perm_k) is NULL");
+  const ClusterLayout L = cluster_layout(g, cp);
+  if (!ws || ws_bytes < L.total)
+    return fail(SA_ERR_WORKSPACE, "cluster workspace %zu < %zu bytes", ws_bytes, L.total);
+  if (!aligned16(ws)) return fail(SA_ERR_INVALID_ARG, "workspace not 16-byte aligned");
+  char* w = static_cast<char*>(ws);
+  sa::ClusterLaunch a{};
+  a.g = g;
+  a.q = q;
+  a.k = k;
+  a.cq = cp->clusters_q;
+  a.ck = cp->clusters_k;
+  a.cmax = L.cmax;
+  a.iters = cp->iters;
+  a.interaction = cp->metric == SA_METRIC_INTERACTION;
+  a.nch = L.nch;
+  a.nchm = L.nchm;
+  a.mspan = L.mspan;
+  a.M = reinterpret_cast<float*>(w + L.M);
+  a.mpart = reinterpret_cast<float*>(w + L.mpart);
+  a.cent = reinterpret_cast<float*>(w + L.cent);
+  a.ghi = reinterpret_cast<uint16_t*>(w + L.ghi);
+  a.glo = reinterpret_cast<uint16_t*>(w + L.glo);
+  a.bvec = reinterpret_cast<float*>(w + L.bvec);
+  a.labels = reinterpret_cast<int32_t*>(w + L.labels);
+  a.perm = reinterpret_cast<int32_t*>(w + L.perm);
+  a.hist = reinterpret_cast<int32_t*>(w + L.hist);
+  a.seg = reinterpret_cast<int32_t*>(w + L.seg);
+  a.cnt = reinterpret_cast<int32_t*>(w + L.cnt);
+  a.perm_q = out->perm_q;
+  a.perm_k = out->perm_k;
+  a.labels_q = out->labels_q;
+  a.labels_k = out->labels_k;
+  hipError_t e = sa::launch_cluster(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(SA_ERR_HIP, "cluster launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+sa_status sparse_attn_permute(const sa_params* p, const void* x, const int32_t* perm,
+                              int32_t inverse, int32_t elem_bytes, void* y, void* stream) {
+  sa::Geometry g;
+  bool empty;
+  sa_status st = check_params(p, &g, &empty);
+  if (st) return st;
+  if (inverse != 0 && inverse != 1) return fail(SA_ERR_INVALID_ARG, "inverse=%d", inverse);
+  if (elem_bytes != 2 && elem_bytes != 4)
+    return fail(SA_ERR_INVALID_ARG, "elem_bytes=%d (2 or 4)", elem_bytes);
+  if (empty) return ok();
+  if (!x || !y || !perm) return fail(SA_ERR_INVALID_ARG, "x, y or perm is NULL");
+  if (x == y) return fail(SA_ERR_INVALID_ARG, "x and y must be different buffers");
+  if (!aligned16(x) || !aligned16(y)) return fail(SA_ERR_INVALID_ARG, "x/y not 16-byte aligned");
+  if ((g.sn * elem_bytes) % 16 || (g.sh * elem_bytes) % 16 || (g.sb * elem_bytes) % 16)
+    return fail(SA_ERR_INVALID_ARG, "strides must keep rows 16-byte aligned");
+  sa::PermuteLaunch a{};
+  a.g = g;
+  a.x = x;
+  a.y = y;
+  a.perm = perm;
+  a.inverse = inverse;
+  a.esz = elem_bytes;
+  a.row_bytes = g.D * elem_bytes;
+  hipError_t e = sa::launch_permute(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(SA_ERR_HIP, "permute launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
 sa_status sparse_attn_info(int32_t* default_group_rows, int32_t* version) {
   if (default_group_rows) *default_group_rows = 32;
   if (version) *version = SPARSE_ATTN_VERSION;

@@ -1,0 +1,431 @@
+// Token reordering for the block-mean predictor: the query tokens and the
+// key tokens of each head are clustered, and each side is put in cluster
+// order, so that the fixed blocks cut from the reordered sequence hold
+// tokens that one mean represents well.
+//
+// iCATS abstract (arxivdaily.com page): grouping tokens by their query-key
+// dot-product interaction estimates block scores better than grouping each
+// side by feature similarity, and that objective is a simple quadratic form;
+// irregular cluster sizes are handled by merging tails rather than padding.
+// PARO abstract (huggingface-mirror search page): reordering tokens turns the
+// attention pattern block-wise.
+//
+// Readings: replacing a query x by c moves its logit with key k by
+// sm (x - c) . k, and the mean square of that move over the keys is
+// sm^2 (x - c)^T M_K (x - c), M_K = K^T K / N.  So queries cluster under the
+// quadratic form of M_K, keys under that of M_Q ("interaction"); "feature"
+// uses M = I.  Centroid m starts at token floor((2m+1) N / (2C)); T Lloyd
+// passes; ties go to the smaller cluster; a cluster without members keeps its
+// centroid; tokens are ordered by (cluster, position), clusters packed back
+// to back with no padding.
+//
+// Kernels, per slot z = 2 (b H + h) + side (side 0 = queries, 1 = keys):
+//   moment_kernel    partial X^T X of the other side over a token range
+//                    (bf16 MFMA: exact products, fp32 sums)
+//   moment_reduce    sums the partials in a fixed order, divides by N
+//   centroid_kernel  the seeds (first pass) or the member means, summed in
+//                    the cluster-sorted order of the previous pass
+//   metric_kernel    G_m = M c_m as bf16 hi + lo parts, b_m = c_m . G_m
+//   assign_kernel    label = argmin_m (b_m - 2 x . G_m), i.e. the quadratic
+//                    form without its constant x^T M x; x . G_m by bf16 MFMA
+//                    on the hi and lo parts (the tokens are bf16, exact)
+//   hist / scan / scatter  stable counting sort of the labels: the order,
+//                    each cluster's offset and size
+//   export_kernel    the order and labels to the caller's [B,H,N] arrays
+//   permute_kernel   row gather (or scatter) by a permutation
+// Every reduction runs in a fixed order, so the results are deterministic.
+#include "sa_device.h"
+#include "sa_internal.h"
+#include "../../include/sparse_attn.h"
+
+namespace sa {
+namespace {
+
+__device__ __forceinline__ const __bf16* slot_tokens(const ClusterLaunch& a, int z, bool other) {
+  const int bh = z >> 1, side = z & 1;
+  const int b = bh / a.g.H, h = bh - b * a.g.H;
+  const bool keys = other ? side == 0 : side == 1;
+  const __bf16* base = static_cast<const __bf16*>(keys ? a.k : a.q);
+  return base + (int64_t)b * a.g.sb + (int64_t)h * a.g.sh;
+}
+
+__device__ __forceinline__ int slot_clusters(const ClusterLaunch& a, int z) {
+  return (z & 1) ? a.ck : a.cq;
+}
+
+__device__ __forceinline__ f32x16 mfma_bf16(const u32x4& a, const u32x4& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// ---------------------------------------------------------------- moments
+constexpr int kMomentTokens = 64;  // tokens per LDS chunk
+
+// Partial sum over tokens [c * span, (c + 1) * span) of x x^T for the other
+// side's tokens of slot z.  The chunk is stored transposed in LDS ([d][token])
+// so that both MFMA operands are 16-byte reads of 8 consecutive tokens.
+template <int D>
+__global__ __launch_bounds__(256) void moment_kernel(ClusterLaunch a, int span) {
+  constexpr int NB = D / 32;
+  constexpr int TPW = NB * NB / 4;            // 32x32 tiles of M per wavefront
+  constexpr int LDT = kMomentTokens + 8;      // padded row, in tokens
+  __shared__ __align__(16) uint16_t T[D * LDT];
+  const int z = blockIdx.y, c = blockIdx.x;
+  const __bf16* X = slot_tokens(a, z, true);
+  const int t0 = c * span, t1 = min(a.g.N, t0 + span);
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int l32 = lane & 31, hh = lane >> 5;
+
+  f32x16 acc[TPW];
+#pragma unroll
+  for (int tt = 0; tt < TPW; ++tt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[tt][r] = 0.f;
+
+  for (int base = t0; base < t1; base += kMomentTokens) {
+    __syncthreads();
+#pragma unroll
+    for (int e = tid; e < kMomentTokens * D / 8; e += 256) {
+      const int tok = e / (D / 8), dc = e - tok * (D / 8);
+      const int row = base + tok;
+      const u32x4 v = row < t1 ? *reinterpret_cast<const u32x4*>(X + (int64_t)row * a.g.sn + dc * 8)
+                               : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        T[(dc * 8 + 2 * i) * LDT + tok] = (uint16_t)(v[i] & 0xffffu);
+        T[(dc * 8 + 2 * i + 1) * LDT + tok] = (uint16_t)(v[i] >> 16);
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int ks = 0; ks < kMomentTokens / 16; ++ks)
+#pragma unroll
+      for (int tt = 0; tt < TPW; ++tt) {
+        const int ti = w * TPW + tt, rb = ti / NB, cb = ti - rb * NB;
+        const u32x4 av =
+            *reinterpret_cast<const u32x4*>(&T[(32 * rb + l32) * LDT + 16 * ks + 8 * hh]);
+        const u32x4 bv =
+            *reinterpret_cast<const u32x4*>(&T[(32 * cb + l32) * LDT + 16 * ks + 8 * hh]);
+        acc[tt] = mfma_bf16(av, bv, acc[tt]);
+      }
+  }
+  float* P = a.mpart + ((size_t)z * a.nchm + c) * D * D;
+#pragma unroll
+  for (int tt = 0; tt < TPW; ++tt) {
+    const int ti = w * TPW + tt, rb = ti / NB, cb = ti - rb * NB;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int i = 32 * rb + 8 * (r >> 2) + 4 * hh + (r & 3);
+      P[i * D + 32 * cb + l32] = acc[tt][r];
+    }
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void moment_reduce(ClusterLaunch a) {
+  const int z = blockIdx.y;
+  const int e = blockIdx.x * 256 + threadIdx.x;
+  if (e >= D * D) return;
+  const float* P = a.mpart + (size_t)z * a.nchm * D * D + e;
+  float s = 0.f;
+  for (int c = 0; c < a.nchm; ++c) s += P[(size_t)c * D * D];
+  a.M[(size_t)z * D * D + e] = s / (float)a.g.N;
+}
+
+// -------------------------------------------------------------- centroids
+// One workgroup per (cluster, slot), thread d owns column d.  First pass: the
+// seed token.  Later passes: the mean of the members, read in the order of
+// the previous pass's sort (fixed), four interleaved partial sums.
+template <int D>
+__global__ __launch_bounds__(128) void centroid_kernel(ClusterLaunch a, int seed_pass) {
+  const int z = blockIdx.y, m = blockIdx.x, d = threadIdx.x;
+  const int C = slot_clusters(a, z);
+  if (m >= C || d >= D) return;
+  const __bf16* X = slot_tokens(a, z, false);
+  float* c = a.cent + ((size_t)z * a.cmax + m) * D;
+  const int64_t sn = a.g.sn;
+  if (seed_pass) {
+    const int s = (int)(((2LL * m + 1) * a.g.N) / (2LL * C));
+    c[d] = (float)X[(int64_t)s * sn + d];
+    return;
+  }
+  const int n = a.cnt[(size_t)z * a.cmax + m];
+  if (n == 0) return;  // no member: the centroid stays
+  const int32_t* pm = a.perm + (size_t)z * a.g.N + a.seg[(size_t)z * a.cmax + m];
+  float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
+  int r = 0;
+  for (; r + 4 <= n; r += 4) {
+    s0 += (float)X[(int64_t)pm[r] * sn + d];
+    s1 += (float)X[(int64_t)pm[r + 1] * sn + d];
+    s2 += (float)X[(int64_t)pm[r + 2] * sn + d];
+    s3 += (float)X[(int64_t)pm[r + 3] * sn + d];
+  }
+  for (; r < n; ++r) s0 += (float)X[(int64_t)pm[r] * sn + d];
+  c[d] = ((s0 + s1) + (s2 + s3)) / (float)n;
+}
+
+// ----------------------------------------------------------------- metric
+constexpr int kMetricClusters = 16;  // clusters per workgroup
+
+// G_m = M c_m for kMetricClusters clusters (M read once per workgroup; M is
+// symmetric, so thread i reads column i: coalesced), stored as bf16 hi and
+// lo = bf16(G - hi); b_m = c_m . G_m in a fixed order.
+template <int D>
+__global__ __launch_bounds__(128) void metric_kernel(ClusterLaunch a) {
+  __shared__ float cs[kMetricClusters][D];
+  __shared__ float gs[kMetricClusters][D];
+  const int z = blockIdx.y, m0 = blockIdx.x * kMetricClusters, i = threadIdx.x;
+  const int C = slot_clusters(a, z);
+  if (m0 >= C) return;
+  const int nm = min(kMetricClusters, C - m0);
+  const float* cent = a.cent + ((size_t)z * a.cmax + m0) * D;
+  for (int e = i; e < nm * D; e += 128) cs[e / D][e % D] = cent[e];
+  __syncthreads();
+  if (i < D) {
+    float g[kMetricClusters];
+#pragma unroll
+    for (int mm = 0; mm < kMetricClusters; ++mm) g[mm] = 0.f;
+    if (a.interaction) {
+      const float* Mz = a.M + (size_t)z * D * D;
+      for (int j = 0; j < D; ++j) {
+        const float mji = Mz[j * D + i];
+#pragma unroll
+        for (int mm = 0; mm < kMetricClusters; ++mm) g[mm] = fmaf(mji, cs[mm][j], g[mm]);
+      }
+    } else {
+#pragma unroll
+      for (int mm = 0; mm < kMetricClusters; ++mm) g[mm] = cs[mm][i];
+    }
+    for (int mm = 0; mm < nm; ++mm) {
+      const __bf16 hi = (__bf16)g[mm];
+      const __bf16 lo = (__bf16)(g[mm] - (float)hi);
+      const size_t off = ((size_t)z * a.cmax + m0 + mm) * D + i;
+      a.ghi[off] = __builtin_bit_cast(uint16_t, hi);
+      a.glo[off] = __builtin_bit_cast(uint16_t, lo);
+      gs[mm][i] = g[mm];
+    }
+  }
+  __syncthreads();
+  if (i < nm) {
+    float s = 0.f;
+    for (int j = 0; j < D; ++j) s = fmaf(cs[i][j], gs[i][j], s);
+    a.bvec[(size_t)z * a.cmax + m0 + i] = s;
+  }
+}
+
+// ----------------------------------------------------------------- assign
+// 256 tokens per workgroup, 64 per wavefront (two 32-token MFMA columns).
+// Cluster tiles of 32 rows of G (hi and lo) go through LDS; the Sᵀ-style
+// product D[m][x] = G_m . x comes out with lane -> token column, so each
+// lane scans 16 clusters per tile in increasing order and the two lane
+// halves merge at the end (ties to the smaller index).
+template <int D>
+__global__ __launch_bounds__(256) void assign_kernel(ClusterLaunch a) {
+  constexpr int NKK = D / 16;
+  constexpr int RS = D * 2 + 16;  // LDS row stride in bytes (padded)
+  __shared__ __align__(16) char Ahi[32 * RS];
+  __shared__ __align__(16) char Alo[32 * RS];
+  __shared__ float bt[32];
+  const int z = blockIdx.y;
+  const int C = slot_clusters(a, z);
+  const __bf16* X = slot_tokens(a, z, false);
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int l32 = lane & 31, hh = lane >> 5;
+  const int tok0 = blockIdx.x * 256 + w * 64;
+
+  u32x4 xf[2][NKK];
+#pragma unroll
+  for (int gi = 0; gi < 2; ++gi) {
+    const int row = tok0 + 32 * gi + l32;
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk)
+      xf[gi][kk] = row < a.g.N ? *reinterpret_cast<const u32x4*>(X + (int64_t)row * a.g.sn +
+                                                                 16 * kk + 8 * hh)
+                               : u32x4{0u, 0u, 0u, 0u};
+  }
+  float best[2] = {INFINITY, INFINITY};
+  int bidx[2] = {0, 0};
+  const uint16_t* ghi = a.ghi + (size_t)z * a.cmax * D;
+  const uint16_t* glo = a.glo + (size_t)z * a.cmax * D;
+  for (int m0 = 0; m0 < C; m0 += 32) {
+    __syncthreads();
+    for (int e = tid; e < 2 * 32 * (D / 8); e += 256) {
+      const int part = e / (32 * (D / 8)), rem = e - part * (32 * (D / 8));
+      const int r = rem / (D / 8), ch = rem - r * (D / 8);
+      const int m = m0 + r;
+      const uint16_t* src = (part ? glo : ghi) + (size_t)m * D + ch * 8;
+      const u32x4 v = m < C ? *reinterpret_cast<const u32x4*>(src) : u32x4{0u, 0u, 0u, 0u};
+      *reinterpret_cast<u32x4*>((part ? Alo : Ahi) + r * RS + ch * 16) = v;
+    }
+    if (tid < 32) bt[tid] = m0 + tid < C ? a.bvec[(size_t)z * a.cmax + m0 + tid] : 0.f;
+    __syncthreads();
+    f32x16 acc[2];
+#pragma unroll
+    for (int gi = 0; gi < 2; ++gi)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[gi][r] = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+      const u32x4 ah = *reinterpret_cast<const u32x4*>(Ahi + l32 * RS + (16 * kk + 8 * hh) * 2);
+      const u32x4 al = *reinterpret_cast<const u32x4*>(Alo + l32 * RS + (16 * kk + 8 * hh) * 2);
+#pragma unroll
+      for (int gi = 0; gi < 2; ++gi) {
+        acc[gi] = mfma_bf16(ah, xf[gi][kk], acc[gi]);
+        acc[gi] = mfma_bf16(al, xf[gi][kk], acc[gi]);
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int i = 8 * (r >> 2) + 4 * hh + (r & 3);
+      if (m0 + i < C) {
+#pragma unroll
+        for (int gi = 0; gi < 2; ++gi) {
+          const float dist = fmaf(-2.f, acc[gi][r], bt[i]);
+          if (dist < best[gi]) {
+            best[gi] = dist;
+            bidx[gi] = m0 + i;
+          }
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int gi = 0; gi < 2; ++gi) {
+    const float pd = __shfl_xor(best[gi], 32, 64);
+    const int pi = __shfl_xor(bidx[gi], 32, 64);
+    if (pd < best[gi] || (pd == best[gi] && pi < bidx[gi])) bidx[gi] = pi;
+    const int row = tok0 + 32 * gi + l32;
+    if (hh == 0 && row < a.g.N) a.labels[(size_t)z * a.g.N + row] = bidx[gi];
+  }
+}
+
+// ------------------------------------------------------------ counting sort
+constexpr int kSortTokens = 256;  // tokens per chunk
+
+__global__ __launch_bounds__(256) void hist_kernel(ClusterLaunch a) {
+  extern __shared__ int32_t hs[];
+  const int z = blockIdx.y, ch = blockIdx.x, tid = threadIdx.x;
+  const int C = slot_clusters(a, z);
+  for (int e = tid; e < C; e += 256) hs[e] = 0;
+  __syncthreads();
+  const int x = ch * kSortTokens + tid;
+  if (x < a.g.N) atomicAdd(&hs[a.labels[(size_t)z * a.g.N + x]], 1);
+  __syncthreads();
+  int32_t* row = a.hist + ((size_t)z * a.nch + ch) * a.cmax;
+  for (int e = tid; e < C; e += 256) row[e] = hs[e];
+}
+
+// Per slot: cluster sizes, their exclusive prefix (cluster offsets), and the
+// chunk counts turned in place into each (chunk, cluster) start position.
+__global__ __launch_bounds__(1024) void scan_kernel(ClusterLaunch a) {
+  __shared__ int32_t tot[kMaxClusters];
+  const int z = blockIdx.x, tid = threadIdx.x;
+  const int C = slot_clusters(a, z);
+  int32_t* H = a.hist + (size_t)z * a.nch * a.cmax;
+  for (int m = tid; m < C; m += 1024) {
+    int s = 0;
+    for (int c = 0; c < a.nch; ++c) s += H[(size_t)c * a.cmax + m];
+    tot[m] = s;
+    a.cnt[(size_t)z * a.cmax + m] = s;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    int run = 0;
+    for (int m = 0; m < C; ++m) {
+      const int t = tot[m];
+      tot[m] = run;
+      run += t;
+    }
+  }
+  __syncthreads();
+  for (int m = tid; m < C; m += 1024) {
+    int run = tot[m];
+    a.seg[(size_t)z * a.cmax + m] = run;
+    for (int c = 0; c < a.nch; ++c) {
+      int32_t* p = H + (size_t)c * a.cmax + m;
+      const int t = *p;
+      *p = run;
+      run += t;
+    }
+  }
+}
+
+// Each token's position: its (chunk, cluster) start plus the number of
+// earlier tokens of the chunk in the same cluster (stable).
+__global__ __launch_bounds__(256) void scatter_kernel(ClusterLaunch a) {
+  __shared__ int32_t lab[kSortTokens];
+  const int z = blockIdx.y, ch = blockIdx.x, tid = threadIdx.x;
+  const int x = ch * kSortTokens + tid;
+  const int L = x < a.g.N ? a.labels[(size_t)z * a.g.N + x] : -1;
+  lab[tid] = L;
+  __syncthreads();
+  if (x < a.g.N) {
+    int rank = 0;
+    for (int t = 0; t < tid; ++t) rank += lab[t] == L ? 1 : 0;
+    const int pos = a.hist[((size_t)z * a.nch + ch) * a.cmax + L] + rank;
+    a.perm[(size_t)z * a.g.N + pos] = x;
+  }
+}
+
+__global__ __launch_bounds__(256) void export_kernel(ClusterLaunch a) {
+  const int z = blockIdx.y, bh = z >> 1, side = z & 1;
+  const int r = blockIdx.x * 256 + threadIdx.x;
+  if (r >= a.g.N) return;
+  const size_t src = (size_t)z * a.g.N + r, dst = (size_t)bh * a.g.N + r;
+  (side ? a.perm_k : a.perm_q)[dst] = a.perm[src];
+  int32_t* lab = side ? a.labels_k : a.labels_q;
+  if (lab) lab[dst] = a.labels[src];
+}
+
+// ---------------------------------------------------------------- permute
+// One 16-byte chunk per thread.  perm entries outside [0, N) are skipped.
+__global__ __launch_bounds__(256) void permute_kernel(PermuteLaunch a) {
+  const int cpr = a.row_bytes / 16, rpw = 256 / cpr;
+  const int bh = blockIdx.y, tid = threadIdx.x;
+  const int r = blockIdx.x * rpw + tid / cpr, ch = tid - (tid / cpr) * cpr;
+  if (tid / cpr >= rpw || r >= a.g.N) return;
+  const int p = a.perm[(size_t)bh * a.g.N + r];
+  if ((unsigned)p >= (unsigned)a.g.N) return;
+  const int src_row = a.inverse ? r : p, dst_row = a.inverse ? p : r;
+  const int b = bh / a.g.H, h = bh - b * a.g.H;
+  const int64_t off = ((int64_t)b * a.g.sb + (int64_t)h * a.g.sh) * a.esz;
+  const int64_t rs = a.g.sn * a.esz;
+  *reinterpret_cast<u32x4*>(static_cast<char*>(a.y) + off + dst_row * rs + ch * 16) =
+      *reinterpret_cast<const u32x4*>(static_cast<const char*>(a.x) + off + src_row * rs + ch * 16);
+}
+
+template <int D>
+hipError_t launch_cluster_t(const ClusterLaunch& a, hipStream_t s) {
+  const int z2 = 2 * a.g.B * a.g.H;
+  if (a.interaction) {
+    hipLaunchKernelGGL((moment_kernel<D>), dim3(a.nchm, z2), dim3(256), 0, s, a, a.mspan);
+    hipLaunchKernelGGL((moment_reduce<D>), dim3((D * D + 255) / 256, z2), dim3(256), 0, s, a);
+  }
+  const dim3 gc(a.cmax, z2), gm((a.cmax + kMetricClusters - 1) / kMetricClusters, z2);
+  const dim3 ga((a.g.N + 255) / 256, z2), gs(a.nch, z2);
+  for (int t = 0; t < a.iters; ++t) {
+    hipLaunchKernelGGL((centroid_kernel<D>), gc, dim3(128), 0, s, a, t == 0 ? 1 : 0);
+    hipLaunchKernelGGL((metric_kernel<D>), gm, dim3(128), 0, s, a);
+    hipLaunchKernelGGL((assign_kernel<D>), ga, dim3(256), 0, s, a);
+    hipLaunchKernelGGL(hist_kernel, gs, dim3(256), a.cmax * sizeof(int32_t), s, a);
+    hipLaunchKernelGGL(scan_kernel, dim3(z2), dim3(1024), 0, s, a);
+    hipLaunchKernelGGL(scatter_kernel, gs, dim3(256), 0, s, a);
+  }
+  hipLaunchKernelGGL(export_kernel, dim3((a.g.N + 255) / 256, z2), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_cluster(const ClusterLaunch& a, hipStream_t s) {
+  return a.g.D == 128 ? launch_cluster_t<128>(a, s) : launch_cluster_t<64>(a, s);
+}
+
+hipError_t launch_permute(const PermuteLaunch& a, hipStream_t s) {
+  const int rpw = 256 / (a.row_bytes / 16);
+  hipLaunchKernelGGL(permute_kernel, dim3((a.g.N + rpw - 1) / rpw, a.g.B * a.g.H), dim3(256), 0,
+                     s, a);
+  return hipGetLastError();
+}
+
+}  // namespace sa

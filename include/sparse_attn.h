@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define SPARSE_ATTN_VERSION 4
+#define SPARSE_ATTN_VERSION 5
 
 #if defined(__GNUC__)
 #define SA_API __attribute__((visibility("default")))
@@ -230,6 +230,78 @@ SA_API sa_status sparse_attn_step(const sa_params* p, sa_schedule* sched, const 
                            float* lse, uint32_t* skip_bits, void* predict_ws,
                            size_t predict_ws_bytes, void* forward_ws,
                            size_t forward_ws_bytes, void* stream);
+
+/* Token reordering ahead of the two stages.  The iCATS abstract
+ * (arxivdaily.com page): block scores estimated from tokens grouped by their
+ * query-key dot-product interaction are more accurate than from query and
+ * key tokens grouped independently by feature similarity, and that
+ * objective is a simple quadratic form; irregular cluster sizes are handled
+ * by merging tails instead of padding.  The PARO abstract (huggingface-mirror
+ * search page): reordering tokens turns the attention pattern block-wise.
+ *
+ * Readings.  Replacing a query x by a representative c moves its logit with
+ * key k by sm (x - c) . k; the mean square of that move over the N keys is
+ * sm^2 (x - c)^T M_K (x - c) with M_K = K^T K / N.  SA_METRIC_INTERACTION
+ * clusters queries under that quadratic form and keys under the one of
+ * M_Q = Q^T Q / N; SA_METRIC_FEATURE uses M = I (plain feature k-means, the
+ * baseline the abstract compares against).  Per (b, h) and side, with C
+ * clusters: centroid m starts at token floor((2m + 1) N / (2C)); `iters`
+ * Lloyd passes each give every token the cluster m minimising
+ * (x - c_m)^T M (x - c_m) (ties to the smaller m), and between passes each
+ * centroid becomes the mean of its members (a cluster without members keeps
+ * its centroid).  The order lists the tokens by (cluster, position):
+ * clusters packed back to back with no padding, so the fixed block_q /
+ * block_k blocks cut from it merge one cluster's tail with the next
+ * cluster's head.  Arithmetic: M and the member sums in fp32; the cluster
+ * decision compares c_m^T M c_m - 2 x^T M c_m in fp32 with x^T M c_m from
+ * bf16 MFMA over x (exact in bf16) and M c_m split into two bf16 parts. */
+enum { SA_METRIC_FEATURE = 0, SA_METRIC_INTERACTION = 1 };
+
+typedef struct sa_cluster_params {
+  int32_t clusters_q;  /* query clusters per head, in [1, min(N, 4096)]      */
+  int32_t clusters_k;  /* key clusters per head, in [1, min(N, 4096)]        */
+  int32_t iters;       /* Lloyd passes, in [1, 64]                           */
+  int32_t metric;      /* SA_METRIC_FEATURE | SA_METRIC_INTERACTION          */
+} sa_cluster_params;
+
+/* Outputs of sparse_attn_cluster, caller-allocated, int32 [B, H, N]:
+ *   perm_q    perm_q[b,h,r] = the query token at reordered position r
+ *   perm_k    the same for keys (and values)
+ *   labels_q  optional: the cluster of each query token, in token order
+ *   labels_k  optional: the same for keys */
+typedef struct sa_reorder {
+  int32_t* perm_q;
+  int32_t* perm_k;
+  int32_t* labels_q;
+  int32_t* labels_k;
+} sa_reorder;
+
+/* Host.  Workspace bytes of sparse_attn_cluster.  Needs dtype = SA_BF16 and
+ * causal = 0 besides the sa_params rules. */
+SA_API sa_status sparse_attn_cluster_workspace_size(const sa_params* p,
+                                                    const sa_cluster_params* cp,
+                                                    size_t* ws);
+
+/* Clusters the query and the key tokens of every head and writes the orders
+ * (and labels) to *out.  Reads q and k ([B,H,N,D] bf16, strides of *p).
+ * Deterministic: the same inputs give the same outputs bit for bit.  Causal
+ * attention is rejected (its mask is defined on the original positions); f32
+ * inputs return SA_ERR_UNSUPPORTED.  The reordered attention is: permute Q by
+ * perm_q and K, V by perm_k (sparse_attn_permute), run predict and forward on
+ * the permuted tensors, and scatter O back by perm_q (inverse = 1). */
+SA_API sa_status sparse_attn_cluster(const sa_params* p, const sa_cluster_params* cp,
+                                     const void* q, const void* k, const sa_reorder* out,
+                                     void* ws, size_t ws_bytes, void* stream);
+
+/* Row permutation of a [B,H,N,D] tensor with the strides of *p and elements
+ * of elem_bytes (2 or 4; e.g. 4 for an fp32 O).  inverse = 0 gathers,
+ * y[b,h,r] = x[b,h,perm[b,h,r]]; inverse = 1 scatters, y[b,h,perm[b,h,r]] =
+ * x[b,h,r].  perm is int32 [B,H,N] and should be a permutation of [0, N):
+ * entries outside [0, N) are skipped (their rows are not written), repeated
+ * entries leave the affected rows undefined.  x and y must not overlap. */
+SA_API sa_status sparse_attn_permute(const sa_params* p, const void* x, const int32_t* perm,
+                                     int32_t inverse, int32_t elem_bytes, void* y,
+                                     void* stream);
 
 /* Host.  Library defaults and version (either pointer may be NULL). */
 SA_API sa_status sparse_attn_info(int32_t* default_group_rows, int32_t* version);

@@ -80,8 +80,8 @@ def quad_dist(X: np.ndarray, c: np.ndarray, M: np.ndarray) -> np.ndarray:
     through the expansion x^T M x - 2 x^T M c_m + c_m^T M c_m."""
     X = np.asarray(X, dtype=np.float64)
     c = np.asarray(c, dtype=np.float64)
-    xm = np.einsum("nd,de,ne->n", X, M, X)
-    cm = np.einsum("md,de,me->m", c, M, c)
+    xm = ((X @ M) * X).sum(axis=1)
+    cm = ((c @ M) * c).sum(axis=1)
     return xm[:, None] - 2.0 * (X @ M @ c.T) + cm[None, :]
 
 

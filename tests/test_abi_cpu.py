@@ -58,7 +58,7 @@ def test_shapes_and_workspace():
     _, fw = sa.sparse_attn_workspace_size(q)
     bh = 16
     assert fw == 2 * bh * 65536 * 128 + bh * 1024 * 128 * 64 + bh * 512 * 4 + 2 * bh * 1024 * 4
-    assert sa.sparse_attn_info() == (32, 4)
+    assert sa.sparse_attn_info() == (32, 5)
     assert sa.sparse_attn_status_str(3) == "SA_ERR_WORKSPACE"
     assert sa.sparse_attn_status_str(99) == "SA_ERR_UNKNOWN"
     p = sa.make_params(2, 3, 0, 64)
@@ -162,3 +162,80 @@ def test_empty_problem_is_ok_without_pointers():
     sa.sparse_attn_forward(p, None, None, None, sa.make_mask(None, None), None, stream=0)
     assert sa.sparse_attn_last_error() == ""
     assert not math.isnan(0.0)
+
+
+def test_cluster_structs_and_workspace():
+    assert ctypes.sizeof(sa.SaClusterParams) == 16
+    assert ctypes.sizeof(sa.SaReorder) == 32
+    p = sa.make_params(1, 2, 1000, 128)
+    cp = sa.make_cluster_params(10, 20, iters=3, metric="feature")
+    z2, C, N, D, nch = 4, 20, 1000, 128, 4
+
+    def r(x):
+        return (x + 255) // 256 * 256
+    want = (r(z2 * C * D * 4) + 2 * r(z2 * C * D * 2) + r(z2 * C * 4) + 2 * r(z2 * N * 4)
+            + r(z2 * nch * C * 4) + 2 * r(z2 * C * 4))
+    assert sa.sparse_attn_cluster_workspace_size(p, cp) == want
+    ci = sa.make_cluster_params(10, 20, iters=3, metric="interaction")
+    nchm = 1   # ceil(1000 / 2048)
+    assert sa.sparse_attn_cluster_workspace_size(p, ci) == \
+        want + r(z2 * D * D * 4) + r(z2 * nchm * D * D * 4)
+    assert sa.sparse_attn_cluster_workspace_size(sa.make_params(0, 2, 1000, 128), cp) == 0
+
+
+@pytest.mark.parametrize("pkw,ckw,code", [
+    (dict(dtype="f32"), {}, sa.SA_ERR_UNSUPPORTED),
+    (dict(causal=True), {}, sa.SA_ERR_INVALID_ARG),
+    ({}, dict(clusters_q=0), sa.SA_ERR_INVALID_ARG),
+    ({}, dict(clusters_k=1001), sa.SA_ERR_INVALID_ARG),
+    ({}, dict(clusters_q=5000), sa.SA_ERR_INVALID_ARG),
+    ({}, dict(iters=0), sa.SA_ERR_INVALID_ARG),
+    ({}, dict(iters=65), sa.SA_ERR_INVALID_ARG),
+    ({}, dict(metric=7), sa.SA_ERR_INVALID_ARG),
+    (dict(D=96), {}, sa.SA_ERR_UNSUPPORTED),
+])
+def test_cluster_invalid_args_rejected_before_launch(pkw, ckw, code):
+    kw = dict(B=1, H=2, N=1000, D=128)
+    kw.update(pkw)
+    p = sa.make_params(kw.pop("B"), kw.pop("H"), kw.pop("N"), kw.pop("D"), **kw)
+    c = dict(clusters_q=8, clusters_k=16, iters=2, metric="interaction")
+    c.update(ckw)
+    cp = sa.make_cluster_params(**c)
+    fake = 1 << 20
+    with pytest.raises(sa.SparseAttnError) as e:
+        sa.sparse_attn_cluster(p, cp, fake, fake, sa.make_reorder(fake, fake), fake,
+                               ws_bytes=1 << 40, stream=0)
+    assert e.value.code == code
+
+
+def test_cluster_and_permute_pointer_errors():
+    p = sa.make_params(1, 2, 1000, 128)
+    cp = sa.make_cluster_params(8, 16)
+    fake = 1 << 20
+    cases = [
+        (dict(q=None), sa.SA_ERR_INVALID_ARG),
+        (dict(out=sa.make_reorder(None, fake)), sa.SA_ERR_INVALID_ARG),
+        (dict(ws_bytes=64), sa.SA_ERR_WORKSPACE),
+        (dict(k=fake + 4), sa.SA_ERR_INVALID_ARG),
+    ]
+    for over, code in cases:
+        a = dict(q=fake, k=fake, out=sa.make_reorder(fake, fake), ws=fake, ws_bytes=1 << 40)
+        a.update(over)
+        with pytest.raises(sa.SparseAttnError) as e:
+            sa.sparse_attn_cluster(p, cp, a["q"], a["k"], a["out"], a["ws"], stream=0,
+                                   ws_bytes=a["ws_bytes"])
+        assert e.value.code == code
+    for args, code in [((fake, fake, 0, fake, 3), sa.SA_ERR_INVALID_ARG),
+                       ((fake, fake, 2, fake, 2), sa.SA_ERR_INVALID_ARG),
+                       ((fake, None, 0, fake + 2048, 2), sa.SA_ERR_INVALID_ARG),
+                       ((fake, fake, 0, fake, 2), sa.SA_ERR_INVALID_ARG),      # x == y
+                       ((fake + 8, fake, 1, fake + 4096, 2), sa.SA_ERR_INVALID_ARG)]:
+        x, perm, inv, y, eb = args
+        with pytest.raises(sa.SparseAttnError) as e:
+            sa.sparse_attn_permute(p, x, perm, inv, y, stream=0, elem_bytes=eb)
+        assert e.value.code == code
+    # empty problems enqueue nothing
+    sa.sparse_attn_cluster(sa.make_params(1, 0, 1000, 128), cp, None, None,
+                           sa.make_reorder(None, None), None, stream=0)
+    sa.sparse_attn_permute(sa.make_params(1, 2, 0, 128), None, None, 0, None, stream=0,
+                           elem_bytes=2)
