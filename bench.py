@@ -67,6 +67,10 @@ def parse():
                     help="skip the GEMM / copy reference measurements")
     ap.add_argument("--cpu-blocks", type=int, default=256,
                     help="query blocks of head 0 in the CPU oracle sample")
+    ap.add_argument("--stage", default="all", choices=("all", "cluster"),
+                    help="cluster: time only sparse_attn_cluster (interaction metric, "
+                         "NQB / NKB clusters, 4 passes) on the workload and print its "
+                         "timing line (for per-kernel profiles)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after the run, launch a plain copy kernel (torch.neg on "
                          "fp32) of this many MiB, 3 times: a known-size reference "
@@ -425,6 +429,30 @@ def main():
     dev = torch.device("cuda:0")
     q, k, v = (torch.from_numpy(x).to(tdt).to(dev) for x in (Q, K, V))
     dense = w.dense_flops()
+
+    if args.stage == "cluster":
+        p = sa.make_params(w.B, w.H, w.N, w.D, dtype=w.dtype)
+        nqb, nkb = sa.sparse_attn_mask_shape(p)
+        cp = sa.make_cluster_params(nqb, nkb, 4, "interaction")
+        ws = torch.empty(sa.sparse_attn_cluster_workspace_size(p, cp), dtype=torch.uint8,
+                         device=dev)
+        pq, pk = (torch.empty((w.B, w.H, w.N), dtype=torch.int32, device=dev) for _ in range(2))
+        ro = sa.make_reorder(pq, pk)
+        for _ in range(args.warmup):
+            sa.sparse_attn_cluster(p, cp, q, k, ro, ws)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.steps):
+            sa.sparse_attn_cluster(p, cp, q, k, ro, ws)
+        e1.record()
+        torch.cuda.synchronize()
+        print(json.dumps({"stage": "sparse_attn_cluster", "workload": w.name,
+                          "clusters_q": nqb, "clusters_k": nkb, "iters": 4,
+                          "metric": "interaction", "steps": args.steps,
+                          "ms_per_call": round(e0.elapsed_time(e1) / max(args.steps, 1), 4)}),
+              flush=True)
+        return
 
     def measure(tau, steps, warmup, skip_rule=None, recall=None, rule=None, topk_blocks=0,
                 tensors=None):

@@ -215,23 +215,57 @@ __global__ __launch_bounds__(128) void metric_kernel(ClusterLaunch a) {
 
 // ----------------------------------------------------------------- assign
 // 256 tokens per workgroup, 64 per wavefront (two 32-token MFMA columns).
-// Cluster tiles of 32 rows of G (hi and lo) go through LDS; the Sᵀ-style
-// product D[m][x] = G_m . x comes out with lane -> token column, so each
-// lane scans 16 clusters per tile in increasing order and the two lane
-// halves merge at the end (ties to the smaller index).
+// Cluster tiles of 32 rows of G (hi and lo) go through LDS in two buffers:
+// the global loads of tile t + 1 are issued before the MFMAs of tile t and
+// land in the other buffer after them, one barrier per tile.  The product
+// D[m][x] = G_m . x comes out with lane -> token column, so each lane scans
+// 16 clusters per tile in increasing order and the two lane halves merge at
+// the end (ties to the smaller index).
 template <int D>
 __global__ __launch_bounds__(256) void assign_kernel(ClusterLaunch a) {
   constexpr int NKK = D / 16;
-  constexpr int RS = D * 2 + 16;  // LDS row stride in bytes (padded)
-  __shared__ __align__(16) char Ahi[32 * RS];
-  __shared__ __align__(16) char Alo[32 * RS];
-  __shared__ float bt[32];
+  constexpr int RS = D * 2 + 16;           // LDS row stride in bytes (padded)
+  constexpr int TILE = 2 * 32 * RS;        // hi rows, then lo rows
+  constexpr int CPT = 2 * 32 * (D / 8);    // 16-byte chunks per tile
+  constexpr int LPT = CPT / 256;           // chunks per thread
+  __shared__ __align__(16) char tiles[2][TILE];
+  __shared__ float bt[2][32];
   const int z = blockIdx.y;
   const int C = slot_clusters(a, z);
   const __bf16* X = slot_tokens(a, z, false);
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int l32 = lane & 31, hh = lane >> 5;
   const int tok0 = blockIdx.x * 256 + w * 64;
+  const uint16_t* ghi = a.ghi + (size_t)z * a.cmax * D;
+  const uint16_t* glo = a.glo + (size_t)z * a.cmax * D;
+  const float* bz = a.bvec + (size_t)z * a.cmax;
+
+  // chunk e of a tile: part (hi / lo), row r, 16-byte column ch
+  u32x4 stage[LPT];
+  float bstage = 0.f;
+  auto fetch = [&](int m0) {
+#pragma unroll
+    for (int n = 0; n < LPT; ++n) {
+      const int e = tid + 256 * n;
+      const int part = e / (32 * (D / 8)), rem = e - part * (32 * (D / 8));
+      const int r = rem / (D / 8), ch = rem - r * (D / 8);
+      const int m = m0 + r;
+      stage[n] = m < C ? *reinterpret_cast<const u32x4*>((part ? glo : ghi) + (size_t)m * D +
+                                                         ch * 8)
+                       : u32x4{0u, 0u, 0u, 0u};
+    }
+    if (tid < 32) bstage = m0 + tid < C ? bz[m0 + tid] : 0.f;
+  };
+  auto store = [&](int buf) {
+#pragma unroll
+    for (int n = 0; n < LPT; ++n) {
+      const int e = tid + 256 * n;
+      const int part = e / (32 * (D / 8)), rem = e - part * (32 * (D / 8));
+      const int r = rem / (D / 8), ch = rem - r * (D / 8);
+      *reinterpret_cast<u32x4*>(&tiles[buf][part * 32 * RS + r * RS + ch * 16]) = stage[n];
+    }
+    if (tid < 32) bt[buf][tid] = bstage;
+  };
 
   u32x4 xf[2][NKK];
 #pragma unroll
@@ -245,20 +279,16 @@ __global__ __launch_bounds__(256) void assign_kernel(ClusterLaunch a) {
   }
   float best[2] = {INFINITY, INFINITY};
   int bidx[2] = {0, 0};
-  const uint16_t* ghi = a.ghi + (size_t)z * a.cmax * D;
-  const uint16_t* glo = a.glo + (size_t)z * a.cmax * D;
-  for (int m0 = 0; m0 < C; m0 += 32) {
-    __syncthreads();
-    for (int e = tid; e < 2 * 32 * (D / 8); e += 256) {
-      const int part = e / (32 * (D / 8)), rem = e - part * (32 * (D / 8));
-      const int r = rem / (D / 8), ch = rem - r * (D / 8);
-      const int m = m0 + r;
-      const uint16_t* src = (part ? glo : ghi) + (size_t)m * D + ch * 8;
-      const u32x4 v = m < C ? *reinterpret_cast<const u32x4*>(src) : u32x4{0u, 0u, 0u, 0u};
-      *reinterpret_cast<u32x4*>((part ? Alo : Ahi) + r * RS + ch * 16) = v;
-    }
-    if (tid < 32) bt[tid] = m0 + tid < C ? a.bvec[(size_t)z * a.cmax + m0 + tid] : 0.f;
-    __syncthreads();
+
+  fetch(0);
+  store(0);
+  __syncthreads();
+  const int ntiles = (C + 31) / 32;
+  for (int t = 0; t < ntiles; ++t) {
+    const int buf = t & 1, m0 = 32 * t;
+    const bool more = t + 1 < ntiles;
+    if (more) fetch(m0 + 32);
+    const char* A = tiles[buf];
     f32x16 acc[2];
 #pragma unroll
     for (int gi = 0; gi < 2; ++gi)
@@ -266,8 +296,9 @@ __global__ __launch_bounds__(256) void assign_kernel(ClusterLaunch a) {
       for (int r = 0; r < 16; ++r) acc[gi][r] = 0.f;
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
-      const u32x4 ah = *reinterpret_cast<const u32x4*>(Ahi + l32 * RS + (16 * kk + 8 * hh) * 2);
-      const u32x4 al = *reinterpret_cast<const u32x4*>(Alo + l32 * RS + (16 * kk + 8 * hh) * 2);
+      const u32x4 ah = *reinterpret_cast<const u32x4*>(A + l32 * RS + (16 * kk + 8 * hh) * 2);
+      const u32x4 al =
+          *reinterpret_cast<const u32x4*>(A + 32 * RS + l32 * RS + (16 * kk + 8 * hh) * 2);
 #pragma unroll
       for (int gi = 0; gi < 2; ++gi) {
         acc[gi] = mfma_bf16(ah, xf[gi][kk], acc[gi]);
@@ -278,9 +309,10 @@ __global__ __launch_bounds__(256) void assign_kernel(ClusterLaunch a) {
     for (int r = 0; r < 16; ++r) {
       const int i = 8 * (r >> 2) + 4 * hh + (r & 3);
       if (m0 + i < C) {
+        const float bi = bt[buf][i];
 #pragma unroll
         for (int gi = 0; gi < 2; ++gi) {
-          const float dist = fmaf(-2.f, acc[gi][r], bt[i]);
+          const float dist = fmaf(-2.f, acc[gi][r], bi);
           if (dist < best[gi]) {
             best[gi] = dist;
             bidx[gi] = m0 + i;
@@ -288,6 +320,10 @@ __global__ __launch_bounds__(256) void assign_kernel(ClusterLaunch a) {
         }
       }
     }
+    // the other buffer was last read in iteration t - 1, before the barrier
+    // that ended it
+    if (more) store(buf ^ 1);
+    __syncthreads();
   }
 #pragma unroll
   for (int gi = 0; gi < 2; ++gi) {
