@@ -23,8 +23,9 @@
 //   moment_kernel    partial X^T X of the other side over a token range
 //                    (bf16 MFMA: exact products, fp32 sums)
 //   moment_reduce    sums the partials in a fixed order, divides by N
-//   centroid_kernel  the seeds (first pass) or the member means, summed in
-//                    the cluster-sorted order of the previous pass
+//   centroid_kernel  the seeds (first pass) or the member means, gathered
+//                    through the previous pass's order and summed in a fixed
+//                    order
 //   metric_kernel    G_m = M c_m as bf16 hi + lo parts, b_m = c_m . G_m
 //   assign_kernel    label = argmin_m (b_m - 2 x . G_m), i.e. the quadratic
 //                    form without its constant x^T M x; x . G_m by bf16 MFMA
@@ -133,35 +134,51 @@ __global__ __launch_bounds__(256) void moment_reduce(ClusterLaunch a) {
 }
 
 // -------------------------------------------------------------- centroids
-// One workgroup per (cluster, slot), thread d owns column d.  First pass: the
-// seed token.  Later passes: the mean of the members, read in the order of
-// the previous pass's sort (fixed), four interleaved partial sums.
+// One workgroup per (cluster, slot).  First pass: the seed token.  Later
+// passes: the mean of the members, gathered through the previous pass's
+// order.  Thread (g, ch) reads 16-byte chunk ch of members g, g + RG, ...
+// (RG row groups in flight), and the RG partial sums of each column are
+// added in group order: a fixed order, so the result is deterministic.
 template <int D>
 __global__ __launch_bounds__(128) void centroid_kernel(ClusterLaunch a, int seed_pass) {
-  const int z = blockIdx.y, m = blockIdx.x, d = threadIdx.x;
+  constexpr int CPR = D / 8;     // 16-byte chunks per row
+  constexpr int RG = 128 / CPR;  // rows read at a time
+  __shared__ float part[RG][D];
+  const int z = blockIdx.y, m = blockIdx.x, tid = threadIdx.x;
   const int C = slot_clusters(a, z);
-  if (m >= C || d >= D) return;
+  if (m >= C) return;
   const __bf16* X = slot_tokens(a, z, false);
   float* c = a.cent + ((size_t)z * a.cmax + m) * D;
   const int64_t sn = a.g.sn;
   if (seed_pass) {
     const int s = (int)(((2LL * m + 1) * a.g.N) / (2LL * C));
-    c[d] = (float)X[(int64_t)s * sn + d];
+    if (tid < D) c[tid] = (float)X[(int64_t)s * sn + tid];
     return;
   }
   const int n = a.cnt[(size_t)z * a.cmax + m];
   if (n == 0) return;  // no member: the centroid stays
   const int32_t* pm = a.perm + (size_t)z * a.g.N + a.seg[(size_t)z * a.cmax + m];
-  float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
-  int r = 0;
-  for (; r + 4 <= n; r += 4) {
-    s0 += (float)X[(int64_t)pm[r] * sn + d];
-    s1 += (float)X[(int64_t)pm[r + 1] * sn + d];
-    s2 += (float)X[(int64_t)pm[r + 2] * sn + d];
-    s3 += (float)X[(int64_t)pm[r + 3] * sn + d];
+  const int ch = tid % CPR, g = tid / CPR;
+  float acc[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+  for (int r = g; r < n; r += RG) {
+    const u32x4 v = *reinterpret_cast<const u32x4*>(X + (int64_t)pm[r] * sn + ch * 8);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      acc[2 * e] += bf16_lo(v[e]);
+      acc[2 * e + 1] += bf16_hi(v[e]);
+    }
   }
-  for (; r < n; ++r) s0 += (float)X[(int64_t)pm[r] * sn + d];
-  c[d] = ((s0 + s1) + (s2 + s3)) / (float)n;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) part[g][ch * 8 + e] = acc[e];
+  __syncthreads();
+  if (tid < D) {
+    float s = 0.f;
+#pragma unroll
+    for (int gg = 0; gg < RG; ++gg) s += part[gg][tid];
+    c[tid] = s / (float)n;
+  }
 }
 
 // ----------------------------------------------------------------- metric
@@ -214,15 +231,20 @@ __global__ __launch_bounds__(128) void metric_kernel(ClusterLaunch a) {
 }
 
 // ----------------------------------------------------------------- assign
-// 256 tokens per workgroup, 64 per wavefront (two 32-token MFMA columns).
+// kAssignTokens tokens per workgroup: kAssignGroups MFMA columns of 32 tokens per
+// wavefront, which share every A fragment.
 // Cluster tiles of 32 rows of G (hi and lo) go through LDS in two buffers:
 // the global loads of tile t + 1 are issued before the MFMAs of tile t and
 // land in the other buffer after them, one barrier per tile.  The product
 // D[m][x] = G_m . x comes out with lane -> token column, so each lane scans
 // 16 clusters per tile in increasing order and the two lane halves merge at
 // the end (ties to the smaller index).
+constexpr int kAssignGroups = 4;
+constexpr int kAssignTokens = 4 * 32 * kAssignGroups;
+
 template <int D>
-__global__ __launch_bounds__(256) void assign_kernel(ClusterLaunch a) {
+__global__ __launch_bounds__(256, 2) void assign_kernel(ClusterLaunch a) {
+  constexpr int NG = kAssignGroups;
   constexpr int NKK = D / 16;
   constexpr int RS = D * 2 + 16;           // LDS row stride in bytes (padded)
   constexpr int TILE = 2 * 32 * RS;        // hi rows, then lo rows
@@ -235,7 +257,7 @@ __global__ __launch_bounds__(256) void assign_kernel(ClusterLaunch a) {
   const __bf16* X = slot_tokens(a, z, false);
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int l32 = lane & 31, hh = lane >> 5;
-  const int tok0 = blockIdx.x * 256 + w * 64;
+  const int tok0 = blockIdx.x * kAssignTokens + w * 32 * NG;
   const uint16_t* ghi = a.ghi + (size_t)z * a.cmax * D;
   const uint16_t* glo = a.glo + (size_t)z * a.cmax * D;
   const float* bz = a.bvec + (size_t)z * a.cmax;
@@ -267,9 +289,9 @@ __global__ __launch_bounds__(256) void assign_kernel(ClusterLaunch a) {
     if (tid < 32) bt[buf][tid] = bstage;
   };
 
-  u32x4 xf[2][NKK];
+  u32x4 xf[NG][NKK];
 #pragma unroll
-  for (int gi = 0; gi < 2; ++gi) {
+  for (int gi = 0; gi < NG; ++gi) {
     const int row = tok0 + 32 * gi + l32;
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk)
@@ -277,8 +299,13 @@ __global__ __launch_bounds__(256) void assign_kernel(ClusterLaunch a) {
                                                                  16 * kk + 8 * hh)
                                : u32x4{0u, 0u, 0u, 0u};
   }
-  float best[2] = {INFINITY, INFINITY};
-  int bidx[2] = {0, 0};
+  float best[NG];
+  int bidx[NG];
+#pragma unroll
+  for (int gi = 0; gi < NG; ++gi) {
+    best[gi] = INFINITY;
+    bidx[gi] = 0;
+  }
 
   fetch(0);
   store(0);
@@ -289,9 +316,9 @@ __global__ __launch_bounds__(256) void assign_kernel(ClusterLaunch a) {
     const bool more = t + 1 < ntiles;
     if (more) fetch(m0 + 32);
     const char* A = tiles[buf];
-    f32x16 acc[2];
+    f32x16 acc[NG];
 #pragma unroll
-    for (int gi = 0; gi < 2; ++gi)
+    for (int gi = 0; gi < NG; ++gi)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[gi][r] = 0.f;
 #pragma unroll
@@ -300,7 +327,7 @@ __global__ __launch_bounds__(256) void assign_kernel(ClusterLaunch a) {
       const u32x4 al =
           *reinterpret_cast<const u32x4*>(A + 32 * RS + l32 * RS + (16 * kk + 8 * hh) * 2);
 #pragma unroll
-      for (int gi = 0; gi < 2; ++gi) {
+      for (int gi = 0; gi < NG; ++gi) {
         acc[gi] = mfma_bf16(ah, xf[gi][kk], acc[gi]);
         acc[gi] = mfma_bf16(al, xf[gi][kk], acc[gi]);
       }
@@ -311,7 +338,7 @@ __global__ __launch_bounds__(256) void assign_kernel(ClusterLaunch a) {
       if (m0 + i < C) {
         const float bi = bt[buf][i];
 #pragma unroll
-        for (int gi = 0; gi < 2; ++gi) {
+        for (int gi = 0; gi < NG; ++gi) {
           const float dist = fmaf(-2.f, acc[gi][r], bi);
           if (dist < best[gi]) {
             best[gi] = dist;
@@ -326,7 +353,7 @@ __global__ __launch_bounds__(256) void assign_kernel(ClusterLaunch a) {
     __syncthreads();
   }
 #pragma unroll
-  for (int gi = 0; gi < 2; ++gi) {
+  for (int gi = 0; gi < NG; ++gi) {
     const float pd = __shfl_xor(best[gi], 32, 64);
     const int pi = __shfl_xor(bidx[gi], 32, 64);
     if (pd < best[gi] || (pd == best[gi] && pi < bidx[gi])) bidx[gi] = pi;
@@ -360,6 +387,7 @@ __global__ __launch_bounds__(1024) void scan_kernel(ClusterLaunch a) {
   int32_t* H = a.hist + (size_t)z * a.nch * a.cmax;
   for (int m = tid; m < C; m += 1024) {
     int s = 0;
+#pragma unroll 16
     for (int c = 0; c < a.nch; ++c) s += H[(size_t)c * a.cmax + m];
     tot[m] = s;
     a.cnt[(size_t)z * a.cmax + m] = s;
@@ -374,14 +402,22 @@ __global__ __launch_bounds__(1024) void scan_kernel(ClusterLaunch a) {
     }
   }
   __syncthreads();
+  // counts -> bases, 16 chunks at a time: all loads of a batch are issued
+  // before its stores
+  constexpr int BATCH = 16;
   for (int m = tid; m < C; m += 1024) {
     int run = tot[m];
     a.seg[(size_t)z * a.cmax + m] = run;
-    for (int c = 0; c < a.nch; ++c) {
-      int32_t* p = H + (size_t)c * a.cmax + m;
-      const int t = *p;
-      *p = run;
-      run += t;
+    for (int c0 = 0; c0 < a.nch; c0 += BATCH) {
+      int v[BATCH];
+#pragma unroll
+      for (int u = 0; u < BATCH; ++u)
+        v[u] = c0 + u < a.nch ? H[(size_t)(c0 + u) * a.cmax + m] : 0;
+#pragma unroll
+      for (int u = 0; u < BATCH; ++u) {
+        if (c0 + u < a.nch) H[(size_t)(c0 + u) * a.cmax + m] = run;
+        run += v[u];
+      }
     }
   }
 }
@@ -438,7 +474,7 @@ hipError_t launch_cluster_t(const ClusterLaunch& a, hipStream_t s) {
     hipLaunchKernelGGL((moment_reduce<D>), dim3((D * D + 255) / 256, z2), dim3(256), 0, s, a);
   }
   const dim3 gc(a.cmax, z2), gm((a.cmax + kMetricClusters - 1) / kMetricClusters, z2);
-  const dim3 ga((a.g.N + 255) / 256, z2), gs(a.nch, z2);
+  const dim3 ga((a.g.N + kAssignTokens - 1) / kAssignTokens, z2), gs(a.nch, z2);
   for (int t = 0; t < a.iters; ++t) {
     hipLaunchKernelGGL((centroid_kernel<D>), gc, dim3(128), 0, s, a, t == 0 ? 1 : 0);
     hipLaunchKernelGGL((metric_kernel<D>), gm, dim3(128), 0, s, a);

@@ -262,3 +262,39 @@ def test_cluster_full_size():
     q, k = to_device(Q, "bf16"), to_device(K, "bf16")
     ties, _ = check_passes(Q, K, q, k, 256, 512, 4, "interaction")
     log(f"   {ties} excused near-ties over 4 passes x 2 heads x 2 sides")
+
+
+def test_cluster_strided_batch():
+    """B = 2 with Q, K stored [B, N, H, D] (caller strides): the same orders
+    as the packed layout, and every pass checked on one (b, h)."""
+    w = Workload("cluster_strided", 421, 2, 2, 1500, 128, "bf16", grid=(6, 10, 25))
+    log("[case] cluster B=2 H=2 N=1500 strided")
+    qs, ks = [], []
+    for b in range(2):
+        for h in range(2):
+            q_, k_, _ = w.head(b, h)
+            qs.append(q_)
+            ks.append(k_)
+    Q = np.stack(qs).reshape(2, 2, w.N, w.D)
+    K = np.stack(ks).reshape(2, 2, w.N, w.D)
+    q, k = to_device(Q, "bf16"), to_device(K, "bf16")
+    packed = gpu_cluster(q, k, 12, 23, 3, "interaction")
+    qt = q.permute(0, 2, 1, 3).contiguous()
+    kt = k.permute(0, 2, 1, 3).contiguous()
+    p = sa.make_params(2, 2, w.N, w.D, strides=(w.N * 2 * w.D, w.D, 2 * w.D))
+    cp = sa.make_cluster_params(12, 23, 3, "interaction")
+    ws = torch.empty(sa.sparse_attn_cluster_workspace_size(p, cp), dtype=torch.uint8,
+                     device="cuda")
+    outs = [torch.full((2, 2, w.N), -7, dtype=torch.int32, device="cuda") for _ in range(4)]
+    sa.sparse_attn_cluster(p, cp, qt, kt, sa.make_reorder(*outs), ws)
+    torch.cuda.synchronize()
+    strided = [t.cpu().numpy().astype(np.int64) for t in outs]
+    assert all(np.array_equal(a, b) for a, b in zip(packed, strided))
+    # the passes of one (b, h) = (1, 0) against the oracle
+    sub_q, sub_k = Q[1:2, 0:1], K[1:2, 0:1]
+    ties, _ = check_passes(sub_q, sub_k, to_device(sub_q, "bf16"), to_device(sub_k, "bf16"),
+                           12, 23, 3, "interaction")
+    pq, pk, lq, lk = (x[1:2, 0:1] for x in packed)
+    one = gpu_cluster(to_device(sub_q, "bf16"), to_device(sub_k, "bf16"), 12, 23, 3,
+                      "interaction")
+    assert np.array_equal(one[0], pq) and np.array_equal(one[2], lq)
