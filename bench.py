@@ -135,7 +135,9 @@ def data_description(w):
         "centroid": "Q/K around 8 centroids in runs of 64, Gaussian V",
         "gauss": "Gaussian Q/K/V",
     }[w.structure]
-    return f"synthetic, seeded ({what})"
+    from synth.workloads import BASE_SEED
+    return (f"synthetic, seeded ({what}; numpy PCG64(SeedSequence({BASE_SEED} + {w.index})), "
+            f"one child per (b, h))")
 
 
 def gen_inputs(w, threads=16):
