@@ -63,7 +63,8 @@ class SaMask(ctypes.Structure):
 
 class SaSchedule(ctypes.Structure):
     _fields_ = [("refresh_every", ctypes.c_int32), ("dense_steps", ctypes.c_int32),
-                ("step", ctypes.c_int32), ("refreshed", ctypes.c_int32)]
+                ("step", ctypes.c_int32), ("refreshed", ctypes.c_int32),
+                ("tau_by_step", ctypes.POINTER(ctypes.c_float)), ("n_tau", ctypes.c_int32)]
 
 
 class SaClusterParams(ctypes.Structure):
@@ -227,9 +228,17 @@ def sparse_attn_forward(p: SaParams, q, k, v, mask: SaMask, o, lse=None, skip_bi
                                    _ptr(ws), nb, _stream(stream)), "sparse_attn_forward")
 
 
-def make_schedule(refresh_every=1, dense_steps=0) -> SaSchedule:
-    """A mask-reuse schedule for sparse_attn_step, at step 0."""
-    return SaSchedule(int(refresh_every), int(dense_steps), 0, 0)
+def make_schedule(refresh_every=1, dense_steps=0, tau_by_step=None) -> SaSchedule:
+    """A mask-reuse schedule for sparse_attn_step, at step 0.  ``tau_by_step``
+    (a sequence of floats) gives the tau of each call's prediction; the
+    schedule keeps the host array alive."""
+    sched = SaSchedule(int(refresh_every), int(dense_steps), 0, 0, None, 0)
+    if tau_by_step is not None:
+        arr = (ctypes.c_float * len(tau_by_step))(*[float(t) for t in tau_by_step])
+        sched._tau_array = arr
+        sched.tau_by_step = ctypes.cast(arr, ctypes.POINTER(ctypes.c_float))
+        sched.n_tau = len(tau_by_step)
+    return sched
 
 
 def sparse_attn_step(p: SaParams, sched: SaSchedule, q, k, v, mask: SaMask, o, lse=None,

@@ -270,6 +270,8 @@ sa_status sparse_attn_step(const sa_params* p, sa_schedule* sched, const void* q
   if (sched->refresh_every < 1 || sched->dense_steps < 0 || sched->step < 0)
     return fail(SA_ERR_INVALID_ARG, "schedule refresh_every=%d dense_steps=%d step=%d",
                 sched->refresh_every, sched->dense_steps, sched->step);
+  if (sched->tau_by_step && sched->n_tau < 1)
+    return fail(SA_ERR_INVALID_ARG, "schedule n_tau=%d with a tau table", sched->n_tau);
   // the call's parameters: a dense step keeps every admissible block and
   // skips nothing; a sparse step predicts on its first call and every
   // refresh_every-th call after, and otherwise reuses the caller's mask
@@ -282,6 +284,10 @@ sa_status sparse_attn_step(const sa_params* p, sa_schedule* sched, const void* q
     refresh = true;
   } else {
     refresh = (sched->step - sched->dense_steps) % sched->refresh_every == 0;
+    if (sched->tau_by_step) {
+      const int e = sched->step < sched->n_tau ? sched->step : sched->n_tau - 1;
+      run.tau = sched->tau_by_step[e];  // validated with the rest of run below
+    }
   }
   sa_status st = SA_OK;
   if (refresh) st = predict_impl(&run, q, k, mask, predict_ws, predict_ws_bytes, stream, true);

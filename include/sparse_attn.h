@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define SPARSE_ATTN_VERSION 5
+#define SPARSE_ATTN_VERSION 6
 
 #if defined(__GNUC__)
 #define SA_API __attribute__((visibility("default")))
@@ -203,8 +203,12 @@ SA_API sa_status sparse_attn_forward(const sa_params* p, const void* q, const vo
  * patterns stay similar across denoising steps and can be precomputed once
  * and reused (SparseD and LiteAttention abstracts on the search page; the
  * DynSparse story: combinable with pre-computed masks), and that early steps
- * are critical (SparseD runs them dense).  Caller-owned; set step = 0 to
- * start a sequence. */
+ * are critical (SparseD runs them dense).  The iCATS abstract adds that the
+ * tolerance to sparse approximation error varies across denoising timesteps
+ * and schedules the sparsity by the signal-to-noise ratio: `tau_by_step`
+ * carries such a schedule, one tau per call, computed by the caller from its
+ * own noise schedule (the pages give no formula).  Caller-owned; set step = 0
+ * to start a sequence. */
 typedef struct sa_schedule {
   int32_t refresh_every;  /* >= 1: sparse calls predict a new mask on their   */
                           /* first call and every refresh_every-th after, and */
@@ -214,13 +218,19 @@ typedef struct sa_schedule {
                           /* rounding)                                        */
   int32_t step;           /* calls made so far; incremented on success        */
   int32_t refreshed;      /* out: 1 if this call ran stage one                */
+  const float* tau_by_step; /* host, optional: a sparse call s predicts with  */
+                          /* tau = tau_by_step[min(s, n_tau - 1)] instead of  */
+                          /* params->tau (same rules); NULL keeps params->tau */
+  int32_t n_tau;          /* entries of tau_by_step (>= 1 when it is given)   */
 } sa_schedule;
 
 /* One call of a sequence: stage one when the schedule says so (writing
  * *mask), then stage two with *mask.  Call number s = sched->step runs
  *   s <  dense_steps: predict and forward with tau = 1 and no skip;
  *   s >= dense_steps: predict iff (s - dense_steps) % refresh_every == 0,
- *                     then forward, with *p as given.
+ *                     then forward, with *p as given except tau, taken
+ *                     from tau_by_step when the schedule has one (a reused
+ *                     mask keeps the tau it was predicted with).
  * A reused mask must come from a call with the same shapes and causality
  * (every entry admissible), which the sequence guarantees when the caller
  * keeps `mask` between calls.  Every argument is validated before anything

@@ -57,7 +57,7 @@ from .quant import (  # noqa: F401
     fp8_quantize_v_blocks,
     sparse_attention_quant_head,
 )
-from .schedule import step_plan, sequence_head  # noqa: F401
+from .schedule import step_plan, sequence_head, call_tau  # noqa: F401
 from .cluster import (  # noqa: F401
     ClusterParams,
     second_moment,

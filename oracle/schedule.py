@@ -8,6 +8,13 @@ with full attention).  Reading: a sequence of calls with a schedule
 admissible block and skips nothing; later calls predict a fresh mask on
 call dense_steps and every refresh_every-th call after it, and otherwise
 reuse the last mask, evaluated on the call's own Q, K, V.
+
+iCATS abstract: the tolerance to sparse approximation error varies across
+denoising timesteps, so the sparsity follows a schedule guided by the
+signal-to-noise ratio.  Reading: an optional per-call tau table supplied by
+the caller (who owns the noise schedule; the pages give no formula); a
+predicting call s uses tau_by_step[min(s, len - 1)], a reused mask keeps
+the tau it was predicted with.
 """
 from __future__ import annotations
 
@@ -35,20 +42,30 @@ def step_plan(n_steps: int, refresh_every: int, dense_steps: int) -> List[Tuple[
     return plan
 
 
-def sequence_head(steps, p: Params, refresh_every: int, dense_steps: int, attention=None):
+def call_tau(p: Params, s: int, tau_by_step=None) -> float:
+    """The tau a predicting call s uses."""
+    if tau_by_step is None or len(tau_by_step) == 0:
+        return float(p.tau)
+    return float(tau_by_step[min(s, len(tau_by_step) - 1)])
+
+
+def sequence_head(steps, p: Params, refresh_every: int, dense_steps: int, attention=None,
+                  tau_by_step=None):
     """``steps``: list of (Q, K, V) for one head.  Returns per call
     (O, lse, kept lists used, plan entry).  ``attention`` is the stage-two
-    oracle (the unquantised one by default)."""
+    oracle (the unquantised one by default); ``tau_by_step`` the optional
+    per-call tau table."""
     attention = attention or sparse_attention_head
     dense_p = dataclasses.replace(p, tau=1.0, skip_rule="lambda", lam=-math.inf)
     out, kept = [], None
-    for (kind, src), (Q, K, V) in zip(step_plan(len(steps), refresh_every, dense_steps), steps):
+    plan = step_plan(len(steps), refresh_every, dense_steps)
+    for s, ((kind, src), (Q, K, V)) in enumerate(zip(plan, steps)):
         if kind == "dense":
             lists = predict_head(Q, K, dense_p)["kept"]
             O, lse, _ = attention(Q, K, V, lists, dense_p)
         else:
             if kind == "refresh":
-                kept = predict_head(Q, K, p)["kept"]
+                kept = predict_head(Q, K, dataclasses.replace(p, tau=call_tau(p, s, tau_by_step)))["kept"]
             lists = kept
             O, lse, _ = attention(Q, K, V, lists, p)
         out.append((O, lse, lists, (kind, src)))

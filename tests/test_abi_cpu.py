@@ -58,7 +58,7 @@ def test_shapes_and_workspace():
     _, fw = sa.sparse_attn_workspace_size(q)
     bh = 16
     assert fw == 2 * bh * 65536 * 128 + bh * 1024 * 128 * 64 + bh * 512 * 4 + 2 * bh * 1024 * 4
-    assert sa.sparse_attn_info() == (32, 5)
+    assert sa.sparse_attn_info() == (32, 6)
     assert sa.sparse_attn_status_str(3) == "SA_ERR_WORKSPACE"
     assert sa.sparse_attn_status_str(99) == "SA_ERR_UNKNOWN"
     p = sa.make_params(2, 3, 0, 64)
@@ -104,11 +104,16 @@ def test_invalid_params_rejected_before_launch(kw, code):
 
 
 def test_step_schedule_validated_before_launch():
-    assert ctypes.sizeof(sa.SaSchedule) == 16
+    assert ctypes.sizeof(sa.SaSchedule) == 32
+    assert sa.SaSchedule.tau_by_step.offset == 16 and sa.SaSchedule.n_tau.offset == 24
     p = sa.make_params(1, 2, 1000, 128, tau=0.9)
     fake = 1 << 20  # never dereferenced: validation fails first
     mask = sa.make_mask(fake, fake)
-    for sched in (sa.make_schedule(0, 0), sa.make_schedule(2, -1), sa.SaSchedule(1, 0, -3, 0)):
+    bad_table = sa.make_schedule(1, 0, tau_by_step=[0.9])
+    bad_table.n_tau = 0
+    nan_tau = sa.make_schedule(1, 0, tau_by_step=[float("nan")])
+    for sched in (sa.make_schedule(0, 0), sa.make_schedule(2, -1), sa.SaSchedule(1, 0, -3, 0),
+                  bad_table, nan_tau):
         with pytest.raises(sa.SparseAttnError) as e:
             sa.sparse_attn_step(p, sched, fake, fake, fake, mask, fake, predict_ws=fake,
                                 forward_ws=fake, predict_ws_bytes=1 << 40,

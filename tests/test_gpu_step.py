@@ -42,17 +42,20 @@ def decode(idx, cnt, bits, h):
     return kept, sk
 
 
-@pytest.mark.parametrize("w,refresh_every,dense_steps", [
+@pytest.mark.parametrize("w,refresh_every,dense_steps,taus", [
     (Workload("step_field", 301, 1, 2, 1000, 128, "bf16", grid=(10, 10, 10), tau=0.9, lam=-5.0),
-     2, 1),
+     2, 1, None),
     (Workload("step_lm_recall", 302, 1, 2, 700, 128, "bf16", structure="lm", causal=True,
-              tau=0.95, skip_rule="recall", recall=0.95), 3, 0),
+              tau=0.95, skip_rule="recall", recall=0.95), 3, 0, None),
     (Workload("step_quant", 303, 1, 1, 800, 128, "bf16", grid=(8, 10, 10), tau=0.9, lam=-5.0,
-              prec="i8fp8"), 2, 1),
-], ids=["field_k2_d1", "lm_recall_k3", "quant_k2_d1"])
-def test_step_sequence(w, refresh_every, dense_steps):
+              prec="i8fp8"), 2, 1, None),
+    (Workload("step_tau_table", 304, 1, 2, 1000, 128, "bf16", grid=(10, 10, 10), tau=0.9,
+              lam=-5.0), 1, 1, [1.0, 0.7, 0.8, 0.95]),
+], ids=["field_k2_d1", "lm_recall_k3", "quant_k2_d1", "field_tau_table"])
+def test_step_sequence(w, refresh_every, dense_steps, taus):
     n_steps = 5
-    log(f"[case] {w.name} steps={n_steps} refresh_every={refresh_every} dense={dense_steps}")
+    log(f"[case] {w.name} steps={n_steps} refresh_every={refresh_every} dense={dense_steps} "
+        f"taus={taus}")
     seqs = [w.drift_head(0, h, n_steps, dtheta=0.1) for h in range(w.H)]
     dev = torch.device("cuda:0")
     kw = dict(dtype="bf16", causal=w.causal, tau=w.tau, lam=w.lam, rule=w.rule, prec=w.prec,
@@ -69,7 +72,7 @@ def test_step_sequence(w, refresh_every, dense_steps):
     nw = (nkb + 31) // 32
     skips = torch.zeros((1, w.H, nqb, 4, nw), dtype=torch.int32, device=dev)
     o = torch.empty((1, w.H, w.N, w.D), dtype=torch.float32, device=dev)
-    sched = sa.make_schedule(refresh_every, dense_steps)
+    sched = sa.make_schedule(refresh_every, dense_steps, tau_by_step=taus)
     op = O.Params(causal=w.causal, tau=float(np.float32(w.tau)), lam=float(np.float32(w.lam)),
                   rule=w.rule, keep_prefix_kblocks=w.keep_prefix_kblocks,
                   sm_scale=float(np.float32(1.0 / math.sqrt(w.D))), skip_rule=w.skip_rule,
@@ -99,6 +102,9 @@ def test_step_sequence(w, refresh_every, dense_steps):
                     assert np.array_equal(idx_h[0, h, i, :c], prev[0][0, h, i, :c])
         prev = (idx_h, cnt_h)
         pr = dense_op if kind == "dense" else op
+        if kind == "refresh":
+            # the call's tau (the table's entry, as float32 like the library's)
+            pr = dataclasses.replace(op, tau=float(np.float32(O.call_tau(op, s, taus))))
         worst = 0.0
         for h in range(w.H):
             qh, kh, vh = Q[0, h], K[0, h], V[0, h]

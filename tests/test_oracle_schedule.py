@@ -59,3 +59,30 @@ def test_sequence_head_against_direct_calls():
     kept3 = O.predict_head(steps[3][0], steps[3][1], p)["kept"]
     assert any(not np.array_equal(a, b) for a, b in zip(kept1, kept3))
     assert out[3][3] == ("refresh", 3) and out[4][3] == ("reuse", 3)
+
+
+def test_tau_table():
+    """A per-call tau table: a predicting call s uses tau_by_step[min(s, n-1)]
+    (so a short table's last entry holds for later calls), a reused mask
+    keeps the tau it was predicted with, dense calls ignore the table, and a
+    table of the parameter's own tau changes nothing."""
+    assert O.call_tau(O.Params(tau=0.9), 3, None) == 0.9
+    assert O.call_tau(O.Params(tau=0.9), 1, [0.5, 0.7]) == 0.7
+    assert O.call_tau(O.Params(tau=0.9), 7, [0.5, 0.7]) == 0.7
+    w = Workload("seq_tau", 202, 1, 1, 256, 16, "f32", structure="gauss", tau=0.9)
+    steps = w.drift_head(0, 0, 5, dtheta=0.3)
+    p = O.Params(BQ=32, BK=16, G=8, tau=0.9, lam=-2.0)
+    table = [0.6, 0.75, 0.95]
+    out = O.sequence_head(steps, p, refresh_every=2, dense_steps=1, tau_by_step=table)
+    # plan: dense 0, refresh 1 (tau 0.75), reuse 2, refresh 3 (tau 0.95: last entry), reuse 4
+    for s, tau in ((1, 0.75), (3, 0.95)):
+        kept = O.predict_head(steps[s][0], steps[s][1], O.Params(BQ=32, BK=16, G=8, tau=tau,
+                                                                 lam=-2.0))["kept"]
+        assert all(np.array_equal(a, b) for a, b in zip(out[s][2], kept))
+        assert all(np.array_equal(a, b) for a, b in zip(out[s + 1][2], kept))
+    # the two refreshes keep different numbers of blocks (the table acts)
+    assert sum(map(len, out[1][2])) < sum(map(len, out[3][2]))
+    same = O.sequence_head(steps, p, 2, 1, tau_by_step=[0.9])
+    base = O.sequence_head(steps, p, 2, 1)
+    for a, b in zip(same, base):
+        np.testing.assert_array_equal(a[0], b[0])
