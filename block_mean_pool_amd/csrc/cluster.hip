@@ -21,7 +21,8 @@
 //
 // Kernels, per slot z = 2 (b H + h) + side (side 0 = queries, 1 = keys):
 //   moment_kernel    partial X^T X of the other side over a token range
-//                    (bf16 MFMA: exact products, fp32 sums)
+//                    (bf16 MFMA on transposing LDS reads: exact products,
+//                    fp32 sums)
 //   moment_reduce    sums the partials in a fixed order, divides by N
 //   centroid_kernel  the seeds (first pass) or the member means, gathered
 //                    through the previous pass's order and summed in a fixed
@@ -35,9 +36,7 @@
 //   export_kernel    the order and labels to the caller's [B,H,N] arrays
 //   permute_kernel   row gather (or scatter) by a permutation
 // Every reduction runs in a fixed order, so the results are deterministic.
-#include "sa_device.h"
-#include "sa_internal.h"
-#include "../../include/sparse_attn.h"
+#include "attn_common.h"
 
 namespace sa {
 namespace {
@@ -60,22 +59,43 @@ __device__ __forceinline__ f32x16 mfma_bf16(const u32x4& a, const u32x4& b, cons
 }
 
 // ---------------------------------------------------------------- moments
-constexpr int kMomentTokens = 64;  // tokens per LDS chunk
+constexpr int kMomentTokens = 64;  // tokens per LDS tile
 
 // Partial sum over tokens [c * span, (c + 1) * span) of x x^T for the other
-// side's tokens of slot z.  The chunk is stored transposed in LDS ([d][token])
-// so that both MFMA operands are 16-byte reads of 8 consecutive tokens.
+// side's tokens of slot z.  Each 64-token tile is stored row-major in LDS with
+// the V-tile chunk permutation of the forward kernel; both MFMA operands
+// (8 consecutive tokens of one d column per lane) come from gfx950's
+// transposing read ds_read_b64_tr_b16, which permutes the tokens inside one
+// MFMA identically for both, so the sum over the 16 tokens is unchanged.
 template <int D>
 __global__ __launch_bounds__(256) void moment_kernel(ClusterLaunch a, int span) {
+  using TL = attn::Tile<__bf16, D>;
+  constexpr int RB = TL::RB, CPR = TL::CPR;
   constexpr int NB = D / 32;
-  constexpr int TPW = NB * NB / 4;            // 32x32 tiles of M per wavefront
-  constexpr int LDT = kMomentTokens + 8;      // padded row, in tokens
-  __shared__ __align__(16) uint16_t T[D * LDT];
+  constexpr int TPW = NB * NB / 4;  // 32x32 tiles of M per wavefront
+  __shared__ __align__(16) char T[kMomentTokens * RB];
   const int z = blockIdx.y, c = blockIdx.x;
   const __bf16* X = slot_tokens(a, z, true);
   const int t0 = c * span, t1 = min(a.g.N, t0 + span);
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int l32 = lane & 31, hh = lane >> 5;
+  // transposing-read bases, as for the V^T operand of the forward kernel
+  const int g16 = lane >> 4, s16 = lane & 15;
+  const int tr_key = 4 * (g16 >> 1) + (s16 >> 2);
+  const int tr_d = 16 * (g16 & 1) + 4 * (s16 & 3);
+  uint32_t ro[NB];
+#pragma unroll
+  for (int bb = 0; bb < NB; ++bb) {
+    const int d = 32 * bb + tr_d;
+    ro[bb] = (uint32_t)(TL::v_off(tr_key, d >> 3) + (d & 7) * 2);
+  }
+  auto frag = [&](int kc, int bb) {
+    const attn::s16x4 lo =
+        __builtin_amdgcn_ds_read_tr16_b64_v4i16((attn::lds_s16x4*)(T + ro[bb] + 16 * kc * RB));
+    const attn::s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (attn::lds_s16x4*)(T + ro[bb] + (16 * kc + 8) * RB));
+    const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+    return u32x4{l2[0], l2[1], h2[0], h2[1]};
+  };
 
   f32x16 acc[TPW];
 #pragma unroll
@@ -86,38 +106,34 @@ __global__ __launch_bounds__(256) void moment_kernel(ClusterLaunch a, int span) 
   for (int base = t0; base < t1; base += kMomentTokens) {
     __syncthreads();
 #pragma unroll
-    for (int e = tid; e < kMomentTokens * D / 8; e += 256) {
-      const int tok = e / (D / 8), dc = e - tok * (D / 8);
+    for (int e = tid; e < kMomentTokens * CPR; e += 256) {
+      const int tok = e / CPR, ch = e - tok * CPR;
       const int row = base + tok;
-      const u32x4 v = row < t1 ? *reinterpret_cast<const u32x4*>(X + (int64_t)row * a.g.sn + dc * 8)
+      const u32x4 v = row < t1 ? *reinterpret_cast<const u32x4*>(X + (int64_t)row * a.g.sn + ch * 8)
                                : u32x4{0u, 0u, 0u, 0u};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        T[(dc * 8 + 2 * i) * LDT + tok] = (uint16_t)(v[i] & 0xffffu);
-        T[(dc * 8 + 2 * i + 1) * LDT + tok] = (uint16_t)(v[i] >> 16);
-      }
+      *reinterpret_cast<u32x4*>(T + TL::v_off(tok, ch)) = v;
     }
     __syncthreads();
 #pragma unroll
-    for (int ks = 0; ks < kMomentTokens / 16; ++ks)
+    for (int kc = 0; kc < kMomentTokens / 16; ++kc) {
+      if constexpr (TPW == 4) {  // D = 128: row block w against all four column blocks
+        const u32x4 fa = frag(kc, w);
 #pragma unroll
-      for (int tt = 0; tt < TPW; ++tt) {
-        const int ti = w * TPW + tt, rb = ti / NB, cb = ti - rb * NB;
-        const u32x4 av =
-            *reinterpret_cast<const u32x4*>(&T[(32 * rb + l32) * LDT + 16 * ks + 8 * hh]);
-        const u32x4 bv =
-            *reinterpret_cast<const u32x4*>(&T[(32 * cb + l32) * LDT + 16 * ks + 8 * hh]);
-        acc[tt] = mfma_bf16(av, bv, acc[tt]);
+        for (int cb = 0; cb < NB; ++cb) acc[cb] = mfma_bf16(fa, frag(kc, cb), acc[cb]);
+      } else {  // D = 64: one tile (w / 2, w % 2) per wavefront
+        acc[0] = mfma_bf16(frag(kc, w >> 1), frag(kc, w & 1), acc[0]);
       }
+    }
   }
   float* P = a.mpart + ((size_t)z * a.nchm + c) * D * D;
+  const int hh = lane >> 5;
 #pragma unroll
   for (int tt = 0; tt < TPW; ++tt) {
     const int ti = w * TPW + tt, rb = ti / NB, cb = ti - rb * NB;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int i = 32 * rb + 8 * (r >> 2) + 4 * hh + (r & 3);
-      P[i * D + 32 * cb + l32] = acc[tt][r];
+      P[i * D + 32 * cb + (lane & 31)] = acc[tt][r];
     }
   }
 }
