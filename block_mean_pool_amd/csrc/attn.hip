@@ -122,9 +122,10 @@ __global__ __launch_bounds__(256, (sizeof(T) == 4 && D == 128) ? 1 : 2) void att
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6;
   const int l32 = lane & 31, hh = lane >> 5;
-  const int wg = xcd_remap(blockIdx.x, a.nwg);
-  const int bh = wg / a.nqb;
-  const int i = wg - bh * a.nqb;
+  const QueryBlock qblk = query_block(a.nwg, a.nqb, CAUSAL);
+  const int wg = qblk.row;  // the query block's row in the mask arrays
+  const int bh = qblk.bh;
+  const int i = qblk.i;
   const int b = bh / a.H, h = bh - b * a.H;
   const int64_t head_off = ((int64_t)b * a.sb + (int64_t)h * a.sh) * TL::E;
   const int64_t row_bytes = a.sn * TL::E;

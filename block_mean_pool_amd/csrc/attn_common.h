@@ -31,6 +31,24 @@ __device__ __forceinline__ float xhalf_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// The query block a workgroup runs.  Consecutive ids stay on one XCD and one
+// head (xcd_remap), so the head's K and V stay in that XCD's L2.  Under
+// causality a head's query blocks run last-first: block i has 2 i + 2
+// admissible key blocks, so the heaviest start first and the light ones fill
+// the end of the grid.
+struct QueryBlock {
+  int row;  // (b H + h) nqb + i: index into the mask arrays
+  int bh;
+  int i;
+};
+__device__ __forceinline__ QueryBlock query_block(int nwg, int nqb, bool causal) {
+  const int wg = xcd_remap(blockIdx.x, nwg);
+  const int bh = wg / nqb;
+  const int j = wg - bh * nqb;
+  const int i = causal ? nqb - 1 - j : j;
+  return QueryBlock{bh * nqb + i, bh, i};
+}
+
 struct AttnArgs {
   const void* q;
   const void* k;

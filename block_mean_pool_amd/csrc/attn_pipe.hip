@@ -76,9 +76,10 @@ __global__ __launch_bounds__(256, 2) void attn_pipe_kernel(AttnArgs a) {
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hh = lane >> 5;
-  const int wg = xcd_remap(blockIdx.x, a.nwg);
-  const int bh = wg / a.nqb;
-  const int i = wg - bh * a.nqb;
+  const QueryBlock qblk = query_block(a.nwg, a.nqb, CAUSAL);
+  const int wg = qblk.row;  // the query block's row in the mask arrays
+  const int bh = qblk.bh;
+  const int i = qblk.i;
   const int b = bh / a.H, h = bh - b * a.H;
   const int64_t head_off = ((int64_t)b * a.sb + (int64_t)h * a.sh) * 2;
   const int64_t row_bytes = a.sn * 2;

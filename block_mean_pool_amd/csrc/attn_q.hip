@@ -15,7 +15,7 @@
 // the attention kernel stages V^T with plain 16-byte copies.
 // attn_q_kernel: the same tiling, online softmax and per-wavefront lambda
 // test as the bf16 kernel, with v_mfma_i32_32x32x32_i8 for S^T = K Q^T and
-// v_mfma_f32_32x32x16_fp8_fp8 for O^T += V^T P^T.
+// v_mfma_f32_32x32x64_f8f6f4 (e4m3 x e4m3) for O^T += V^T P^T.
 #include <type_traits>
 
 #include "attn_common.h"
@@ -181,9 +181,10 @@ __global__ __launch_bounds__(256, 2) void attn_q_kernel(AttnQArgs a) {
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hh = lane >> 5;
-  const int wg = xcd_remap(blockIdx.x, a.nwg);
-  const int bh = wg / a.nqb;
-  const int i = wg - bh * a.nqb;
+  const attn::QueryBlock qblk = attn::query_block(a.nwg, a.nqb, CAUSAL);
+  const int wg = qblk.row;  // the query block's row in the mask arrays
+  const int bh = qblk.bh;
+  const int i = qblk.i;
   const int b = bh / a.H, h = bh - b * a.H;
   const int wrow0 = i * 128 + 32 * w;
   const int qrow = wrow0 + l32;
