@@ -54,6 +54,7 @@ from .quant import (  # noqa: F401
     e4m3_round,
     e4m3_encode,
     int8_quantize_blocks,
+    int_quantize_blocks,
     fp8_quantize_v_blocks,
     sparse_attention_quant_head,
 )

@@ -21,6 +21,12 @@ fix no format, so the readings are:
   normal 2^-6, subnormals k * 2^-9.  Conversion rounds to nearest, ties to
   even, and saturates finite overflow to +-448.
 * Stage one (pooling, scores, mask) uses the unquantised inputs.
+* 4-bit Q.K^T (``qmax = 7``): the PARO abstract on the search page reports
+  INT4 attention once tokens are reordered.  Reading: the same per-block
+  symmetric codes with absmax / 7 as the scale and codes clamped to
+  [-7, 7]; the dot products stay exact integers.  gfx950 has no INT4 MFMA,
+  so the kernel runs these codes on the INT8 one: the mode measures the
+  accuracy of 4-bit Q.K^T, not its speed.
 """
 from __future__ import annotations
 
@@ -65,9 +71,9 @@ def e4m3_encode(x) -> np.ndarray:
     return code
 
 
-def int8_quantize_blocks(X, bs: int):
-    """Per-block symmetric INT8 codes.  Returns (codes int8 [N, d],
-    scales float32 [NB])."""
+def int_quantize_blocks(X, bs: int, qmax: int):
+    """Per-block symmetric integer codes in [-qmax, qmax] with scale
+    absmax / qmax.  Returns (codes int8 [N, d], scales float32 [NB])."""
     X = np.asarray(X, dtype=np.float32)
     N, d = X.shape
     nb = n_blocks(N, bs)
@@ -76,11 +82,17 @@ def int8_quantize_blocks(X, bs: int):
     for b in range(nb):
         blk = X[b * bs:min(N, (b + 1) * bs)]
         amax = np.float32(np.abs(blk).max())
-        s = np.float32(amax / np.float32(127.0)) if amax > 0 else np.float32(1.0)
+        s = np.float32(amax / np.float32(qmax)) if amax > 0 else np.float32(1.0)
         q = np.rint(blk / s)                      # float32 division, half-even
-        codes[b * bs:min(N, (b + 1) * bs)] = np.clip(q, -127, 127).astype(np.int8)
+        codes[b * bs:min(N, (b + 1) * bs)] = np.clip(q, -qmax, qmax).astype(np.int8)
         scales[b] = s
     return codes, scales
+
+
+def int8_quantize_blocks(X, bs: int):
+    """Per-block symmetric INT8 codes.  Returns (codes int8 [N, d],
+    scales float32 [NB])."""
+    return int_quantize_blocks(X, bs, 127)
 
 
 def fp8_quantize_v_blocks(V, bk: int):
@@ -102,18 +114,19 @@ def fp8_quantize_v_blocks(V, bk: int):
 
 def sparse_attention_quant_head(Q, K, V, kept: List[np.ndarray], p: Params,
                                 force_skip: Optional[List[np.ndarray]] = None,
-                                deltas: Optional[list] = None):
+                                deltas: Optional[list] = None, qmax: int = 127):
     """Quantised stage two: the same online softmax, processing order and
     skip rule as the unquantised oracle, with
     S = sm * s_q(i) * s_k(j) * (Qcode . Kcode)  (exact integer dot product) and
     the P.V term  s_v(j) * 2^-8 * sum_c e4m3(2^8 * P) * Vcode.
     ``deltas`` collects the group statistics and the skip rule (lambda or
-    recall) is applied as in the unquantised oracle.
+    recall) is applied as in the unquantised oracle.  ``qmax`` = 127 for
+    INT8 Q/K codes, 7 for 4-bit ones.
     Returns (O, lse, skips)."""
     N, d = np.asarray(Q).shape
     sm = p.sm(d)
-    qc, qs = int8_quantize_blocks(Q, p.BQ)
-    kc, ks = int8_quantize_blocks(K, p.BK)
+    qc, qs = int_quantize_blocks(Q, p.BQ, qmax)
+    kc, ks = int_quantize_blocks(K, p.BK, qmax)
     vq, vs = fp8_quantize_v_blocks(V, p.BK)
     qc = qc.astype(np.int64)
     kc = kc.astype(np.int64)
@@ -170,5 +183,5 @@ def sparse_attention_quant_head(Q, K, V, kept: List[np.ndarray], p: Params,
     return O, lse, skips
 
 
-__all__ = ["e4m3_round", "e4m3_encode", "int8_quantize_blocks",
+__all__ = ["e4m3_round", "e4m3_encode", "int8_quantize_blocks", "int_quantize_blocks",
            "fp8_quantize_v_blocks", "sparse_attention_quant_head", "math"]

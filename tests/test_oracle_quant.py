@@ -118,3 +118,62 @@ def test_quant_attention_matches_brute():
                                        lam, G, score=score, pv=pv)
             np.testing.assert_allclose(got, np.array(exp), atol=1e-12)
             assert [s.tolist() for s in sk] == esk
+
+
+def test_int4_codes_exact_on_scale_multiples_and_rounding():
+    """qmax = 7: codes in [-7, 7]; blocks built as code * scale with a
+    power-of-two scale round-trip exactly; halves round to even."""
+    rng = np.random.default_rng(3)
+    N, d, bs = 64, 8, 16
+    scales = np.float32(2.0) ** rng.integers(-4, 3, size=4).astype(np.float32)
+    codes = rng.integers(-7, 8, size=(N, d)).astype(np.float32)
+    for b in range(4):
+        codes[b * bs, 0] = -7.0            # block absmax exactly 7 * s
+    X = codes * np.repeat(scales, bs)[:, None]
+    c, s = O.int_quantize_blocks(X, bs, 7)
+    np.testing.assert_array_equal(s, scales)
+    np.testing.assert_array_equal(c.astype(np.float32), codes)
+    assert np.abs(c).max() == 7
+    X = np.array([[7.0, 0.5], [1.5, -2.5], [-7.0, 3.5], [0.0, -0.5]], np.float32)
+    c, s = O.int_quantize_blocks(X, 4, 7)
+    assert s[0] == 1.0
+    np.testing.assert_array_equal(c, [[7, 0], [2, -2], [-7, 4], [0, 0]])
+    # the INT8 helper is the qmax = 127 case
+    c8, s8 = O.int8_quantize_blocks(X, 4)
+    c127, s127 = O.int_quantize_blocks(X, 4, 127)
+    np.testing.assert_array_equal(c8, c127)
+    np.testing.assert_array_equal(s8, s127)
+
+
+def test_int4_quant_attention_matches_brute():
+    rng = np.random.default_rng(4)
+    N, d, BQ, BK, G = 36, 4, 8, 4, 4
+    q = rng.standard_normal((N, d)).astype(np.float32) * 2
+    k = rng.standard_normal((N, d)).astype(np.float32) * 2
+    v = rng.standard_normal((N, d)).astype(np.float32)
+    p = O.Params(BQ=BQ, BK=BK, tau=0.8, lam=-1.0, G=G)
+    pr = O.predict_head(q, k, p)
+    got, _, sk = O.sparse_attention_quant_head(q, k, v, pr["kept"], p, qmax=7)
+    qc, qs = O.int_quantize_blocks(q, BQ, 7)
+    kc, ks = O.int_quantize_blocks(k, BK, 7)
+    vq, vs = O.fp8_quantize_v_blocks(v, BK)
+    assert np.abs(qc).max() <= 7 and np.abs(kc).max() <= 7
+    sm = 1 / math.sqrt(d)
+
+    def score(r, c):
+        dot = sum(int(qc[r, e]) * int(kc[c, e]) for e in range(d))
+        return sm * float(qs[r // BQ]) * float(ks[c // BK]) * dot
+
+    def pv(r, c, pval):
+        pq = float(O.e4m3_round(np.array([pval * 256.0]))[0]) / 256.0
+        return [float(vs[c // BK]) * pq * vq[c, e] for e in range(d)]
+
+    exp, esk = brute.attention(q.tolist(), k.tolist(), v.tolist(),
+                               [list(x) for x in pr["kept"]], BQ, BK, False,
+                               -1.0, G, score=score, pv=pv)
+    np.testing.assert_allclose(got, np.array(exp), atol=1e-12)
+    assert [s.tolist() for s in sk] == esk
+    # coarser codes: farther from the unquantised result than INT8 codes
+    o8, _, _ = O.sparse_attention_quant_head(q, k, v, pr["kept"], p)
+    ref, _, _ = O.sparse_attention_head(q, k, v, pr["kept"], p)
+    assert np.abs(got - ref).mean() > np.abs(o8 - ref).mean()
