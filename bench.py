@@ -151,12 +151,12 @@ class Runner:
     """Owns the device buffers of one configuration and runs the two calls."""
 
     def __init__(self, sa, torch, w, q, k, v, tau, skip_rule="lambda", recall=1.0, rule=None,
-                 topk_blocks=0):
+                 topk_blocks=0, prec=None):
         self.sa, self.torch, self.w = sa, torch, w
         self.q, self.k, self.v = q, k, v
         self.o = torch.empty_like(q)
         self.p = sa.make_params(w.B, w.H, w.N, w.D, dtype=w.dtype, causal=w.causal, tau=tau,
-                                lam=w.lam, rule=rule or w.rule, prec=w.prec,
+                                lam=w.lam, rule=rule or w.rule, prec=prec or w.prec,
                                 topk_blocks=topk_blocks,
                                 keep_prefix_kblocks=w.keep_prefix_kblocks,
                                 skip_rule=skip_rule, recall=recall)
@@ -328,7 +328,7 @@ def reuse_sweep(sa, torch, w, oracle, n_steps=6, ks=(1, 3, 6), dtheta=0.05, thre
 
 
 def reorder_sweep(sa, torch, w, q, k, v, Q, K, V, oracle, measure_on, taus=(0.9, 0.95, 0.98),
-                  iters=4, reps=3):
+                  iters=4, reps=3, quant=None):
     """Token reordering (sparse_attn_cluster + sparse_attn_permute) ahead of
     the two stages: per metric, the time of the clustering (NQB query and NKB
     key clusters per head, ``iters`` passes) and of the four row
@@ -375,6 +375,17 @@ def reorder_sweep(sa, torch, w, q, k, v, Q, K, V, oracle, measure_on, taus=(0.9,
                              pv_skip_fraction=round(m["skip"], 5), rel_l1=round(rl, 6),
                              predict_forward_ms=round(m["ms"], 4)))
             del r
+        if quant is not None and metric == "interaction":
+            for prec in ("i8fp8", "i4fp8"):
+                r, m = measure_on(qp, kp, vp, w.tau, prec)
+                sa.sparse_attn_permute(p, r.o, pq, 1, o_back)
+                torch.cuda.synchronize()
+                rl, _ = rel_l1_sample(w, Q, K, V, o_back.float().cpu().numpy()[0], oracle)
+                quant.append(dict(order="interaction clusters", prec=prec, tau=w.tau,
+                                  sparsity=round(m["sparsity"], 5),
+                                  pv_skip_fraction=round(m["skip"], 5), rel_l1=round(rl, 6),
+                                  forward_ms=round(m["forward_ms"], 4)))
+                del r
         out.append(dict(metric=metric, clusters_q=nqb, clusters_k=nkb, iters=iters,
                         cluster_ms=round(cluster_ms, 4), permute_ms=round(permute_ms, 4),
                         by_tau=rows))
@@ -457,12 +468,12 @@ def main():
         return
 
     def measure(tau, steps, warmup, skip_rule=None, recall=None, rule=None, topk_blocks=0,
-                tensors=None):
+                tensors=None, prec=None):
         qq, kk, vv = tensors or (q, k, v)
         r = Runner(sa, torch, w, qq, kk, vv, tau,
                    skip_rule=skip_rule or args.skip_rule,
                    recall=args.recall if recall is None else recall, rule=rule,
-                   topk_blocks=topk_blocks)
+                   topk_blocks=topk_blocks, prec=prec)
         ms, pred_ms, fwd_ms, wall = r.time_steps(steps, warmup)
         cnt, skipped = r.decisions()
         adm = admissible_count(w, r.nqb, r.nkb)
@@ -541,14 +552,27 @@ def main():
             print(f"[bench] reuse {r_}", file=sys.stderr, flush=True)
 
     reorder = []
+    quant = []
     if not args.no_sweep and w.name == "wan_video":
+        # INT8 and 4-bit Q.K^T (FP8 P.V) at the headline tau, contiguous order
+        for prec in ("i8fp8", "i4fp8"):
+            rs, ms_ = measure(w.tau, max(3, args.steps // 4), 1, prec=prec)
+            rl, _ = rel_l1_sample(w, Q, K, V, rs.o.float().cpu().numpy()[0], oracle)
+            quant.append(dict(order="contiguous", prec=prec, tau=w.tau,
+                              sparsity=round(ms_["sparsity"], 5),
+                              pv_skip_fraction=round(ms_["skip"], 5), rel_l1=round(rl, 6),
+                              forward_ms=round(ms_["forward_ms"], 4)))
+            del rs
         print("[bench] token reordering", file=sys.stderr, flush=True)
         reorder = reorder_sweep(
             sa, torch, w, q, k, v, Q, K, V, oracle,
-            lambda qq, kk, vv, tau: measure(tau, max(3, args.steps // 4), 1,
-                                            tensors=(qq, kk, vv)))
+            lambda qq, kk, vv, tau, prec=None: measure(tau, max(3, args.steps // 4), 1,
+                                                       tensors=(qq, kk, vv), prec=prec),
+            quant=quant)
         for r_ in reorder:
             print(f"[bench] reorder {r_}", file=sys.stderr, flush=True)
+        for r_ in quant:
+            print(f"[bench] quantised Q.K^T {r_}", file=sys.stderr, flush=True)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -599,6 +623,7 @@ def main():
         "mask_reuse": {"sequence": "6 calls, inputs cos(0.05 s) A + sin(0.05 s) B (seeded)",
                        "by_refresh_every": reuse},
         "token_reorder": reorder,
+        "qk_precision": quant,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

@@ -42,10 +42,10 @@ sa_status check_params(const sa_params* p, sa::Geometry* g, bool* empty) {
   if (p->block_q != 128 || p->block_k != 64)
     return fail(SA_ERR_UNSUPPORTED, "block sizes %dx%d (supported: 128x64)", p->block_q, p->block_k);
   if (p->dtype != SA_F32 && p->dtype != SA_BF16) return fail(SA_ERR_INVALID_ARG, "dtype=%d", p->dtype);
-  if (p->prec != SA_PREC_NATIVE && p->prec != SA_PREC_I8_FP8)
+  if (p->prec != SA_PREC_NATIVE && p->prec != SA_PREC_I8_FP8 && p->prec != SA_PREC_I4_FP8)
     return fail(SA_ERR_INVALID_ARG, "prec=%d", p->prec);
-  if (p->prec == SA_PREC_I8_FP8 && (p->dtype != SA_BF16 || p->D != 128))
-    return fail(SA_ERR_UNSUPPORTED, "INT8/FP8 variant needs bf16 inputs and D=128");
+  if (p->prec != SA_PREC_NATIVE && (p->dtype != SA_BF16 || p->D != 128))
+    return fail(SA_ERR_UNSUPPORTED, "INT8/INT4/FP8 variants need bf16 inputs and D=128");
   if (p->rule != SA_RULE_TOPCDF && p->rule != SA_RULE_ENERGY && p->rule != SA_RULE_TOPK)
     return fail(SA_ERR_INVALID_ARG, "rule=%d", p->rule);
   if (p->rule == SA_RULE_TOPK && p->topk_blocks < 1)
@@ -106,7 +106,7 @@ struct ForwardLayout {
 };
 ForwardLayout forward_layout(const sa::Geometry& g, int prec) {
   ForwardLayout L{};
-  if (prec != SA_PREC_I8_FP8) return L;
+  if (prec == SA_PREC_NATIVE) return L;
   const size_t bh = (size_t)g.B * g.H;
   L.qc = 0;
   L.kc = L.qc + round_up(bh * g.N * g.D);
@@ -227,7 +227,8 @@ sa_status forward_impl(const sa_params* p, const void* q, const void* k, const v
   if (dry) return ok();
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e;
-  if (p->prec == SA_PREC_I8_FP8) {
+  if (p->prec != SA_PREC_NATIVE) {
+    a.qmax = p->prec == SA_PREC_I4_FP8 ? 7 : 127;
     char* w = static_cast<char*>(ws);
     a.qc = reinterpret_cast<int8_t*>(w + L.qc);
     a.kc = reinterpret_cast<int8_t*>(w + L.kc);

@@ -3,8 +3,11 @@
 // The SpargeAttn abstract calls the method sparse *and quantized*; the
 // DynSparse story notes the filter combines with quantization.  The pages fix
 // no format, so this follows the stated reading:
-//   Q, K: one scale per (b, h, block) = block absmax / 127 (1 if zero),
-//         code = rint(x / scale) clamped to [-127, 127] (fp32 division);
+//   Q, K: one scale per (b, h, block) = block absmax / qmax (1 if zero),
+//         code = rint(x / scale) clamped to [-qmax, qmax] (fp32 division);
+//         qmax = 127 (INT8), or 7 for 4-bit codes (the PARO abstract on the
+//         search page reports INT4 attention after token reordering; gfx950
+//         has no INT4 MFMA, so 4-bit codes run on the INT8 one);
 //   V:    one scale per key block = absmax / 448, code = e4m3(x / scale);
 //   P:    e4m3(2^8 p), the product rescaled by scale_v * 2^-8; the running
 //         sum l uses the unquantised p.
@@ -82,7 +85,8 @@ __global__ __launch_bounds__(256) void quant_kernel(ForwardLaunch f) {
   amax = block_max(amax, scratch);
 
   if (kind < 2) {
-    const float scale = amax > 0.f ? __fdiv_rn(amax, 127.0f) : 1.0f;
+    const float qm = (float)f.qmax;
+    const float scale = amax > 0.f ? __fdiv_rn(amax, qm) : 1.0f;
     int8_t* dst = (kind == 0 ? f.qc : f.kc) + (size_t)bh * g.N * D;
     if (tid == 0) (kind == 0 ? f.sq : f.sk)[bh * (kind == 0 ? g.nqb : g.nkb) + blk] = scale;
 #pragma unroll
@@ -95,7 +99,7 @@ __global__ __launch_bounds__(256) void quant_kernel(ForwardLaunch f) {
           const uint32_t w = buf[it][e >> 1];
           const float x = (e & 1) ? bf16_hi(w) : bf16_lo(w);
           float qv = rintf(__fdiv_rn(x, scale));
-          qv = fminf(fmaxf(qv, -127.f), 127.f);
+          qv = fminf(fmaxf(qv, -qm), qm);
           packed[e >> 2] |= ((uint32_t)(int)qv & 0xffu) << (8 * (e & 3));
         }
         *reinterpret_cast<u32x2*>(dst + (int64_t)r * D + c * 8) = u32x2{packed[0], packed[1]};

@@ -45,6 +45,7 @@ struct ForwardLaunch {
   float lambda;
   int recall_on;             // skip rule: 0 lambda, 1 recall
   float recall;              // target recall rho (recall rule)
+  int qmax;                  // quantised variant: Q/K code range [-qmax, qmax]
   // quantised variant: workspace buffers
   int8_t* qc;                // [B,H,N,D]
   int8_t* kc;                // [B,H,N,D]

@@ -11,7 +11,8 @@
  *                         group of rows when the tile cannot matter there
  *                         (the softmax-aware lambda test inside the online
  *                         softmax).  Native precision (bf16 / fp32) or the
- *                         quantised variant (INT8 Q.K^T, FP8 e4m3 P.V).
+ *                         quantised variants (INT8 or 4-bit Q.K^T, FP8 e4m3
+ *                         P.V).
  *
  * Sources: the SpargeAttn abstract (taxoreview.com page; also on the
  * huggingface-mirror search page) defines the two-stage online filter --
@@ -45,7 +46,7 @@
  * - Supported: D in {64, 128}; block_q = 128, block_k = 64; lambda group of
  *   32 rows (one wavefront's rows); N <= 262144 (4096 key blocks); one
  *   head's rows (N + 64) * stride_n elements under 2 GiB.  The
- *   quantised variant needs dtype = SA_BF16 and D = 128.  Anything else
+ *   quantised variants need dtype = SA_BF16 and D = 128.  Anything else
  *   returns SA_ERR_UNSUPPORTED.
  */
 #ifndef SPARSE_ATTN_H
@@ -58,7 +59,7 @@
 extern "C" {
 #endif
 
-#define SPARSE_ATTN_VERSION 6
+#define SPARSE_ATTN_VERSION 7
 
 #if defined(__GNUC__)
 #define SA_API __attribute__((visibility("default")))
@@ -78,8 +79,12 @@ typedef enum sa_status {
 enum { SA_F32 = 0, SA_BF16 = 1 };
 /* Arithmetic of stage two: native (bf16 MFMA / fp32 MFMA) or INT8 Q.K^T with
  * FP8 e4m3 P.V (per-block scales: Q and K absmax/127, V absmax/448 per key
- * block; P pre-scaled by 2^8). */
-enum { SA_PREC_NATIVE = 0, SA_PREC_I8_FP8 = 1 };
+ * block; P pre-scaled by 2^8).  SA_PREC_I4_FP8 is the same with 4-bit Q and
+ * K codes (scale absmax/7, codes in [-7, 7]), the INT4 attention the PARO
+ * abstract (huggingface-mirror search page) reports after token
+ * reordering; gfx950 has no INT4 MFMA, so the codes run on the INT8 MFMA and
+ * the mode changes accuracy, not speed. */
+enum { SA_PREC_NATIVE = 0, SA_PREC_I8_FP8 = 1, SA_PREC_I4_FP8 = 2 };
 /* Mask rule of stage one.  TOPCDF: P-hat = softmax of the block scores over
  * the admissible key blocks.  ENERGY: P-hat_j proportional to
  * n_j * exp(s_j), n_j the number of keys in block j (a cumulative-energy
@@ -101,7 +106,8 @@ typedef struct sa_params {
   int32_t block_q, block_k;    /* query / key block rows: 128 and 64           */
   int32_t causal;              /* 1: key c visible to row r only if c <= r     */
   int32_t dtype;               /* SA_F32 | SA_BF16                             */
-  int32_t prec;                /* SA_PREC_NATIVE | SA_PREC_I8_FP8              */
+  int32_t prec;                /* SA_PREC_NATIVE | SA_PREC_I8_FP8 |            */
+                               /* SA_PREC_I4_FP8                               */
   int32_t rule;                /* SA_RULE_TOPCDF | SA_RULE_ENERGY              */
   float tau;                   /* cumulative-mass target in (0, 1]; >= 1 keeps */
                                /* every admissible block                       */
@@ -145,7 +151,8 @@ SA_API sa_status sparse_attn_mask_shape(const sa_params* p, int64_t* nqb, int64_
  * pointer may be NULL).  Layouts (offsets rounded up to 256 bytes):
  *   predict: qbar float [B,H,NQB,D], then kbar float [B,H,NKB,D] -- the
  *            block means, left in place after the call.
- *   forward, SA_PREC_I8_FP8: Q codes int8 [B,H,N,D], K codes int8 [B,H,N,D],
+ *   forward, SA_PREC_I8_FP8 and SA_PREC_I4_FP8: Q codes int8 [B,H,N,D], K
+ *            codes int8 [B,H,N,D] (in [-7, 7] for SA_PREC_I4_FP8),
  *            V codes e4m3 [B,H,NKB,D,64] (each key block stored transposed,
  *            keys permuted: byte (d, p) of block j holds key
  *            j*64 + 32t + 8g + 4h + e for p = 32h + 16t + 4g + e, with

@@ -58,7 +58,9 @@ def test_shapes_and_workspace():
     _, fw = sa.sparse_attn_workspace_size(q)
     bh = 16
     assert fw == 2 * bh * 65536 * 128 + bh * 1024 * 128 * 64 + bh * 512 * 4 + 2 * bh * 1024 * 4
-    assert sa.sparse_attn_info() == (32, 6)
+    q4 = sa.make_params(1, 16, 65536, 128, prec="i4fp8", rule="energy")
+    assert sa.sparse_attn_workspace_size(q4)[1] == fw
+    assert sa.sparse_attn_info() == (32, 7)
     assert sa.sparse_attn_status_str(3) == "SA_ERR_WORKSPACE"
     assert sa.sparse_attn_status_str(99) == "SA_ERR_UNKNOWN"
     p = sa.make_params(2, 3, 0, 64)
@@ -75,6 +77,8 @@ def test_shapes_and_workspace():
     (dict(sm_scale=-1.0), sa.SA_ERR_INVALID_ARG),
     (dict(lambda_group_rows=16), sa.SA_ERR_UNSUPPORTED),
     (dict(prec="i8fp8", dtype="f32"), sa.SA_ERR_UNSUPPORTED),
+    (dict(prec="i4fp8", D=64), sa.SA_ERR_UNSUPPORTED),
+    (dict(prec=3), sa.SA_ERR_INVALID_ARG),
     (dict(keep_prefix_kblocks=-1), sa.SA_ERR_INVALID_ARG),
     (dict(N=300000), sa.SA_ERR_UNSUPPORTED),
     (dict(strides=(0, 0, 100)), sa.SA_ERR_INVALID_ARG),

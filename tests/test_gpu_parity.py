@@ -34,7 +34,7 @@ from synth import Workload, make_workload, round_to_bf16  # noqa: E402
 import compare  # noqa: E402
 import gpu_harness  # noqa: E402
 
-SKIP_TOL = {"bf16": 1e-3, "f32": 1e-4, "i8fp8": 1e-3}
+SKIP_TOL = {"bf16": 1e-3, "f32": 1e-4, "i8fp8": 1e-3, "i4fp8": 1e-3}
 RECALL_TOL = 1e-4  # relative slack of the recall rule (fp32 sums vs fp64)
 
 
@@ -67,7 +67,8 @@ def check_case(w: Workload, layout="bhnd", check_out=True):
                  sm_scale=float(np.float32(1.0 / math.sqrt(w.D))),
                  skip_rule=w.skip_rule, recall=float(np.float32(w.recall)),
                  topk_blocks=w.topk_blocks)
-    mode = w.prec if w.prec == "i8fp8" else w.dtype
+    mode = w.prec if w.prec in ("i8fp8", "i4fp8") else w.dtype
+    qmax = 7 if w.prec == "i4fp8" else 127
     worst = 0.0
     n_rows = n_exact = 0
     skip_n = skip_mis = n_skipped = 0
@@ -89,7 +90,11 @@ def check_case(w: Workload, layout="bhnd", check_out=True):
                 continue
             gk = r["kept"][hid]
             gs = r["skips"][hid]
-            fn = O.sparse_attention_quant_head if w.prec == "i8fp8" else O.sparse_attention_head
+            if mode in ("i8fp8", "i4fp8"):
+                def fn(*args, **kw):
+                    return O.sparse_attention_quant_head(*args, qmax=qmax, **kw)
+            else:
+                fn = O.sparse_attention_head
             if w.skip_rule == "recall":
                 # the rule's state follows the skips taken: evaluate the
                 # oracle's decisions along the GPU's own history
@@ -113,9 +118,9 @@ def check_case(w: Workload, layout="bhnd", check_out=True):
                                               round_to_bf16(r["O"][b, h]))
             fin = np.isfinite(lse_ref)
             np.testing.assert_allclose(r["lse"][b, h][fin], lse_ref[fin], atol=1e-3, rtol=0)
-            if w.prec == "i8fp8":
-                qc, qs = O.int8_quantize_blocks(q, 128)
-                kc, ks = O.int8_quantize_blocks(k, 64)
+            if mode in ("i8fp8", "i4fp8"):
+                qc, qs = O.int_quantize_blocks(q, 128, qmax)
+                kc, ks = O.int_quantize_blocks(k, 64, qmax)
                 np.testing.assert_array_equal(r["qc"][b, h], qc)
                 np.testing.assert_array_equal(r["kc"][b, h], kc)
                 np.testing.assert_array_equal(r["sq"][b, h], qs)
@@ -179,6 +184,13 @@ CASES = [
        topk_blocks=3, keep_prefix_kblocks=2, lam=-5.0),
     wl("topk_quant", 121, 1, 1, 900, 128, grid=(9, 10, 10), rule="topk", topk_blocks=6,
        prec="i8fp8", lam=-5.0),
+    # 4-bit Q / K codes on the INT8 MFMA
+    wl("quant4_energy", 122, 1, 2, 1000, 128, grid=(10, 10, 10), tau=0.95, lam=-5.0,
+       rule="energy", prec="i4fp8"),
+    wl("quant4_causal", 123, 1, 1, 700, 128, structure="lm", causal=True, tau=0.9,
+       lam=-5.0, prec="i4fp8"),
+    wl("quant4_recall", 124, 1, 2, 800, 128, grid=(8, 10, 10), tau=0.9, prec="i4fp8",
+       skip_rule="recall", recall=0.9),
 ]
 
 
@@ -216,7 +228,7 @@ def test_dense_identity_on_gpu():
 def test_positive_lambda_zeroes_output():
     w = wl("lam_pos", 111, 1, 2, 500, 128, grid=(5, 10, 10), tau=0.9, lam=0.5)
     Q, K, V = stacked(w)
-    for prec in ("native", "i8fp8"):
+    for prec in ("native", "i8fp8", "i4fp8"):
         log(f"[case] lambda > 0, {prec}")
         r = gpu_harness.run(Q, K, V, tau=0.9, lam=0.5, prec=prec)
         assert np.all(r["O"] == 0.0)
