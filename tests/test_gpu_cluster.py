@@ -146,6 +146,11 @@ def test_cluster_edge_cases():
     ties, _ = check_passes(Q2, K, q2, k, 7, 5, 3, "feature")
     pq, _, lq, _ = gpu_cluster(q2, k, 7, 5, 3, "feature")
     assert not lq.any()
+    # tiny sequences: one token, and fewer tokens than one sort chunk
+    for n, c in ((1, 1), (50, 6)):
+        qn, kn = to_device(Q[:, :, :n].copy(), "bf16"), to_device(K[:, :, :n].copy(), "bf16")
+        ties, out = check_passes(Q[:, :, :n], K[:, :, :n], qn, kn, c, c, 2, "interaction")
+        assert sorted(out[0][0, 0].tolist()) == list(range(n))
 
 
 def test_permute_roundtrip():
