@@ -7,16 +7,16 @@
 // stage two); what differs is the schedule:
 //
 //   iteration t (tile = t-th kept key block, in list order):
-//     DMA   K of tile t+2 and V of tile t, global -> LDS directly
-//           (buffer_load ... lds, no staging registers), into the stages
-//           whose previous contents iteration t-1 finished reading;
 //     scalar part of the softmax of tile t: masking (edge tiles only),
 //           row max, lambda ballot, running max (the recall rule decides
 //           after the region, once tile t's energy is summed);
 //     one region, in four chunks of 16 keys: the 4 MFMAs of P.V for tile
 //           t-1 (not issued when tile t-1 was skipped), 4 MFMAs of Q.K^T
 //           for tile t+1, and 8 exp2/FMA/add plus bf16 packing of tile t's
-//           softmax;
+//           softmax; after the first chunk, the DMA of K of tile t+2 and V
+//           of tile t, global -> LDS directly (buffer_load ... lds, no
+//           staging registers), into the stages whose previous contents
+//           iteration t-1 finished reading;
 //     wait until this wave's DMA has landed, barrier.
 //
 // LDS: two stages of K and of V (64 KiB, two workgroups per CU), each stage
@@ -212,9 +212,14 @@ __global__ __launch_bounds__(256, 2) void attn_pipe_kernel(AttnArgs a) {
       nxt = wbase + 64 + lane < cnt ? lst[wbase + 64 + lane] : 0;
     }
     const int key_far = entry_key(t + 2);
-    dma(krs, dk0, k_free, key_far);
-    dma(vrs, dv0, v_free, kq0);
     const int key_cur = kq0;
+    // the DMA of this step goes out after the region's first chunk: the first
+    // MFMAs start without waiting behind it, and it still has the rest of
+    // the region to land
+    auto issue_dma = [&]() {
+      dma(krs, dk0, k_free, key_far);
+      dma(vrs, dv0, v_free, key_cur);
+    };
 
     if (__any(ss.rescale != 1.f)) {  // m grew at t - 1
 #pragma unroll
@@ -294,12 +299,14 @@ __global__ __launch_bounds__(256, 2) void attn_pipe_kernel(AttnArgs a) {
         chunk_pv(c);
         chunk_qk(c);
         chunk_soft(c);
+        if (c == 0) issue_dma();
       }
     } else {
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         chunk_qk(c);
         chunk_soft(c);
+        if (c == 0) issue_dma();
       }
     }
     ss.l += psum;
