@@ -347,6 +347,9 @@ __global__ __launch_bounds__(256, 2) void attn_q_kernel(AttnQArgs a) {
       for (int r = 0; r < 16; ++r) x[kt][r] = (float)sc[kt][r];
     const bool need_mask =
         (key_cur + 64 > a.N) || wave_partial || (CAUSAL && key_cur + 63 > wrow0);
+    // a select per score, not a branch: this file is built with SimplifyCFG's
+    // sinking and hoisting off, which would leave `if (!ok)` as one branch per
+    // score (a third more code)
     if (need_mask) {
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
@@ -354,7 +357,7 @@ __global__ __launch_bounds__(256, 2) void attn_q_kernel(AttnQArgs a) {
         for (int r = 0; r < 16; ++r) {
           const int key = key_cur + 32 * kt + 8 * (r >> 2) + 4 * hh + (r & 3);
           const bool ok = qvalid && key < a.N && (!CAUSAL || key <= qrow);
-          if (!ok) x[kt][r] = -INFINITY;
+          x[kt][r] = ok ? x[kt][r] : -INFINITY;
         }
     }
     float xmax = -INFINITY;
