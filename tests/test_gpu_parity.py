@@ -191,6 +191,14 @@ CASES = [
        lam=-5.0, prec="i4fp8"),
     wl("quant4_recall", 124, 1, 2, 800, 128, grid=(8, 10, 10), tau=0.9, prec="i4fp8",
        skip_rule="recall", recall=0.9),
+    # the remaining kernel instantiations: bf16 causal at d = 64, fp32 non-causal at
+    # d = 128, fp32 causal at d = 64
+    wl("lm_causal_d64", 125, 2, 2, 555, 64, structure="lm", causal=True, tau=0.9,
+       lam=-4.0, keep_prefix_kblocks=1),
+    wl("fp32_field_d128", 126, 1, 2, 300, 128, dtype="f32", grid=(3, 10, 10), tau=0.9,
+       lam=-5.0),
+    wl("fp32_causal_d64", 127, 1, 2, 200, 64, dtype="f32", structure="lm", causal=True,
+       tau=0.95, lam=-3.0),
 ]
 
 
