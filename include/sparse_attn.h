@@ -108,7 +108,8 @@ typedef struct sa_params {
   int32_t dtype;               /* SA_F32 | SA_BF16                             */
   int32_t prec;                /* SA_PREC_NATIVE | SA_PREC_I8_FP8 |            */
                                /* SA_PREC_I4_FP8                               */
-  int32_t rule;                /* SA_RULE_TOPCDF | SA_RULE_ENERGY              */
+  int32_t rule;                /* SA_RULE_TOPCDF | SA_RULE_ENERGY |            */
+                               /* SA_RULE_TOPK                                 */
   float tau;                   /* cumulative-mass target in (0, 1]; >= 1 keeps */
                                /* every admissible block                       */
   float lambda;                /* skip threshold, natural-log units of the     */
