@@ -155,6 +155,8 @@ __global__ __launch_bounds__(256) void moment_reduce(ClusterLaunch a) {
 // order.  Thread (g, ch) reads 16-byte chunk ch of members g, g + RG, ...
 // (RG row groups in flight), and the RG partial sums of each column are
 // added in group order: a fixed order, so the result is deterministic.
+constexpr int kGatherRows = 4;  // member rows in flight per thread
+
 template <int D>
 __global__ __launch_bounds__(128) void centroid_kernel(ClusterLaunch a, int seed_pass) {
   constexpr int CPR = D / 8;     // 16-byte chunks per row
@@ -178,14 +180,28 @@ __global__ __launch_bounds__(128) void centroid_kernel(ClusterLaunch a, int seed
   float acc[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) acc[e] = 0.f;
-  for (int r = g; r < n; r += RG) {
-    const u32x4 v = *reinterpret_cast<const u32x4*>(X + (int64_t)pm[r] * sn + ch * 8);
+  auto add_row = [&](const u32x4& v) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       acc[2 * e] += bf16_lo(v[e]);
       acc[2 * e + 1] += bf16_hi(v[e]);
     }
+  };
+  // kGatherRows member rows per thread in flight (their indices first, then
+  // the rows), added in member order: the same sums as one row at a time
+  int r = g;
+  for (; r + (kGatherRows - 1) * RG < n; r += kGatherRows * RG) {
+    int idx[kGatherRows];
+#pragma unroll
+    for (int u = 0; u < kGatherRows; ++u) idx[u] = pm[r + u * RG];
+    u32x4 v[kGatherRows];
+#pragma unroll
+    for (int u = 0; u < kGatherRows; ++u)
+      v[u] = *reinterpret_cast<const u32x4*>(X + (int64_t)idx[u] * sn + ch * 8);
+#pragma unroll
+    for (int u = 0; u < kGatherRows; ++u) add_row(v[u]);
   }
+  for (; r < n; r += RG) add_row(*reinterpret_cast<const u32x4*>(X + (int64_t)pm[r] * sn + ch * 8));
 #pragma unroll
   for (int e = 0; e < 8; ++e) part[g][ch * 8 + e] = acc[e];
   __syncthreads();
