@@ -91,38 +91,50 @@ __global__ __launch_bounds__(kThreads) void mask_kernel(PredictLaunch a, int P2)
   }
   __syncthreads();
 
-  // 1. scores and classes (0 forced, 1 admissible, 2 inadmissible, 3 pad)
+  // 1. scores and classes (0 forced, 1 admissible, 2 inadmissible, 3 pad).
+  // Eight lanes share a key row: lane e reads the row's 16-byte chunks e,
+  // e + 8, ..., so one wavefront load covers eight rows in whole cache lines
+  // (one row per lane would touch 64 lines per load); the eight fp64 partial
+  // sums meet in a butterfly, which leaves the same sum on all eight lanes.
+  constexpr int CPL = D / 4 / 8;  // 16-byte chunks per lane
+  const int e8 = tid & 7;
   double lmax = -INFINITY;
   int n_adm = 0, n_forced = 0;
-  for (int j = tid; j < P2; j += kThreads) {
-    int cls = 3;
-    double s = -INFINITY;
-    if (j < g.nkb) {
-      const int first_key = j * 64;
-      const int last_key = min(g.N, first_key + 64) - 1;
-      const bool adm = !a.causal || first_key <= last_row;
-      if (adm) {
-        const f32x4* kr = reinterpret_cast<const f32x4*>(kb + (size_t)j * D);
-        double acc = 0.0;
-#pragma unroll 8
-        for (int c = 0; c < D / 4; ++c) {
-          const f32x4 kv = kr[c];
+  for (int j = tid >> 3; j < P2; j += kThreads / 8) {  // P2 / 32 rounds for every lane
+    const bool real = j < g.nkb;
+    const int first_key = j * 64;
+    const bool adm = real && (!a.causal || first_key <= last_row);
+    double acc = 0.0;
+    if (adm) {
+      const f32x4* kr = reinterpret_cast<const f32x4*>(kb + (size_t)j * D);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) acc = fma((double)qs[4 * c + e], (double)kv[e], acc);
-        }
+      for (int u = 0; u < CPL; ++u) {
+        const int c = e8 + 8 * u;
+        const f32x4 kv = kr[c];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) acc = fma((double)qs[4 * c + k], (double)kv[k], acc);
+      }
+    }
+    acc += __shfl_xor(acc, 1, 8);
+    acc += __shfl_xor(acc, 2, 8);
+    acc += __shfl_xor(acc, 4, 8);
+    if (e8 == 0) {
+      int cls = 3;
+      double s = -INFINITY;
+      if (adm) {
         s = (double)a.sm * acc;
-        const bool forced =
-            j < a.keep_prefix || (a.causal && last_key >= first_row);
+        const int last_key = min(g.N, first_key + 64) - 1;
+        const bool forced = j < a.keep_prefix || (a.causal && last_key >= first_row);
         cls = forced ? 0 : 1;
         lmax = fmax(lmax, s);
         ++n_adm;
         n_forced += forced;
-      } else {
+      } else if (real) {
         cls = 2;
       }
+      val[j] = s;
+      key[j] = (cls << 16) | j;
     }
-    val[j] = s;
-    key[j] = (cls << 16) | j;
   }
   if (n_adm) atomicAdd(&s_counts[0], n_adm);
   if (n_forced) atomicAdd(&s_counts[1], n_forced);
