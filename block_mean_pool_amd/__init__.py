@@ -2,8 +2,10 @@
 
 Argument marshalling only: every step of block-sparse attention runs in the
 library's HIP kernels.  PyTorch supplies device memory and the current
-stream; tensors are passed by ``data_ptr()``.  Importing this module fails
-loudly when the library has not been built (``python
+stream; tensors are passed by ``data_ptr()``, after a check that each is a
+device tensor of the expected element type whose storage covers the shape
+the parameters describe (raw integer pointers pass unchecked).  Importing
+this module fails loudly when the library has not been built (``python
 block_mean_pool_amd/build.py``) -- there is no CPU fallback.
 
 Entry points have the C names:
@@ -186,6 +188,57 @@ def _nbytes(t) -> int:
     return 0 if t is None else t.numel() * t.element_size()
 
 
+# Checks on the tensors handed to the library, made before any call: a host
+# tensor, a wrong element type or a buffer too short for the described shape
+# would otherwise reach the kernels.  Raw integer pointers are passed through
+# unchecked (the caller vouches for them).
+def _dtype_name(t) -> str:
+    return str(t.dtype).replace("torch.", "")
+
+
+def _need(t, name, dtypes=None, elems=None):
+    if t is None or isinstance(t, int):
+        return
+    if not getattr(t, "is_cuda", False):
+        raise ValueError(f"{name} must be a device tensor (got {getattr(t, 'device', type(t))})")
+    if dtypes is not None and _dtype_name(t) not in dtypes:
+        raise TypeError(f"{name} has dtype {_dtype_name(t)}, expected {' or '.join(dtypes)}")
+    if elems is not None:
+        avail = t.untyped_storage().nbytes() // t.element_size() - t.storage_offset()
+        if avail < elems:
+            raise ValueError(f"{name} holds {avail} elements from its data pointer, "
+                             f"{elems} needed")
+
+
+def _extent(p: SaParams) -> int:
+    """Elements spanned by a [B, H, N, D] tensor with the strides of ``p``."""
+    if p.B <= 0 or p.H <= 0 or p.N <= 0:
+        return 0
+    sn = p.stride_n or p.D
+    sh = p.stride_h or p.N * sn
+    sb = p.stride_b or p.H * sh
+    return (p.B - 1) * sb + (p.H - 1) * sh + (p.N - 1) * sn + p.D
+
+
+def _io_dtype(p: SaParams):
+    return ("bfloat16",) if p.dtype == SA_BF16 else ("float32",)
+
+
+def _check_qkv(p: SaParams, **tensors):
+    n = _extent(p)
+    for name, t in tensors.items():
+        _need(t, name, _io_dtype(p), n)
+
+
+def _check_outputs(p: SaParams, o, lse, skip_bits):
+    _need(o, "o", ("float32",) if p.o_fp32 else _io_dtype(p), _extent(p))
+    bhn = max(p.B, 0) * max(p.H, 0) * max(p.N, 0)
+    _need(lse, "lse", ("float32",), bhn)
+    nqb, nkb = (p.N + 127) // 128, (p.N + 63) // 64
+    _need(skip_bits, "skip_bits", ("int32", "uint32"),
+          max(p.B, 0) * max(p.H, 0) * nqb * 4 * ((nkb + 31) // 32))
+
+
 def sparse_attn_mask_shape(p: SaParams):
     nq, nk = ctypes.c_int64(), ctypes.c_int64()
     _check(lib.sparse_attn_mask_shape(ctypes.byref(p), ctypes.byref(nq), ctypes.byref(nk)),
@@ -207,6 +260,9 @@ def sparse_attn_info():
 
 
 def make_mask(kept_idx, kept_cnt, block_prob=None) -> SaMask:
+    _need(kept_idx, "kept_idx", ("int32",))
+    _need(kept_cnt, "kept_cnt", ("int32",))
+    _need(block_prob, "block_prob", ("float32",))
     return SaMask(_ptr(kept_idx), _ptr(kept_cnt), _ptr(block_prob))
 
 
@@ -214,6 +270,8 @@ def sparse_attn_predict(p: SaParams, q, k, mask: SaMask, ws, stream=None, ws_byt
     """Stage one.  ``q``, ``k``: device tensors; ``mask``: SaMask over device
     int32 buffers; ``ws``: device buffer of sparse_attn_workspace_size()[0]
     bytes."""
+    _check_qkv(p, q=q, k=k)
+    _need(ws, "ws", ("uint8", "int8"))
     nb = _nbytes(ws) if ws_bytes is None else ws_bytes
     _check(lib.sparse_attn_predict(ctypes.byref(p), _ptr(q), _ptr(k), ctypes.byref(mask),
                                    _ptr(ws), nb, _stream(stream)), "sparse_attn_predict")
@@ -222,6 +280,9 @@ def sparse_attn_predict(p: SaParams, q, k, mask: SaMask, ws, stream=None, ws_byt
 def sparse_attn_forward(p: SaParams, q, k, v, mask: SaMask, o, lse=None, skip_bits=None,
                         ws=None, stream=None, ws_bytes=None):
     """Stage two.  Writes ``o`` (and ``lse`` / ``skip_bits`` when given)."""
+    _check_qkv(p, q=q, k=k, v=v)
+    _check_outputs(p, o, lse, skip_bits)
+    _need(ws, "ws", ("uint8", "int8"))
     nb = _nbytes(ws) if ws_bytes is None else ws_bytes
     _check(lib.sparse_attn_forward(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v),
                                    ctypes.byref(mask), _ptr(o), _ptr(lse), _ptr(skip_bits),
@@ -246,6 +307,10 @@ def sparse_attn_step(p: SaParams, sched: SaSchedule, q, k, v, mask: SaMask, o, l
                      predict_ws_bytes=None, forward_ws_bytes=None):
     """One call of a sequence: stage one when ``sched`` says so, then stage
     two.  Updates ``sched`` (step, refreshed)."""
+    _check_qkv(p, q=q, k=k, v=v)
+    _check_outputs(p, o, lse, skip_bits)
+    _need(predict_ws, "predict_ws", ("uint8", "int8"))
+    _need(forward_ws, "forward_ws", ("uint8", "int8"))
     pb = _nbytes(predict_ws) if predict_ws_bytes is None else predict_ws_bytes
     fb = _nbytes(forward_ws) if forward_ws_bytes is None else forward_ws_bytes
     _check(lib.sparse_attn_step(ctypes.byref(p), ctypes.byref(sched), _ptr(q), _ptr(k), _ptr(v),
@@ -262,6 +327,9 @@ def make_cluster_params(clusters_q, clusters_k, iters=4, metric="interaction") -
 
 
 def make_reorder(perm_q, perm_k, labels_q=None, labels_k=None) -> SaReorder:
+    for name, t in (("perm_q", perm_q), ("perm_k", perm_k), ("labels_q", labels_q),
+                    ("labels_k", labels_k)):
+        _need(t, name, ("int32",))
     return SaReorder(_ptr(perm_q), _ptr(perm_k), _ptr(labels_q), _ptr(labels_k))
 
 
@@ -277,6 +345,8 @@ def sparse_attn_cluster(p: SaParams, cp: SaClusterParams, q, k, out: SaReorder, 
                         stream=None, ws_bytes=None):
     """Clusters query and key tokens; writes the orders (and labels) of
     ``out`` (SaReorder over device int32 [B, H, N] buffers)."""
+    _check_qkv(p, q=q, k=k)
+    _need(ws, "ws", ("uint8", "int8"))
     nb = _nbytes(ws) if ws_bytes is None else ws_bytes
     _check(lib.sparse_attn_cluster(ctypes.byref(p), ctypes.byref(cp), _ptr(q), _ptr(k),
                                    ctypes.byref(out), _ptr(ws), nb, _stream(stream)),
@@ -288,6 +358,14 @@ def sparse_attn_permute(p: SaParams, x, perm, inverse, y, stream=None, elem_byte
     y[perm[r]] = x[r]) of [B, H, N, D] tensors; ``elem_bytes`` defaults to
     x's element size."""
     eb = x.element_size() if elem_bytes is None else int(elem_bytes)
+    n = _extent(p)
+    for name, t in (("x", x), ("y", y)):
+        _need(t, name, None, None)
+        if t is not None and not isinstance(t, int):
+            if t.element_size() != eb:
+                raise TypeError(f"{name} has {t.element_size()}-byte elements, {eb} expected")
+            _need(t, name, None, n)
+    _need(perm, "perm", ("int32",), max(p.B, 0) * max(p.H, 0) * max(p.N, 0))
     _check(lib.sparse_attn_permute(ctypes.byref(p), _ptr(x), _ptr(perm), int(inverse), eb,
                                    _ptr(y), _stream(stream)), "sparse_attn_permute")
 
