@@ -207,6 +207,16 @@ def test_parity_small(w):
     check_case(w)
 
 
+@pytest.mark.parametrize("rule", ["topcdf", "energy"])
+def test_long_sequence_masks(rule):
+    """N > 131072: the mask kernel's largest sort (4096 keys, 51.7 KB of LDS
+    per workgroup).  Block means, P-hat and the whole head's masks against
+    the oracle."""
+    w = wl(f"long_field_{rule}", 128, 1, 1, 140000, 64, grid=(14, 100, 100), tau=0.95,
+           lam=-5.0, rule=rule)
+    check_case(w, check_out=False)
+
+
 def test_parity_strided_layout():
     w = wl("strided_bnhd", 109, 2, 3, 600, 128, grid=(6, 10, 10), tau=0.9, lam=-5.0)
     check_case(w, layout="bnhd")
