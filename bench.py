@@ -19,6 +19,7 @@ timed on a bounded sample as a baseline.
 from __future__ import annotations
 
 import argparse
+import ctypes
 import json
 import math
 import os
@@ -38,7 +39,7 @@ METRIC = "dense-equiv attention TFLOPS + sparsity at fixed rel-L1, N=32760 H=40 
 # measured on: a changed kernel reports null until it is measured again.
 MEASURED_TRAFFIC = {
     # workload -> (source hash, bytes read, bytes written)
-    "wan_video": ("bbdb3a9004adc7c3", 111_176_090_752, 387_945_024),
+    "wan_video": ("619a1419a9d45f1d", 111_213_331_584, 387_947_232),
 }
 # the forward kernel that dominates each kind of workload, and its sources
 FORWARD_KERNELS = {
@@ -49,6 +50,7 @@ FORWARD_KERNELS = {
 PEAK_BF16_TFLOPS = 2500.0
 PEAK_I8FP8_TOPS = 5000.0
 PEAK_FP32_TFLOPS = 157.3
+PEAK_CLOCK_GHZ = 2.4  # the engine clock the published peaks assume
 
 
 def parse():
@@ -82,31 +84,139 @@ def forward_kind(w):
     return "i8fp8" if w.prec == "i8fp8" else w.dtype
 
 
+def _build_module():
+    import importlib.util
+    spec = importlib.util.spec_from_file_location(
+        "sa_build", os.path.join(ROOT, "block_mean_pool_amd", "build.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return mod
+
+
 def kernel_source_hash(kind):
-    """Hash of the forward kernel's sources and of the build script (whose
-    compiler flags shape the compiled kernel)."""
+    """Hash of the forward kernel's sources and of the compiler flags the
+    build gives them (which shape the compiled kernel)."""
     import hashlib
+    b = _build_module()
     h = hashlib.sha256()
     for name in FORWARD_KERNELS[kind][1]:
         h.update(open(os.path.join(ROOT, "block_mean_pool_amd", "csrc", name), "rb").read())
-    h.update(open(os.path.join(ROOT, "block_mean_pool_amd", "build.py"), "rb").read())
+        if name.endswith(".hip"):
+            h.update(repr((b.FLAGS, b.PER_FILE_FLAGS.get(name, []))).encode())
     return h.hexdigest()[:16]
 
 
-def measured_peaks(torch, dev):
-    """What this GPU reaches on a plain bf16 GEMM (torch.matmul, 8192^3) and
-    a plain 1 GiB fp32 copy: context for the roofline fractions, which are
-    taken against the published peaks."""
+PROBE_LIB = os.path.join(ROOT, "block_mean_pool_amd", "libsa_probe.so")
+
+
+def load_probe():
+    """The benchmark's measurement helpers (clock sampler, MFMA loop), built
+    next to the attention library; None when absent."""
+    if not os.path.exists(PROBE_LIB):
+        return None
+    lib = ctypes.CDLL(PROBE_LIB)
+    lib.sa_probe_clock.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_uint64,
+                                   ctypes.c_void_p]
+    lib.sa_probe_mfma.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    return lib
+
+
+class ClockSampler:
+    """Reads the engine clock while other work runs: one wavefront on a side
+    stream (default priority) samples the engine-clock counter against the
+    constant-rate real-time counter over a bounded window."""
+
+    def __init__(self, torch, probe, dev):
+        self.torch, self.probe = torch, probe
+        self.S = probe.sa_probe_clock_max_samples()
+        self.buf = torch.zeros(2 * self.S + 1, dtype=torch.int64, device=dev)
+        self.side = torch.cuda.Stream(device=dev)
+        self.rt_hz = self._calibrate()
+
+    def _launch(self, ticks):
+        rc = self.probe.sa_probe_clock(self.buf.data_ptr(), int(ticks), max(1, int(ticks) // 64),
+                                       self.side.cuda_stream)
+        if rc:
+            raise RuntimeError(f"clock sampler launch failed (hipError {rc})")
+
+    def _samples(self):
+        b = self.buf.cpu().numpy().view(np.uint64)
+        n = int(b[2 * self.S])
+        return b[0:2 * n:2].astype(np.float64), b[1:2 * n:2].astype(np.float64)
+
+    def _calibrate(self):
+        """Real-time counter rate: the sampler alone over 5e6 ticks, timed
+        with events on its stream."""
+        torch = self.torch
+        self._launch(1000)  # first launch loads the code object: keep it out of the timing
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(self.side)
+        self._launch(5_000_000)
+        e1.record(self.side)
+        torch.cuda.synchronize()
+        _, r = self._samples()
+        return (r[-1] - r[0]) / (e0.elapsed_time(e1) * 1e-3)
+
+    def around(self, work, window_s):
+        """Engine clock (GHz) over window_s seconds of real time, sampled
+        while work() (launched right after the sampler) runs."""
+        torch = self.torch
+        torch.cuda.synchronize()
+        self._launch(window_s * self.rt_hz)
+        work()
+        torch.cuda.synchronize()
+        m, r = self._samples()
+        if len(m) < 2 or r[-1] <= r[0]:
+            return None
+        return float((m[-1] - m[0]) / (r[-1] - r[0]) * self.rt_hz / 1e9)
+
+
+def mfma_loop_peak(torch, probe, sampler, dev):
+    """Dense MFMA loop on every SIMD (four wavefronts each, eight independent
+    32x32x16 bf16 chains per wavefront): TFLOP/s and the clock it ran at."""
+    blocks, iters = 1024, 40000
+    out = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream().cuda_stream
+    for it in (2000, iters):  # warm-up, then the timed size
+        rc = probe.sa_probe_mfma(out.data_ptr(), blocks, it, stream)
+        if rc:
+            raise RuntimeError(f"MFMA loop launch failed (hipError {rc})")
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def run():
+        e0.record()
+        for _ in range(3):
+            probe.sa_probe_mfma(out.data_ptr(), blocks, iters, stream)
+        e1.record()
+
+    clock = sampler.around(run, 0.03)
+    flops = 3.0 * blocks * 4 * iters * probe.sa_probe_mfma_chains() * 2 * 32 * 32 * 16
+    return flops / (e0.elapsed_time(e1) * 1e-3) / 1e12, clock
+
+
+def measured_peaks(torch, dev, sampler=None, probe=None):
+    """What this GPU reaches on a plain bf16 GEMM (torch.matmul, 8192^3), a
+    plain 1 GiB fp32 copy and a dense MFMA loop, with the engine clock of the
+    GEMM and the loop: context for the roofline fractions, which are taken
+    against the published peaks."""
     n = 8192
     a = torch.randn(n, n, device=dev, dtype=torch.bfloat16)
     b = torch.randn(n, n, device=dev, dtype=torch.bfloat16)
     for _ in range(3):
         torch.matmul(a, b)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(10):
-        torch.matmul(a, b)
-    e1.record()
+
+    def gemms():
+        e0.record()
+        for _ in range(10):
+            torch.matmul(a, b)
+        e1.record()
+
+    gemm_clock = sampler.around(gemms, 0.005) if sampler else None
+    if sampler is None:
+        gemms()
     torch.cuda.synchronize()
     gemm = 2.0 * n ** 3 * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e12
     del a, b
@@ -120,8 +230,19 @@ def measured_peaks(torch, dev):
     torch.cuda.synchronize()
     copy = 2.0 * x.numel() * 4 * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e9
     del x, y
-    return {"bf16_gemm_8192_tflops": round(gemm, 1), "copy_1gib_gbps": round(copy, 1),
-            "published": {"bf16_dense_tflops": PEAK_BF16_TFLOPS, "hbm_gbps": 8000.0}}
+    out = {"bf16_gemm_8192_tflops": round(gemm, 1), "copy_1gib_gbps": round(copy, 1),
+           "published": {"bf16_dense_tflops": PEAK_BF16_TFLOPS, "hbm_gbps": 8000.0}}
+    if sampler is not None:
+        loop, loop_clock = mfma_loop_peak(torch, probe, sampler, dev)
+        out.update({"bf16_gemm_clock_ghz": _r3(gemm_clock),
+                    "bf16_mfma_loop_tflops": round(loop, 1),
+                    "bf16_mfma_loop_clock_ghz": _r3(loop_clock),
+                    "realtime_counter_mhz": round(sampler.rt_hz / 1e6, 3)})
+    return out
+
+
+def _r3(x):
+    return None if x is None else round(x, 3)
 
 
 def data_description(w):
@@ -579,7 +700,20 @@ def main():
         print("[bench] timing the CPU oracle sample", file=sys.stderr, flush=True)
         cpu = cpu_baseline(w, Q, K, V, w.tau, args.cpu_blocks, args.skip_rule, args.recall)
 
-    peaks = None if args.no_peaks else measured_peaks(torch, dev)
+    peaks, clock = None, None
+    if not args.no_peaks:
+        probe = load_probe()
+        sampler = ClockSampler(torch, probe, dev) if probe is not None else None
+        if sampler is not None:
+            # the engine clock while the timed configuration's forward runs
+            # (ten untimed launches; 0.1 s of them sampled)
+            ghz = sampler.around(lambda: [r.forward() for _ in range(10)], 0.1)
+            if ghz:
+                clock = {"forward_ghz": round(ghz, 3),
+                         "frac_at_clock": round(achieved / (peak * ghz / PEAK_CLOCK_GHZ), 4),
+                         "source": "s_memtime against s_memrealtime, one wavefront on a side "
+                                   "stream during ten forward launches"}
+        peaks = measured_peaks(torch, dev, sampler, probe)
 
     kind = forward_kind(w)
     traffic = None
@@ -616,6 +750,7 @@ def main():
                      "kernel": FORWARD_KERNELS[kind][0],
                      "kernel_source_hash": kernel_source_hash(kind),
                      "executed_flops_per_launch": m["exec_flops"],
+                     "clock": clock,
                      "measured_peaks": peaks},
         "tau_sweep": sweep,
         "recall_rule_sweep": recall_sweep,

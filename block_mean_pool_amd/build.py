@@ -4,8 +4,10 @@
                                           package loads the built library)
 
 Every .hip file under csrc/ is compiled with hipcc for gfx950 and linked
-into one shared library next to this file.  Packed-fp32 VALU instructions
-are disabled for all device code.
+into one shared library next to this file; the benchmark's measurement
+helpers under probe/ go into a library of their own (libsa_probe.so), so the
+attention library's ABI holds only the method.  Packed-fp32 VALU
+instructions are disabled for all device code.
 """
 from __future__ import annotations
 
@@ -18,6 +20,8 @@ import tempfile
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libsparse_attn.so")
+PROBE_DIR = os.path.join(HERE, "probe")
+PROBE_LIB = os.path.join(HERE, "libsa_probe.so")
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
@@ -43,16 +47,23 @@ PER_FILE_FLAGS = {
 }
 
 
-def sources():
-    return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
+def sources(folder=CSRC):
+    return sorted(os.path.join(folder, f) for f in os.listdir(folder) if f.endswith(".hip"))
 
 
 def build(verbose: bool = False, jobs: int = 8) -> str:
-    """Compiles every source (in parallel) and links LIB.  Returns its path."""
+    """Builds LIB and PROBE_LIB.  Returns LIB's path."""
+    _build_lib(sources(CSRC), LIB, verbose, jobs)
+    _build_lib(sources(PROBE_DIR), PROBE_LIB, verbose, jobs)
+    return LIB
+
+
+def _build_lib(srcs, lib, verbose, jobs):
+    """Compiles srcs (in parallel) and links them into lib."""
     objdir = tempfile.mkdtemp(prefix="sa_build_")
     try:
         procs, objs = [], []
-        for src in sources():
+        for src in srcs:
             obj = os.path.join(objdir, os.path.basename(src) + ".o")
             cmd = [HIPCC, *FLAGS, *PER_FILE_FLAGS.get(os.path.basename(src), []), "-c", src,
                    "-o", obj]
@@ -65,17 +76,16 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
                 _wait(procs.pop(0))
         for p in procs:
             _wait(p)
-        tmp = LIB + ".tmp"
+        tmp = lib + ".tmp"
         cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
         if verbose:
             print(" ".join(cmd), flush=True)
         out = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
         if out.returncode:
             raise RuntimeError("link failed:\n" + out.stdout)
-        os.replace(tmp, LIB)
+        os.replace(tmp, lib)
     finally:
         shutil.rmtree(objdir, ignore_errors=True)
-    return LIB
 
 
 def _wait(item):

@@ -25,6 +25,20 @@ def test_exports_every_declared_function():
         assert hasattr(sa.lib, n), n
 
 
+def test_probe_library_exports():
+    """The benchmark's measurement helpers build into their own library,
+    outside the attention library's ABI."""
+    import os
+    path = os.path.join(os.path.dirname(sa.LIB_PATH), "libsa_probe.so")
+    probe = ctypes.CDLL(path)
+    for n in ("sa_probe_clock", "sa_probe_clock_max_samples", "sa_probe_mfma",
+              "sa_probe_mfma_chains"):
+        assert hasattr(probe, n), n
+    assert probe.sa_probe_clock_max_samples() == 256
+    assert not any(n.startswith("sa_probe") for n in declared_functions())
+    assert not hasattr(sa.lib, "sa_probe_clock")
+
+
 def test_binding_exposes_the_same_names():
     for n in declared_functions():
         assert callable(getattr(sa, n)), n
