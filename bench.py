@@ -702,18 +702,28 @@ def main():
 
     peaks, clock = None, None
     if not args.no_peaks:
-        probe = load_probe()
-        sampler = ClockSampler(torch, probe, dev) if probe is not None else None
-        if sampler is not None:
-            # the engine clock while the timed configuration's forward runs
-            # (ten untimed launches; 0.1 s of them sampled)
-            ghz = sampler.around(lambda: [r.forward() for _ in range(10)], 0.1)
-            if ghz:
-                clock = {"forward_ghz": round(ghz, 3),
-                         "frac_at_clock": round(achieved / (peak * ghz / PEAK_CLOCK_GHZ), 4),
-                         "source": "s_memtime against s_memrealtime, one wavefront on a side "
-                                   "stream during ten forward launches"}
-        peaks = measured_peaks(torch, dev, sampler, probe)
+        # context only: a failure here leaves these fields null, not the line
+        sampler = probe = None
+        try:
+            probe = load_probe()
+            sampler = ClockSampler(torch, probe, dev) if probe is not None else None
+            if sampler is not None:
+                # the engine clock while the timed configuration's forward
+                # runs (ten untimed launches; 0.1 s of them sampled)
+                ghz = sampler.around(lambda: [r.forward() for _ in range(10)], 0.1)
+                if ghz:
+                    clock = {"forward_ghz": round(ghz, 3),
+                             "frac_at_clock": round(achieved / (peak * ghz / PEAK_CLOCK_GHZ),
+                                                    4),
+                             "source": "s_memtime against s_memrealtime, one wavefront on a "
+                                       "side stream during ten forward launches"}
+        except Exception as e:  # noqa: BLE001
+            print(f"[bench] clock reading skipped: {e}", file=sys.stderr, flush=True)
+            sampler = None
+        try:
+            peaks = measured_peaks(torch, dev, sampler, probe)
+        except Exception as e:  # noqa: BLE001
+            print(f"[bench] reference peaks skipped: {e}", file=sys.stderr, flush=True)
 
     kind = forward_kind(w)
     traffic = None
