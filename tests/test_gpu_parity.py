@@ -207,6 +207,45 @@ def test_parity_small(w):
     check_case(w)
 
 
+def random_cases(n=16, seed=20261203):
+    """Seeded random combinations of the parameters the hand-picked cases fix
+    one at a time: head dimension, causality, input type, Q.K^T precision,
+    mask rule, skip rule, ragged N, batch and heads, tau, lambda and the
+    forced prefix."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for c in range(n):
+        quant = c % 4 == 3  # every fourth case runs the quantised forward
+        D = 128 if quant else int(rng.choice([64, 128]))
+        dtype = "bf16" if quant else str(rng.choice(["bf16", "bf16", "bf16", "f32"]))
+        prec = str(rng.choice(["i8fp8", "i4fp8"])) if quant else "native"
+        causal = bool(rng.random() < 0.4)
+        rule = str(rng.choice(["topcdf", "energy", "topk"]))
+        skip_rule = str(rng.choice(["lambda", "lambda", "recall"]))
+        N = int(rng.integers(130, 1100))
+        B, H = int(rng.integers(1, 3)), int(rng.integers(1, 3))
+        kw = dict(tau=float(rng.choice([0.8, 0.9, 0.95, 1.0])),
+                  lam=float(rng.choice([-8.0, -5.0, -2.0, 0.0])),
+                  keep_prefix_kblocks=int(rng.integers(0, 3)), rule=rule, prec=prec,
+                  skip_rule=skip_rule, recall=float(rng.choice([0.8, 0.9, 0.99])),
+                  topk_blocks=int(rng.integers(1, 8)) if rule == "topk" else 0)
+        if causal:
+            w = wl(f"random_{c}", 200 + c, B, H, N, D, dtype=dtype, structure="lm",
+                   causal=True, **kw)
+        else:
+            w = wl(f"random_{c}", 200 + c, B, H, N, D, dtype=dtype, grid=(N, 1, 1), **kw)
+        out.append(w)
+    return out
+
+
+RANDOM_CASES = random_cases()
+
+
+@pytest.mark.parametrize("w", RANDOM_CASES, ids=[c.name for c in RANDOM_CASES])
+def test_parity_random(w):
+    check_case(w)
+
+
 @pytest.mark.parametrize("rule", ["topcdf", "energy"])
 def test_long_sequence_masks(rule):
     """N > 131072: the mask kernel's largest sort (4096 keys, 51.7 KB of LDS
