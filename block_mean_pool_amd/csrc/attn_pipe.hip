@@ -9,14 +9,16 @@
 //   iteration t (tile = t-th kept key block, in list order):
 //     scalar part of the softmax of tile t: masking (edge tiles only),
 //           row max, lambda ballot, running max (the recall rule decides
-//           after the region, once tile t's energy is summed);
+//           after the region, once tile t's energy is summed).  The VOTE
+//           variant runs it at the end of iteration t - 1 instead, as soon
+//           as tile t's Q.K^T is complete, and votes on tile t's V transfer;
 //     one region, in four chunks of 16 keys: the 4 MFMAs of P.V for tile
 //           t-1 (not issued when tile t-1 was skipped), 4 MFMAs of Q.K^T
 //           for tile t+1, and 8 exp2/FMA/add plus bf16 packing of tile t's
 //           softmax; after the first chunk, the DMA of K of tile t+2 and V
-//           of tile t, global -> LDS directly (buffer_load ... lds, no
-//           staging registers), into the stages whose previous contents
-//           iteration t-1 finished reading;
+//           of tile t (unless no wavefront multiplies tile t), global -> LDS
+//           directly (buffer_load ... lds, no staging registers), into the
+//           stages whose previous contents iteration t-1 finished reading;
 //     wait until this wave's DMA has landed, barrier.
 //
 // LDS: two stages of K and of V (64 KiB, two workgroups per CU), each stage
@@ -30,6 +32,7 @@
 // rounding, which alone can move O by 1e-2).  l is rescaled at once when m
 // grows; acc one step later, before the P.V of the tile that set the new m
 // (in score order m grows on about 2 % of a wavefront's tiles).
+#include <algorithm>
 #include <type_traits>
 
 #include "attn_common.h"
@@ -44,15 +47,17 @@ typedef __attribute__((address_space(3))) void lds_void;
 struct Soft {
   float m;        // running max (log2 units), the exponent offset
   float l;        // this lane's share of sum exp2(c S - m)
-  float rescale;  // pending factor for acc
+  float resc_a;   // acc factor applied at the start of the next step
+  float resc_b;   // acc factor of the latest scalar part, one step later
   float drop;     // recall rule: energy the row has dropped, same offset as l
 };
 
 template <int I>
 using Int = std::integral_constant<int, I>;
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool VOTE>
 __global__ __launch_bounds__(256, 2) void attn_pipe_kernel(AttnArgs a) {
+  static_assert(!(CAUSAL && VOTE), "the V vote is a non-causal schedule");
   using TL = Tile<__bf16, D>;
   constexpr int RB = TL::RB, TB = TL::TBYTES;
   constexpr int NI = TB / 4096;  // DMA wave-instructions per tile per wave
@@ -63,6 +68,9 @@ __global__ __launch_bounds__(256, 2) void attn_pipe_kernel(AttnArgs a) {
   __shared__ __align__(16) char k1[TB];
   __shared__ __align__(16) char v0[TB];
   __shared__ __align__(16) char v1[TB];
+  // per tile parity and wavefront: 1 if the wavefront multiplies the tile's
+  // P.V (lambda rule, VOTE kernels); a tile no wavefront needs gets no V
+  __shared__ __align__(16) uint32_t vote[2][4];
   auto kst = [&](auto s) -> char* {
     if constexpr (decltype(s)::value % 2 == 0) return k0;
     else return k1;
@@ -180,8 +188,57 @@ __global__ __launch_bounds__(256, 2) void attn_pipe_kernel(AttnArgs a) {
   u32x4 pf[4];  // P of the previous tile, bf16, as the P.V B operand
 #pragma unroll
   for (int c = 0; c < 4; ++c) pf[c] = u32x4{0u, 0u, 0u, 0u};
-  Soft ss{-INFINITY, 0.f, 1.f, 0.f};
+  Soft ss{-INFINITY, 0.f, 1.f, 1.f, 0.f};
   bool pv_prev = false;
+  // VOTE kernels (non-causal, chosen by the host when K and V stream from
+  // HBM) vote on each tile's V transfer: the lambda decision is known once
+  // the tile's Q.K^T is complete, so the scalar part runs at the end of the
+  // previous step and the vote is in LDS by the barrier before the tile's
+  // step; a tile no wavefront multiplies is not fetched (a third of them at
+  // tau = 0.9 on the video workloads).  The recall rule decides after the
+  // tile's energy is summed, so it always fetches V.  The other kernels run
+  // the scalar part at the start of the step.
+  const bool vote_on = VOTE && !a.lam_off && !a.recall_on;
+
+  // softmax, scalar part of the tile whose scores are s (first key key0):
+  // masking, row max, lambda ballot, running max; the acc factor for a
+  // raised m goes to resc_b and reaches acc at the start of the step whose
+  // region multiplies this tile's P.V
+  auto scalar_part = [&](f32x16(&s)[2], int key0, int u) -> bool {
+    const bool need_mask = (key0 + 64 > a.N) || wave_partial || (CAUSAL && key0 + 63 > wrow0);
+    // a select per score, not a branch: this file is built with SimplifyCFG's
+    // sinking and hoisting off, which would leave `if (!ok)` as one branch per
+    // score (a third more code; 4 % slower on the video workload)
+    if (need_mask) {
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = key0 + 32 * kt + 8 * (r >> 2) + 4 * hh + (r & 3);
+          const bool ok = qvalid && key < a.N && (!CAUSAL || key <= qrow);
+          s[kt][r] = ok ? s[kt][r] : -INFINITY;
+        }
+    }
+    float mloc = -INFINITY;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mloc = fmaxf(mloc, s[kt][r]);
+    mloc = xhalf_max(mloc) * a.c2;
+    const float mnew = fmaxf(ss.m, mloc);
+    bool do_pv = true;
+    if (!a.lam_off) do_pv = __any((mloc != -INFINITY) && (mloc - mnew >= a.lam2));
+    if (__any(mnew != ss.m)) {
+      // 0 when m was -inf (nothing accumulated yet), 1 where m did not move
+      const float f = (mnew == ss.m) ? 1.f : __builtin_amdgcn_exp2f(ss.m - mnew);
+      ss.l *= f;
+      ss.drop *= f;
+      ss.resc_b *= f;
+      ss.m = mnew;
+    }
+    if (vote_on && lane == 0) vote[u & 1][w] = do_pv ? 1u : 0u;
+    return do_pv;
+  };
 
   int kq0 = entry_key(0), kq1 = entry_key(1);  // keys of entries t, t + 1
 
@@ -196,7 +253,9 @@ __global__ __launch_bounds__(256, 2) void attn_pipe_kernel(AttnArgs a) {
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) sA[kt] = qk_mfma(kst(Int<0>{}), kt, kk, sA[kt]);
   }
-  __syncthreads();  // stage 0 of K is refilled in iteration 0
+  bool dpv_next = true;  // the lambda decision of the next tile (VOTE kernels)
+  if (VOTE && cnt > 0) dpv_next = scalar_part(sA, kq0, 0);
+  __syncthreads();  // stage 0 of K is refilled in iteration 0; entry 0's vote
 
   // one pipeline step for entry t with phase PH = t % 2
   auto step = [&](auto ph, int t, f32x16(&sc)[2], f32x16(&sn)[2]) {
@@ -213,55 +272,30 @@ __global__ __launch_bounds__(256, 2) void attn_pipe_kernel(AttnArgs a) {
     }
     const int key_far = entry_key(t + 2);
     const int key_cur = kq0;
+    bool need_v = true;
+    if (vote_on) {
+      const u32x4 vv = *reinterpret_cast<const u32x4*>(vote[t & 1]);
+      need_v = __builtin_amdgcn_readfirstlane((vv[0] | vv[1] | vv[2] | vv[3]) != 0u);
+    }
     // the DMA of this step goes out after the region's first chunk: the first
     // MFMAs start without waiting behind it, and it still has the rest of
     // the region to land
     auto issue_dma = [&]() {
       dma(krs, dk0, k_free, key_far);
-      dma(vrs, dv0, v_free, key_cur);
+      if (need_v) dma(vrs, dv0, v_free, key_cur);
     };
 
-    if (__any(ss.rescale != 1.f)) {  // m grew at t - 1
+    bool do_pv = dpv_next;  // the lambda decision of tile t
+    if constexpr (!VOTE) do_pv = scalar_part(sc, key_cur, t);
+    if (__any(ss.resc_a != 1.f)) {  // m grew at t - 1
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc[dt][r] *= ss.rescale;
-      ss.rescale = 1.f;
+        for (int r = 0; r < 16; ++r) acc[dt][r] *= ss.resc_a;
     }
+    ss.resc_a = ss.resc_b;
+    ss.resc_b = 1.f;
 
-    // softmax, scalar part: masking, row max, lambda ballot, running max
-    const bool need_mask =
-        (key_cur + 64 > a.N) || wave_partial || (CAUSAL && key_cur + 63 > wrow0);
-    // a select per score, not a branch: this file is built with SimplifyCFG's
-    // sinking and hoisting off, which would leave `if (!ok)` as one branch per
-    // score (a third more code; 4 % slower on the video workload)
-    if (need_mask) {
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = key_cur + 32 * kt + 8 * (r >> 2) + 4 * hh + (r & 3);
-          const bool ok = qvalid && key < a.N && (!CAUSAL || key <= qrow);
-          sc[kt][r] = ok ? sc[kt][r] : -INFINITY;
-        }
-    }
-    float mloc = -INFINITY;
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mloc = fmaxf(mloc, sc[kt][r]);
-    mloc = xhalf_max(mloc) * a.c2;
-    const float mnew = fmaxf(ss.m, mloc);
-    bool do_pv = true;
-    if (!a.lam_off) do_pv = __any((mloc != -INFINITY) && (mloc - mnew >= a.lam2));
-    if (__any(mnew != ss.m)) {
-      // 0 when m was -inf (nothing accumulated yet), 1 where m did not move
-      const float f = (mnew == ss.m) ? 1.f : __builtin_amdgcn_exp2f(ss.m - mnew);
-      ss.l *= f;
-      ss.drop *= f;
-      ss.rescale *= f;
-      ss.m = mnew;
-    }
     const float negm = (ss.m == -INFINITY) ? 0.f : -ss.m;
     const float c2 = a.c2;
 
@@ -331,7 +365,8 @@ __global__ __launch_bounds__(256, 2) void attn_pipe_kernel(AttnArgs a) {
     pv_prev = do_pv;
     kq0 = kq1;
     kq1 = key_far;
-    // the DMA issued above is what iteration t + 1 reads
+    if (VOTE && t + 1 < cnt) dpv_next = scalar_part(sn, kq0, t + 1);
+    // the DMA issued above is what iteration t + 1 reads; the vote on its V
     __syncthreads();
   };
 
@@ -343,11 +378,11 @@ __global__ __launch_bounds__(256, 2) void attn_pipe_kernel(AttnArgs a) {
   if (t < cnt) step(Int<0>{}, t, sA, sB);
 
   if (cnt > 0) {
-    if (__any(ss.rescale != 1.f)) {
+    if (__any(ss.resc_a != 1.f)) {
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc[dt][r] *= ss.rescale;
+        for (int r = 0; r < 16; ++r) acc[dt][r] *= ss.resc_a;
     }
     if (pv_prev) {  // P.V of the last entry, V in stage (cnt - 1) % 2
       const char* vlast = ((cnt - 1) & 1) ? v1 : v0;
@@ -382,13 +417,24 @@ __global__ __launch_bounds__(256, 2) void attn_pipe_kernel(AttnArgs a) {
   }
 }
 
+// The V vote pays where K and V stream from HBM: when the K and V of the
+// heads in flight (one per XCD) exceed the 256 MiB Infinity Cache.  Measured
+// on the video workloads at tau = 0.9: 4.8 % faster at N = 119056 (488 MB in
+// flight), 1.3 % slower at N = 32760 (134 MB), bit-identical output.
+bool vote_pays(const ForwardLaunch& f) {
+  const int64_t heads = std::min<int64_t>(8, (int64_t)f.g.B * f.g.H);
+  return !f.causal && heads * 2 * f.g.N * (int64_t)f.g.D * 2 > (int64_t)256 << 20;
+}
+
 template <int D>
 hipError_t launch_pipe_t(const ForwardLaunch& f, hipStream_t s) {
   const AttnArgs a = make_args(f);
   if (f.causal)
-    hipLaunchKernelGGL((attn_pipe_kernel<D, true>), dim3(a.nwg), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((attn_pipe_kernel<D, true, false>), dim3(a.nwg), dim3(256), 0, s, a);
+  else if (vote_pays(f))
+    hipLaunchKernelGGL((attn_pipe_kernel<D, false, true>), dim3(a.nwg), dim3(256), 0, s, a);
   else
-    hipLaunchKernelGGL((attn_pipe_kernel<D, false>), dim3(a.nwg), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((attn_pipe_kernel<D, false, false>), dim3(a.nwg), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -60,6 +60,11 @@ def decode_skips(bits, cnt):
     ("quant_long", [5], 4, {}),
     ("wan_video", [11], 4, dict(skip_rule="recall", recall=0.95)),
     ("lm_causal", [9], 4, dict(skip_rule="recall", recall=0.9)),
+    # K and V of the eight heads in flight (270 MB) exceed the Infinity Cache:
+    # the forward runs its V-vote schedule
+    ("wan_video", [0, 7], 4, dict(H=8, N=66000, grid=(22, 50, 60))),
+    ("wan_video", [3], 4, dict(H=8, N=66000, grid=(22, 50, 60), skip_rule="recall",
+                               recall=0.95)),
 ])
 def test_fullsize_parity(name, heads, nblocks, over):
     w = dataclasses.replace(make_workload(name), **over)
