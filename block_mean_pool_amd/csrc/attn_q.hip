@@ -404,9 +404,14 @@ __global__ __launch_bounds__(256, 2) void attn_q_kernel(AttnQArgs a) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) p[e] = __builtin_amdgcn_exp2f(fmaf(x[kt][r0 + e], csc, cb));
       psum += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
-      int lo = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
+      // the first conversion of each word writes its low half; the second
+      // overwrites the high half, so the word's old contents do not matter
+      int lo, hi;  // defined by empty asm: no instruction, no zeroing move
+      asm("" : "=v"(lo) : "v"(p[0]));
+      asm("" : "=v"(hi) : "v"(p[4]));
+      lo = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], lo, false);
       lo = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], lo, true);
-      int hi = __builtin_amdgcn_cvt_pk_fp8_f32(p[4], p[5], 0, false);
+      hi = __builtin_amdgcn_cvt_pk_fp8_f32(p[4], p[5], hi, false);
       hi = __builtin_amdgcn_cvt_pk_fp8_f32(p[6], p[7], hi, true);
       pn[2 * c] = lo;
       pn[2 * c + 1] = hi;
