@@ -31,18 +31,27 @@ __device__ __forceinline__ float xhalf_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// The query block a workgroup runs.  Consecutive ids stay on one XCD and one
-// head (xcd_remap), so the head's K and V stay in that XCD's L2.  Under
-// causality a head's query blocks run last-first: block i has 2 i + 2
-// admissible key blocks, so the heaviest start first and the light ones fill
-// the end of the grid.
+// The query block a workgroup runs.
+// * Default: consecutive ids stay on one XCD and one head (xcd_remap), so
+//   each XCD works through whole heads and the head's K and V are shared in
+//   its L2.  Under causality a head's query blocks run last-first: block i
+//   has 2 i + 2 admissible key blocks, so the heaviest start first and the
+//   light ones fill the end of the grid.
+// * window (non-causal calls whose K and V would stream from HBM, eight
+//   heads in flight exceeding the 256 MiB Infinity Cache): xcd_window_remap
+//   with windows of 512 query blocks, what the chip holds at once (2
+//   workgroups on each of 256 CUs).  The whole chip works on one or two
+//   heads at a time, whose K and V then stay in the Infinity Cache, and each
+//   XCD runs 64 consecutive query blocks, which share its L2.
+constexpr int kWindowPerXcd = 64;
 struct QueryBlock {
   int row;  // (b H + h) nqb + i: index into the mask arrays
   int bh;
   int i;
 };
-__device__ __forceinline__ QueryBlock query_block(int nwg, int nqb, bool causal) {
-  const int wg = xcd_remap(blockIdx.x, nwg);
+__device__ __forceinline__ QueryBlock query_block(int nwg, int nqb, bool causal,
+                                                bool window = false) {
+  const int wg = window ? xcd_window_remap(blockIdx.x, nwg, kWindowPerXcd) : xcd_remap(blockIdx.x, nwg);
   const int bh = wg / nqb;
   const int j = wg - bh * nqb;
   const int i = causal ? nqb - 1 - j : j;

@@ -84,7 +84,7 @@ __global__ __launch_bounds__(256, 2) void attn_pipe_kernel(AttnArgs a) {
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hh = lane >> 5;
-  const QueryBlock qblk = query_block(a.nwg, a.nqb, CAUSAL);
+  const QueryBlock qblk = query_block(a.nwg, a.nqb, CAUSAL, VOTE);
   const int wg = qblk.row;  // the query block's row in the mask arrays
   const int bh = qblk.bh;
   const int i = qblk.i;
@@ -190,8 +190,9 @@ __global__ __launch_bounds__(256, 2) void attn_pipe_kernel(AttnArgs a) {
   for (int c = 0; c < 4; ++c) pf[c] = u32x4{0u, 0u, 0u, 0u};
   Soft ss{-INFINITY, 0.f, 1.f, 1.f, 0.f};
   bool pv_prev = false;
-  // VOTE kernels (non-causal, chosen by the host when K and V stream from
-  // HBM) vote on each tile's V transfer: the lambda decision is known once
+  // VOTE kernels (chosen by the host for non-causal calls whose K and V
+  // would stream from HBM; they also take the windowed workgroup order)
+  // vote on each tile's V transfer: the lambda decision is known once
   // the tile's Q.K^T is complete, so the scalar part runs at the end of the
   // previous step and the vote is in LDS by the barrier before the tile's
   // step; a tile no wavefront multiplies is not fetched (a third of them at
@@ -417,10 +418,13 @@ __global__ __launch_bounds__(256, 2) void attn_pipe_kernel(AttnArgs a) {
   }
 }
 
-// The V vote pays where K and V stream from HBM: when the K and V of the
-// heads in flight (one per XCD) exceed the 256 MiB Infinity Cache.  Measured
-// on the video workloads at tau = 0.9: 4.8 % faster at N = 119056 (488 MB in
-// flight), 1.3 % slower at N = 32760 (134 MB), bit-identical output.
+// The VOTE variant (windowed workgroup order + V vote) pays where K and V
+// would stream from HBM: when the K and V of eight heads, one per XCD in the
+// default order, exceed the 256 MiB Infinity Cache.  Rotated medians at
+// N = 119056 (488 MB), bit-identical output: the V vote alone -4.8 %, with
+// the windowed order -11.8 % (lambda = -5) and -15.3 % (lambda = -inf).  At
+// N = 32760 (134 MB, cache-resident either way) the variant measured
+// between -2 % and +1.6 % on different boxes, so the plain kernel stays.
 bool vote_pays(const ForwardLaunch& f) {
   const int64_t heads = std::min<int64_t>(8, (int64_t)f.g.B * f.g.H);
   return !f.causal && heads * 2 * f.g.N * (int64_t)f.g.D * 2 > (int64_t)256 << 20;

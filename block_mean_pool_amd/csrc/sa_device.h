@@ -54,4 +54,18 @@ __device__ __forceinline__ int xcd_remap(int id, int n) {
   return xcd < r ? xcd * (q + 1) + local : r * (q + 1) + (xcd - r) * q + local;
 }
 
+// Workgroup id remap that keeps the whole chip on one stretch of logical
+// ids: XCD x's k-th workgroup (hardware id 8 k + x) works in window
+// w = k / c of 8 c logical ids, on its slice (x + w) % 8 of c consecutive
+// ids.  All eight XCDs share each window, and the slice an XCD takes turns
+// with the window, so an XCD does not meet the same part of every head
+// (where work varies along the sequence).  The last partial window falls
+// back to xcd_remap.  A bijection on [0, n).
+__device__ __forceinline__ int xcd_window_remap(int id, int n, int c) {
+  const int s = 8 * c, full = n / s * s;
+  if (id >= full) return full + xcd_remap(id - full, n - full);
+  const int k = id >> 3, x = id & 7, w = k / c;
+  return w * s + ((x + w) & 7) * c + k % c;
+}
+
 }  // namespace sa

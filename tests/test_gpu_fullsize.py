@@ -60,8 +60,9 @@ def decode_skips(bits, cnt):
     ("quant_long", [5], 4, {}),
     ("wan_video", [11], 4, dict(skip_rule="recall", recall=0.95)),
     ("lm_causal", [9], 4, dict(skip_rule="recall", recall=0.9)),
-    # K and V of the eight heads in flight (270 MB) exceed the Infinity Cache:
-    # the forward runs its V-vote schedule
+    # K and V of eight heads (270 MB) exceed the Infinity Cache: the forward
+    # runs its V-vote schedule in the windowed workgroup order, whose
+    # 512-block windows straddle the heads' 516 query blocks
     ("wan_video", [0, 7], 4, dict(H=8, N=66000, grid=(22, 50, 60))),
     ("wan_video", [3], 4, dict(H=8, N=66000, grid=(22, 50, 60), skip_rule="recall",
                                recall=0.95)),

@@ -199,6 +199,9 @@ CASES = [
        lam=-5.0),
     wl("fp32_causal_d64", 127, 1, 2, 200, 64, dtype="f32", structure="lm", causal=True,
        tau=0.95, lam=-3.0),
+    # lambda = -inf with a real mask: nothing skipped, every kept tile multiplied
+    wl("lam_off_field", 128, 1, 2, 1000, 128, grid=(10, 10, 10), tau=0.9, lam=-math.inf),
+    wl("lam_off_d64", 129, 2, 1, 515, 64, grid=(5, 103, 1), tau=0.9, lam=-math.inf),
 ]
 
 
