@@ -40,6 +40,7 @@ METRIC = "dense-equiv attention TFLOPS + sparsity at fixed rel-L1, N=32760 H=40 
 MEASURED_TRAFFIC = {
     # workload -> (source hash, bytes read, bytes written)
     "wan_video": ("a94fdf35de14c2f0", 111_185_240_064, 387_946_496),
+    "hunyuan_video": ("a94fdf35de14c2f0", 983_599_722_112, 800_134_400),
 }
 # the forward kernel that dominates each kind of workload, and its sources
 FORWARD_KERNELS = {
