@@ -279,7 +279,11 @@ sa_status sparse_attn_step(const sa_params* p, sa_schedule* sched, const void* q
   sa_params run = *p;
   bool refresh;
   if (sched->step < sched->dense_steps) {
+    // every admissible block: tau = 1 under a cumulative-mass rule; a top-k
+    // budget would still cut, so a dense call reads it as top-cdf
     run.tau = 1.0f;
+    if (run.rule == SA_RULE_TOPK) run.rule = SA_RULE_TOPCDF;
+    run.topk_blocks = 0;
     run.skip_rule = SA_SKIP_LAMBDA;
     run.lambda = -INFINITY;
     refresh = true;

@@ -234,7 +234,8 @@ typedef struct sa_schedule {
 
 /* One call of a sequence: stage one when the schedule says so (writing
  * *mask), then stage two with *mask.  Call number s = sched->step runs
- *   s <  dense_steps: predict and forward with tau = 1 and no skip;
+ *   s <  dense_steps: predict and forward with tau = 1 and no skip (every
+ *                     admissible block kept, also under SA_RULE_TOPK);
  *   s >= dense_steps: predict iff (s - dense_steps) % refresh_every == 0,
  *                     then forward, with *p as given except tau, taken
  *                     from tau_by_step when the schedule has one (a reused

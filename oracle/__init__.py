@@ -45,6 +45,7 @@ from .sparse_attn_oracle import (  # noqa: F401
     processing_order,
     cut_length,
     predict_head,
+    predict_from_means,
     group_skip,
     sparse_attention_head,
     dense_attention_head,
@@ -58,7 +59,7 @@ from .quant import (  # noqa: F401
     fp8_quantize_v_blocks,
     sparse_attention_quant_head,
 )
-from .schedule import step_plan, sequence_head, call_tau  # noqa: F401
+from .schedule import step_plan, sequence_head, call_tau, dense_params  # noqa: F401
 from .cluster import (  # noqa: F401
     ClusterParams,
     second_moment,
@@ -75,7 +76,11 @@ from .cluster import (  # noqa: F401
 )
 from .metrics import (  # noqa: F401
     rel_l1,
+    max_abs,
+    admissible_counts,
     block_sparsity,
+    real_groups,
     skip_fraction,
+    predicted_kept_mass,
     true_recall,
 )

@@ -5,9 +5,10 @@ sparse patterns of a head stay similar across denoising steps, so a mask can
 be computed once and reused; early steps matter most (SparseD runs them
 with full attention).  Reading: a sequence of calls with a schedule
 (refresh_every >= 1, dense_steps >= 0).  Call s < dense_steps keeps every
-admissible block and skips nothing; later calls predict a fresh mask on
-call dense_steps and every refresh_every-th call after it, and otherwise
-reuse the last mask, evaluated on the call's own Q, K, V.
+admissible block (whatever the mask rule) and skips nothing; later calls
+predict a fresh mask on call dense_steps and every refresh_every-th call
+after it, and otherwise reuse the last mask, evaluated on the call's own
+Q, K, V.
 
 iCATS abstract: the tolerance to sparse approximation error varies across
 denoising timesteps, so the sparsity follows a schedule guided by the
@@ -49,6 +50,16 @@ def call_tau(p: Params, s: int, tau_by_step=None) -> float:
     return float(tau_by_step[min(s, len(tau_by_step) - 1)])
 
 
+def dense_params(p: Params) -> Params:
+    """The parameters of a dense call: every admissible block kept (tau = 1
+    under a cumulative-mass rule; a top-k budget would still cut, so a
+    dense call reads the top-k rule as top-cdf) and no P.V product
+    skipped (lambda = -inf)."""
+    rule = "topcdf" if p.rule == "topk" else p.rule
+    return dataclasses.replace(p, tau=1.0, rule=rule, topk_blocks=0, skip_rule="lambda",
+                               lam=-math.inf)
+
+
 def sequence_head(steps, p: Params, refresh_every: int, dense_steps: int, attention=None,
                   tau_by_step=None):
     """``steps``: list of (Q, K, V) for one head.  Returns per call
@@ -56,7 +67,7 @@ def sequence_head(steps, p: Params, refresh_every: int, dense_steps: int, attent
     oracle (the unquantised one by default); ``tau_by_step`` the optional
     per-call tau table."""
     attention = attention or sparse_attention_head
-    dense_p = dataclasses.replace(p, tau=1.0, skip_rule="lambda", lam=-math.inf)
+    dense_p = dense_params(p)
     out, kept = [], None
     plan = step_plan(len(steps), refresh_every, dense_steps)
     for s, ((kind, src), (Q, K, V)) in enumerate(zip(plan, steps)):

@@ -206,9 +206,16 @@ def predict_head(Q: np.ndarray, K: np.ndarray, p: Params) -> dict:
     processing order), the predicted map, scores and sets."""
     Q = np.asarray(Q, dtype=np.float64)
     K = np.asarray(K, dtype=np.float64)
-    N, d = Q.shape
-    qbar = pool_means(Q, p.BQ)
-    kbar = pool_means(K, p.BK)
+    return predict_from_means(pool_means(Q, p.BQ), pool_means(K, p.BK), Q.shape[0], p)
+
+
+def predict_from_means(qbar: np.ndarray, kbar: np.ndarray, N: int, p: Params) -> dict:
+    """Stage one after pooling, O2..O7, for block means given as input (the
+    oracle's own, or another implementation's, to check the later steps on
+    their own)."""
+    qbar = np.asarray(qbar, dtype=np.float64)
+    kbar = np.asarray(kbar, dtype=np.float64)
+    d = qbar.shape[1]
     adm = admissible_blocks(N, p.BQ, p.BK, p.causal)
     s = block_scores(qbar, kbar, p.sm(d))
     nkb = kbar.shape[0]

@@ -176,3 +176,46 @@ def dense(Q, K, V, causal, sm=None):
         den = sum(x for _, x in w)
         O.append([sum(x * float(V[c][e]) for c, x in w) / den for e in range(d)])
     return O
+
+
+def true_recall(Q, K, lists, BQ, BK, causal, sm=None, blocks=None):
+    """Mean over the rows of ``blocks`` of the exact softmax mass on the keys
+    of the row's kept key blocks, one row and one key at a time."""
+    n, d = len(Q), len(Q[0])
+    if sm is None:
+        sm = 1.0 / math.sqrt(d)
+    if blocks is None:
+        blocks = range(len(lists))
+    tot, cnt = 0.0, 0
+    for i in blocks:
+        kept_keys = set()
+        for j in lists[i]:
+            for c in range(j * BK, min(n, (j + 1) * BK)):
+                kept_keys.add(c)
+        for r in range(i * BQ, min(n, (i + 1) * BQ)):
+            s = {}
+            for c in range(n):
+                if causal and c > r:
+                    continue
+                s[c] = sm * sum(float(Q[r][e]) * float(K[c][e]) for e in range(d))
+            mx = max(s.values())
+            den = sum(math.exp(v - mx) for v in s.values())
+            num = sum(math.exp(v - mx) for c, v in s.items() if c in kept_keys)
+            tot += num / den
+            cnt += 1
+    return tot / cnt
+
+
+def admissible(n, BQ, BK, causal):
+    """|A_i| per query block, from the token-level definition: key block j
+    is admissible when some key of it is visible to some row of block i."""
+    out = []
+    for i in range(nblk(n, BQ)):
+        rows = range(i * BQ, min(n, (i + 1) * BQ))
+        cnt = 0
+        for j in range(nblk(n, BK)):
+            keys = range(j * BK, min(n, (j + 1) * BK))
+            if any((not causal) or c <= r for r in rows for c in keys):
+                cnt += 1
+        out.append(cnt)
+    return out

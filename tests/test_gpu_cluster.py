@@ -257,6 +257,51 @@ def test_reordered_attention(metric):
     log(f"   max-abs {worst:.3g}")
 
 
+def test_reordered_attention_full_size():
+    """The reordered pipeline at the video workload's N = 32760 with the
+    bench's cluster counts (256 / 512, 4 passes), on two of its heads: the
+    mask of every query block of the reordered tokens against the oracle's
+    stage one, and skip bits and fp32 output of sampled query blocks (first,
+    last, seeded random ones) against the oracle under the GPU's own mask and
+    skips, compared in the original row order."""
+    w = make_workload("wan_video")
+    heads = [0, 21]
+    log(f"[case] reordered attention full size N={w.N} heads {heads}")
+    Q, K, V = heads_of(w, heads)
+    tau32, lam32 = float(np.float32(w.tau)), float(np.float32(w.lam))
+    r = reordered_run(Q, K, V, dict(tau=w.tau, lam=w.lam), 256, 512, 4, "interaction")
+    p = O.Params(tau=tau32, lam=lam32, sm_scale=float(np.float32(1 / math.sqrt(w.D))))
+    nqb = (w.N + 127) // 128
+    rng = np.random.default_rng(17)
+    worst = 0.0
+    for h in range(len(heads)):
+        pq, pk = r["perm_q"][0, h], r["perm_k"][0, h]
+        assert sorted(pq.tolist()) == list(range(w.N)) and sorted(pk.tolist()) == list(range(w.N))
+        Qp, Kp, Vp = Q[0, h][pq], K[0, h][pk], V[0, h][pk]
+        pred = O.predict_head(Qp, Kp, p)
+        _, ex, fails = compare.compare_masks([r["kept"][h]], [pred], tau32)
+        assert not fails, fails[:3]
+        blocks = sorted({0, nqb - 1, *rng.choice(nqb, size=4, replace=False).tolist()})
+        sub_kept = [r["kept"][h][i] if i in blocks else np.zeros(0, dtype=np.int64)
+                    for i in range(nqb)]
+        sub_skip = [r["skips"][h][i] if i in blocks else np.zeros((0, 4), dtype=bool)
+                    for i in range(nqb)]
+        stats = []
+        _, _, osk = O.sparse_attention_head(Qp, Kp, Vp, sub_kept, p, deltas=stats)
+        _, mis, sf = compare.compare_skips([sub_skip[i] for i in blocks],
+                                           [osk[i] for i in blocks],
+                                           [stats[i] for i in blocks], lam32, 1e-3)
+        assert not sf, sf[:3]
+        Op, _, _ = O.sparse_attention_head(Qp, Kp, Vp, sub_kept, p, force_skip=sub_skip)
+        rows = np.concatenate([np.arange(i * 128, min(w.N, (i + 1) * 128)) for i in blocks])
+        err = float(np.abs(r["O"][0, h][pq[rows]] - Op[rows]).max())
+        worst = max(worst, err)
+        assert err <= compare.out_tol("bf16"), f"head {heads[h]}: max-abs {err}"
+        log(f"   head {heads[h]}: masks {ex}/{nqb} exact, {mis} near-lambda skips, blocks "
+            f"{blocks}, max-abs {err:.3g}")
+    log(f"   max-abs {worst:.3g}")
+
+
 def test_cluster_full_size():
     """The video workload's shape (N = 32760, D = 128) with the cluster counts
     the bench uses (NQB and NKB: 256 / 512, 4 passes), on two of its heads;

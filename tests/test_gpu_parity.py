@@ -82,7 +82,9 @@ def check_case(w: Workload, layout="bhnd", check_out=True):
             np.testing.assert_allclose(r["block_prob"][b, h], pred["P"], rtol=0, atol=1e-6)
             # the top-k rule has no mass threshold to be near (tau 2 never is)
             cut_tau = 2.0 if w.rule == "topk" else tau32
-            n, ex, fails = compare.compare_masks([r["kept"][hid]], [pred], cut_tau)
+            # and the scoring, sort and cut alone, on the GPU's own block means
+            mpred = O.predict_from_means(r["qbar"][b, h], r["kbar"][b, h], w.N, p)
+            n, ex, fails = compare.compare_masks([r["kept"][hid]], [pred], cut_tau, [mpred])
             assert not fails, f"mask mismatch head {hid}: {fails[:3]}"
             n_rows += n
             n_exact += ex

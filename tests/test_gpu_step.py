@@ -51,7 +51,10 @@ def decode(idx, cnt, bits, h):
               prec="i8fp8"), 2, 1, None),
     (Workload("step_tau_table", 304, 1, 2, 1000, 128, "bf16", grid=(10, 10, 10), tau=0.9,
               lam=-5.0), 1, 1, [1.0, 0.7, 0.8, 0.95]),
-], ids=["field_k2_d1", "lm_recall_k3", "quant_k2_d1", "field_tau_table"])
+    # a dense call keeps every admissible block under the top-k rule too
+    (Workload("step_topk", 305, 1, 2, 1000, 128, "bf16", structure="lm", causal=True,
+              tau=0.9, lam=-5.0, rule="topk", topk_blocks=3), 2, 1, None),
+], ids=["field_k2_d1", "lm_recall_k3", "quant_k2_d1", "field_tau_table", "topk_causal_d1"])
 def test_step_sequence(w, refresh_every, dense_steps, taus):
     n_steps = 5
     log(f"[case] {w.name} steps={n_steps} refresh_every={refresh_every} dense={dense_steps} "
@@ -60,7 +63,7 @@ def test_step_sequence(w, refresh_every, dense_steps, taus):
     dev = torch.device("cuda:0")
     kw = dict(dtype="bf16", causal=w.causal, tau=w.tau, lam=w.lam, rule=w.rule, prec=w.prec,
               keep_prefix_kblocks=w.keep_prefix_kblocks, skip_rule=w.skip_rule, recall=w.recall,
-              o_fp32=True)
+              topk_blocks=w.topk_blocks, o_fp32=True)
     p = sa.make_params(w.B, w.H, w.N, w.D, **kw)
     nqb, nkb = sa.sparse_attn_mask_shape(p)
     pws, fws = sa.sparse_attn_workspace_size(p)
@@ -76,8 +79,9 @@ def test_step_sequence(w, refresh_every, dense_steps, taus):
     op = O.Params(causal=w.causal, tau=float(np.float32(w.tau)), lam=float(np.float32(w.lam)),
                   rule=w.rule, keep_prefix_kblocks=w.keep_prefix_kblocks,
                   sm_scale=float(np.float32(1.0 / math.sqrt(w.D))), skip_rule=w.skip_rule,
-                  recall=float(np.float32(w.recall)))
-    dense_op = dataclasses.replace(op, tau=1.0, skip_rule="lambda", lam=-math.inf)
+                  recall=float(np.float32(w.recall)), topk_blocks=w.topk_blocks)
+    dense_op = O.dense_params(op)
+    n_adm = O.admissible_counts(w.N, 128, 64, w.causal)
     fn = O.sparse_attention_quant_head if w.prec == "i8fp8" else O.sparse_attention_head
     plan = O.step_plan(n_steps, refresh_every, dense_steps)
     prev = None
@@ -115,6 +119,7 @@ def test_step_sequence(w, refresh_every, dense_steps, taus):
                 assert not fails, f"step {s} head {h}: {fails[:3]}"
             if kind == "dense":
                 assert not any(x.any() for x in gs)
+                assert cnt_h[0, h].tolist() == n_adm.tolist(), f"step {s} head {h}: not dense"
             stats = []
             if pr.skip_rule == "recall":
                 Oref, _, _ = fn(qh, kh, vh, gk, pr, force_skip=gs, deltas=stats)

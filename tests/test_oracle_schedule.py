@@ -86,3 +86,25 @@ def test_tau_table():
     base = O.sequence_head(steps, p, 2, 1)
     for a, b in zip(same, base):
         np.testing.assert_array_equal(a[0], b[0])
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_dense_calls_keep_everything_under_the_topk_rule(causal):
+    """A dense call keeps every admissible block and skips nothing, whatever
+    the mask rule: under a small top-k budget the dense call must still equal
+    dense softmax attention (a closed form), while the sparse calls keep the
+    budget."""
+    w = Workload("seq_topk", 203, 1, 1, 400, 16, "f32", structure="gauss", causal=causal)
+    steps = w.drift_head(0, 0, 3, dtheta=0.2)
+    p = O.Params(BQ=64, BK=32, G=16, causal=causal, rule="topk", topk_blocks=2, lam=-1.0)
+    dp = O.dense_params(p)
+    assert (dp.rule, dp.tau, dp.lam, dp.skip_rule) == ("topcdf", 1.0, -math.inf, "lambda")
+    out = O.sequence_head(steps, p, refresh_every=1, dense_steps=1)
+    adm = O.admissible_blocks(400, 64, 32, causal).sum(axis=1)
+    assert [len(x) for x in out[0][2]] == adm.tolist()
+    od, _ = O.dense_attention_head(*steps[0], 1.0 / math.sqrt(16), causal)
+    np.testing.assert_allclose(out[0][0], od, atol=1e-12)
+    forced = O.forced_blocks(400, 64, 32, causal, 0, O.admissible_blocks(400, 64, 32, causal))
+    for s in (1, 2):
+        want = [min(a, max(f, 2)) for a, f in zip(adm, forced.sum(axis=1))]
+        assert [len(x) for x in out[s][2]] == want
