@@ -12,9 +12,19 @@ seeded synthetic smoothed-field Q/K and Gaussian V.
 
 Printed: ONE JSON line with the headline metric, the roofline of the forward
 kernel (executed MFMA FLOPs / its average launch time, measured with HIP
-events on the launch stream), sparsity, P.V skip fraction, relative L1 vs
-dense fp64 attention on sampled rows, a tau sweep, and the fp64 CPU oracle
-timed on a bounded sample as a baseline.
+events on the launch stream) and of the predictor's pooling kernel (bytes /
+its launch time), a tau sweep and the other mask and skip rules, and the
+CPU-baseline leg.
+
+The CPU-baseline leg is the only part that runs the fp64 oracle (oracle/):
+worker processes, forked before anything touches the GPU, time the oracle
+on a bounded sample of the workload (sampled heads: stage one for the whole
+head, stage two for evenly spaced query blocks under the GPU's mask and skip
+decisions) and compute the dense fp64 rows of that sample.  The same leg
+reports what the oracle says about the GPU's results: max-abs against the
+oracle, rel-L1 against dense attention, true recall, predicted kept mass,
+block sparsity and P.V skip fraction (oracle/metrics.py).  Without it
+(--no-cpu-baseline) those fields are null.
 """
 from __future__ import annotations
 
@@ -22,6 +32,7 @@ import argparse
 import ctypes
 import json
 import math
+import multiprocessing
 import os
 import sys
 import time
@@ -33,25 +44,32 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "dense-equiv attention TFLOPS + sparsity at fixed rel-L1, N=32760 H=40 d=128"
-# HBM traffic of the forward kernel per launch, from two rocprofv3 --pmc
-# passes (FETCH_SIZE x 2.000, WRITE_SIZE x 1.000, the factors a 1 GiB copy
-# reads on the same counters), keyed by the hash of the kernel sources it was
-# measured on: a changed kernel reports null until it is measured again.
+# HBM traffic per launch, from two rocprofv3 --pmc passes (FETCH_SIZE x 2.000,
+# WRITE_SIZE x 1.000, the factors a 1 GiB copy reads on the same counters),
+# keyed by the hash of the kernel sources it was measured on: a changed
+# kernel reports null until it is measured again.
 MEASURED_TRAFFIC = {
-    # workload -> (source hash, bytes read, bytes written)
-    "wan_video": ("a94fdf35de14c2f0", 111_185_240_064, 387_946_496),
-    "hunyuan_video": ("a94fdf35de14c2f0", 983_599_722_112, 800_134_400),
+    # (kernel kind, workload) -> (source hash, bytes read, bytes written)
+    ("bf16", "wan_video"): ("a94fdf35de14c2f0", 111_185_240_064, 387_946_496),
+    ("bf16", "hunyuan_video"): ("a94fdf35de14c2f0", 983_599_722_112, 800_134_400),
 }
-# the forward kernel that dominates each kind of workload, and its sources
+# the forward kernel that dominates each kind of workload, and its sources;
+# "pool" is the predictor's HBM-bound first step
 FORWARD_KERNELS = {
     "bf16": ("attn_pipe_kernel (sparse_attn_forward)", ("attn_pipe.hip", "attn_common.h")),
     "f32": ("attn_kernel (sparse_attn_forward)", ("attn.hip", "attn_common.h")),
     "i8fp8": ("attn_q_kernel (sparse_attn_forward)", ("attn_q.hip", "attn_common.h")),
 }
+POOL_KERNEL = ("pool_kernel (sparse_attn_pool, first step of sparse_attn_predict)",
+               ("pool.hip", "sa_device.h"))
 PEAK_BF16_TFLOPS = 2500.0
 PEAK_I8FP8_TOPS = 5000.0
 PEAK_FP32_TFLOPS = 157.3
+PEAK_HBM_GBPS = 8000.0
 PEAK_CLOCK_GHZ = 2.4  # the engine clock the published peaks assume
+MAX_WORKERS = 16      # the host CPU share of one GPU on the measurement boxes
+SAMPLE_HEADS = 16     # heads the CPU-baseline leg runs the oracle on
+SAMPLE_BLOCKS = 16    # evenly spaced query blocks of each sampled head
 
 
 def parse():
@@ -68,8 +86,6 @@ def parse():
                     help="target recall of the recall skip rule")
     ap.add_argument("--no-peaks", action="store_true",
                     help="skip the GEMM / copy reference measurements")
-    ap.add_argument("--cpu-blocks", type=int, default=256,
-                    help="query blocks of head 0 in the CPU oracle sample")
     ap.add_argument("--stage", default="all", choices=("all", "cluster"),
                     help="cluster: time only sparse_attn_cluster (interaction metric, "
                          "NQB / NKB clusters, 4 passes) on the workload and print its "
@@ -95,24 +111,26 @@ def _build_module():
 
 
 def kernel_source_hash(kind):
-    """Hash of the forward kernel's sources and of the compiler flags the
-    build gives them (which shape the compiled kernel)."""
+    """Hash of a kernel's sources and of the compiler flags the build gives
+    them (which shape the compiled kernel); ``kind`` is a FORWARD_KERNELS key
+    or "pool"."""
     import hashlib
     b = _build_module()
     h = hashlib.sha256()
-    for name in FORWARD_KERNELS[kind][1]:
+    files = POOL_KERNEL[1] if kind == "pool" else FORWARD_KERNELS[kind][1]
+    for name in files:
         h.update(open(os.path.join(ROOT, "block_mean_pool_amd", "csrc", name), "rb").read())
         if name.endswith(".hip"):
             h.update(repr((b.FLAGS, b.PER_FILE_FLAGS.get(name, []))).encode())
     return h.hexdigest()[:16]
 
 
-PROBE_LIB = os.path.join(ROOT, "block_mean_pool_amd", "libsa_probe.so")
+PROBE_LIB = os.path.join(ROOT, "probe", "libsa_probe.so")
 
 
 def load_probe():
     """The benchmark's measurement helpers (clock sampler, MFMA loop), built
-    next to the attention library; None when absent."""
+    beside bench.py; None when absent."""
     if not os.path.exists(PROBE_LIB):
         return None
     lib = ctypes.CDLL(PROBE_LIB)
@@ -232,7 +250,7 @@ def measured_peaks(torch, dev, sampler=None, probe=None):
     copy = 2.0 * x.numel() * 4 * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e9
     del x, y
     out = {"bf16_gemm_8192_tflops": round(gemm, 1), "copy_1gib_gbps": round(copy, 1),
-           "published": {"bf16_dense_tflops": PEAK_BF16_TFLOPS, "hbm_gbps": 8000.0}}
+           "published": {"bf16_dense_tflops": PEAK_BF16_TFLOPS, "hbm_gbps": PEAK_HBM_GBPS}}
     if sampler is not None:
         loop, loop_clock = mfma_loop_peak(torch, probe, sampler, dev)
         out.update({"bf16_gemm_clock_ghz": _r3(gemm_clock),
@@ -244,6 +262,10 @@ def measured_peaks(torch, dev, sampler=None, probe=None):
 
 def _r3(x):
     return None if x is None else round(x, 3)
+
+
+def _rd(x, n=6):
+    return None if x is None else round(float(x), n)
 
 
 def data_description(w):
@@ -269,6 +291,43 @@ def gen_inputs(w, threads=16):
     return tuple(np.stack([x[t] for x in heads]).reshape(shape) for t in range(3))
 
 
+def sample_blocks(nqb, n=SAMPLE_BLOCKS):
+    """n query blocks evenly spaced over the sequence (first and last
+    included)."""
+    return sorted({int(round(x)) for x in np.linspace(0, nqb - 1, min(n, nqb))})
+
+
+def sample_heads(H, n=SAMPLE_HEADS):
+    """n heads evenly spaced over 0 .. H - 1 (first and last included)."""
+    return sorted({int(round(x)) for x in np.linspace(0, H - 1, min(n, H))})
+
+
+def block_rows(blocks, N):
+    return np.concatenate([np.arange(i * 128, min(N, (i + 1) * 128)) for i in blocks])
+
+
+class Sample:
+    """The rows the CPU-baseline leg evaluates: evenly spaced query blocks of
+    evenly spaced heads (batch 0)."""
+
+    def __init__(self, w, n_heads=SAMPLE_HEADS, n_blocks=SAMPLE_BLOCKS):
+        self.nqb = (w.N + 127) // 128
+        self.heads = sample_heads(w.H, n_heads)
+        self.blocks = sample_blocks(self.nqb, n_blocks)
+        self.rows = block_rows(self.blocks, w.N)
+
+    def describe(self, w):
+        return (f"heads {self.heads} of {w.H} (batch 0), query blocks {self.blocks} of "
+                f"{self.nqb} ({len(self.rows)} rows per head)")
+
+    def take(self, torch, o):
+        """The sampled rows of an O tensor [B, H, N, D] as float64 numpy
+        [len(heads), len(rows), D]."""
+        hi = torch.as_tensor(self.heads, device=o.device)
+        ri = torch.as_tensor(self.rows, device=o.device)
+        return o[0].index_select(0, hi).index_select(1, ri).float().cpu().numpy()
+
+
 class Runner:
     """Owns the device buffers of one configuration and runs the two calls."""
 
@@ -277,11 +336,12 @@ class Runner:
         self.sa, self.torch, self.w = sa, torch, w
         self.q, self.k, self.v = q, k, v
         self.o = torch.empty_like(q)
-        self.p = sa.make_params(w.B, w.H, w.N, w.D, dtype=w.dtype, causal=w.causal, tau=tau,
-                                lam=w.lam, rule=rule or w.rule, prec=prec or w.prec,
-                                topk_blocks=topk_blocks,
-                                keep_prefix_kblocks=w.keep_prefix_kblocks,
-                                skip_rule=skip_rule, recall=recall)
+        kw = dict(dtype=w.dtype, causal=w.causal, tau=tau, lam=w.lam, rule=rule or w.rule,
+                  prec=prec or w.prec, topk_blocks=topk_blocks,
+                  keep_prefix_kblocks=w.keep_prefix_kblocks, skip_rule=skip_rule,
+                  recall=recall)
+        self.p = sa.make_params(w.B, w.H, w.N, w.D, **kw)
+        self.p32 = sa.make_params(w.B, w.H, w.N, w.D, o_fp32=True, **kw)
         self.nqb, self.nkb = sa.sparse_attn_mask_shape(self.p)
         pws, fws = sa.sparse_attn_workspace_size(self.p)
         dev = q.device
@@ -325,23 +385,62 @@ class Runner:
         fwd = float(np.mean([b.elapsed_time(c) for _, b, c in ev]))
         return total / steps, pred, fwd, wall
 
-    def decisions(self):
-        """Kept counts and skip bits (one untimed forward with skip output)."""
+    def time_pool(self, steps):
+        """Mean time of the predictor's pooling kernel alone
+        (sparse_attn_pool), HIP events on the launch stream."""
+        torch = self.torch
+        for _ in range(2):
+            self.sa.sparse_attn_pool(self.p, self.q, self.k, self.ws_p)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            self.sa.sparse_attn_pool(self.p, self.q, self.k, self.ws_p)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+
+    def decisions(self, sample=None):
+        """One untimed predict + forward writing skip bits and an fp32 O (the
+        same arithmetic as the timed calls; only the store differs): kept
+        counts and skip words of every query block, and for the sampled heads
+        their kept lists, skip bits and fp32 O rows."""
         torch = self.torch
         nw = (self.nkb + 31) // 32
         skips = torch.zeros((self.w.B, self.w.H, self.nqb, 4, nw), dtype=torch.int32,
                             device=self.q.device)
+        o32 = torch.empty(self.q.shape, dtype=torch.float32, device=self.q.device)
         self.predict()
-        self.forward(skips)
+        self.sa.sparse_attn_forward(self.p32, self.q, self.k, self.v, self.mask, o32, None,
+                                    skips, self.ws_f)
         torch.cuda.synchronize()
-        cnt = self.cnt.cpu().numpy().astype(np.int64)
-        bits = skips.cpu().numpy().view(np.uint32)
-        skipped = 0
-        for t in range(int(cnt.max())):
-            live = cnt > t  # [B, H, nqb]
-            bit = (bits[..., t // 32] >> np.uint32(t % 32)) & 1  # [B, H, nqb, 4]
-            skipped += int((bit.astype(bool) & live[..., None]).sum())
-        return cnt, skipped
+        out = dict(cnt=self.cnt.cpu().numpy().astype(np.int64),
+                   bits=skips.cpu().numpy().view(np.uint32))
+        if sample is not None:
+            idx = self.idx[0].index_select(0, torch.as_tensor(sample.heads, device=self.q.device))
+            idx = idx.cpu().numpy()
+            out["kept"] = {h: [idx[n, i, :out["cnt"][0, h, i]].astype(np.int64)
+                               for i in range(self.nqb)] for n, h in enumerate(sample.heads)}
+            out["o32_rows"] = sample.take(torch, o32)
+        del o32, skips
+        return out
+
+
+def executed_tiles(cnt, bits, N):
+    """Kept tiles, and (tile, group) pairs whose P.V ran, over every query
+    block: groups past the last row of a partial query block hold no rows
+    and count as neither."""
+    tiles = int(cnt.sum())
+    nqb = cnt.shape[-1]
+    real = np.array([min(4, (min(N, (i + 1) * 128) - i * 128 + 31) // 32) for i in range(nqb)])
+    skipped = 0
+    for t in range(int(cnt.max()) if cnt.size else 0):
+        live = cnt > t  # [B, H, nqb]
+        bit = ((bits[..., t // 32] >> np.uint32(t % 32)) & 1).astype(bool)  # [B, H, nqb, 4]
+        bit &= np.arange(4)[None, None, None, :] < real[None, None, :, None]
+        skipped += int((bit & live[..., None]).sum())
+    groups = int((cnt * real[None, None, :]).sum())
+    return tiles, groups, skipped
 
 
 def admissible_count(w, nqb, nkb):
@@ -354,47 +453,234 @@ def admissible_count(w, nqb, nkb):
     return w.B * w.H * tot
 
 
-_DENSE_CACHE = {}
+# --------------------------------------------------------------------------
+# The CPU-baseline leg: the only code here that runs the fp64 oracle.  Its
+# worker processes are forked before the parent initialises the GPU and
+# never touch it; each regenerates its head from the seeded generator.
+# --------------------------------------------------------------------------
+def cpu_cores():
+    """Host cores this process may use, capped at the CPU share of one GPU."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        n = os.cpu_count() or 1
+    return max(1, min(n, MAX_WORKERS))
 
 
-def sample_blocks(nqb, n=16):
-    """n query blocks evenly spaced over the sequence (first and last
-    included)."""
-    return sorted({int(round(x)) for x in np.linspace(0, nqb - 1, min(n, nqb))})
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
-def rel_l1_sample(w, Q, K, V, O_gpu, oracle):
-    """rel-L1 of the GPU output vs dense fp64 attention on sampled rows: 16
-    evenly spaced query blocks of 3 heads (the dense rows are computed once
-    per workload and reused across calls)."""
-    heads = sorted({0, w.H // 2, w.H - 1})
-    nqb = (w.N + 127) // 128
-    blocks = sample_blocks(nqb)
-    num = den = 0.0
+def _worker_init():
+    from threadpoolctl import threadpool_limits
+    global _LIMIT
+    _LIMIT = threadpool_limits(1)  # one BLAS thread per worker process
+
+
+def _oracle_params(w, tau, skip_rule, recall, rule, topk_blocks):
+    import oracle as O
+    return O.Params(causal=w.causal, tau=float(np.float32(tau)), lam=float(np.float32(w.lam)),
+                    rule=rule, keep_prefix_kblocks=w.keep_prefix_kblocks,
+                    sm_scale=float(np.float32(1.0 / math.sqrt(w.D))), skip_rule=skip_rule,
+                    recall=float(np.float32(recall)), topk_blocks=topk_blocks)
+
+
+def _oracle_sparse_task(task):
+    """Timed part, one head: stage one for the whole head, then stage two
+    for the sampled query blocks under the GPU's kept lists and skip bits."""
+    import oracle as O
+    w, h, blocks, kept, skips, pkw = task
+    q, k, v = w.head(0, h)
+    p = _oracle_params(w, **pkw)
+    nqb = len(kept)
+    t0 = time.perf_counter()
+    pred = O.predict_head(q, k, p)
+    t1 = time.perf_counter()
+    sub_kept = [kept[i] if i in blocks else np.zeros(0, dtype=np.int64) for i in range(nqb)]
+    sub_skip = [skips[i] if i in blocks else np.zeros((0, 4), dtype=bool) for i in range(nqb)]
+    if w.prec == "i8fp8":
+        Ob, _, _ = O.sparse_attention_quant_head(q, k, v, sub_kept, p, force_skip=sub_skip)
+    else:
+        Ob, _, _ = O.sparse_attention_head(q, k, v, sub_kept, p, force_skip=sub_skip)
+    t2 = time.perf_counter()
+    return dict(h=h, t_stage1=t1 - t0, t_stage2=t2 - t1, O=Ob[block_rows(blocks, w.N)],
+                mask_exact=int(sum(np.array_equal(a, b) for a, b in zip(kept, pred["kept"]))),
+                pred_mass=O.predicted_kept_mass(pred["P"], kept))
+
+
+def _oracle_dense_task(task):
+    """Dense fp64 rows of the sampled query blocks of one head, and the true
+    recall of the GPU's mask on them."""
+    import oracle as O
+    w, h, blocks, kept = task
+    q, k, v = w.head(0, h)
     sm = 1.0 / math.sqrt(w.D)
-    rows = np.concatenate([np.arange(i * 128, min(w.N, (i + 1) * 128)) for i in blocks])
-    for h in heads:
-        key = (w.name, h)
-        if key not in _DENSE_CACHE:
-            _DENSE_CACHE[key] = oracle.dense_attention_head(Q[0, h], K[0, h], V[0, h], sm,
-                                                            w.causal, rows=rows)[0]
-        od = _DENSE_CACHE[key]
-        num += float(np.abs(O_gpu[h][rows] - od).sum())
-        den += float(np.abs(od).sum())
-    return num / den, f"heads {heads}, {len(blocks)} evenly spaced query blocks {blocks}"
+    t0 = time.perf_counter()
+    od, _ = O.dense_attention_head(q, k, v, sm, w.causal, rows=block_rows(blocks, w.N))
+    t1 = time.perf_counter()
+    rec = O.true_recall(q, k, kept, 128, 64, sm, w.causal, blocks=blocks)
+    return dict(h=h, dense=od, t_dense=t1 - t0, recall=rec)
 
 
-def reuse_sweep(sa, torch, w, oracle, n_steps=6, ks=(1, 3, 6), dtheta=0.05, threads=16):
+def _oracle_drift_task(task):
+    """Dense fp64 rows of the sampled query blocks of one head for every
+    call of a drifting sequence."""
+    import oracle as O
+    w, h, blocks, n_steps, dtheta = task
+    seq = w.drift_head(0, h, n_steps, dtheta)
+    rows = block_rows(blocks, w.N)
+    sm = 1.0 / math.sqrt(w.D)
+    return h, [O.dense_attention_head(*seq[s], sm, w.causal, rows=rows)[0]
+               for s in range(n_steps)]
+
+
+def decode_skips(bits, cnt):
+    """Skip bits of one query block as bool [cnt, 4] (list entry, group)."""
+    t = np.arange(cnt)
+    return ((bits[:, t // 32] >> (t % 32).astype(np.uint32)) & 1).T.astype(bool)
+
+
+class CpuBaselineLeg:
+    """Forked before the GPU is touched; afterwards runs the oracle on the
+    sample and reports the baseline and the oracle's view of the results."""
+
+    def __init__(self, cores):
+        self.cores = cores
+        self.pool = multiprocessing.get_context("fork").Pool(cores, initializer=_worker_init)
+
+    def close(self):
+        self.pool.close()
+        self.pool.join()
+
+    def run(self, w, sample, head, others, reuse, pkw):
+        import oracle as O
+        # timed: the sparse path of the oracle on the sample, all workers
+        tasks = []
+        for h in sample.heads:
+            skips = [decode_skips(head["bits"][0, h, i], head["cnt"][0, h, i])
+                     if i in sample.blocks else None for i in range(sample.nqb)]
+            tasks.append((w, h, sample.blocks, head["kept"][h], skips, pkw))
+        workers = min(self.cores, len(tasks))
+        t0 = time.perf_counter()
+        sparse = self.pool.map(_oracle_sparse_task, tasks, chunksize=1)
+        wall_map = time.perf_counter() - t0
+        # the dense fp64 leg (the rel-L1 reference) and the true recall
+        t0 = time.perf_counter()
+        dense = self.pool.map(_oracle_dense_task,
+                              [(w, h, sample.blocks, head["kept"][h]) for h in sample.heads],
+                              chunksize=1)
+        wall_dense = time.perf_counter() - t0
+        drift = {}
+        if reuse:
+            drift = dict(self.pool.map(
+                _oracle_drift_task,
+                [(w, h, reuse["sample"].blocks, reuse["n_steps"], reuse["dtheta"])
+                 for h in reuse["sample"].heads], chunksize=1))
+        Od = np.stack([d["dense"] for d in dense])          # [heads, rows, D]
+        Oo = np.stack([r["O"] for r in sparse])
+        # the oracle's view of the GPU's results
+        rows_per_block = [min(w.N, (i + 1) * 128) - i * 128 for i in range(sample.nqb)]
+        adm = np.tile(O.admissible_counts(w.N, 128, 64, w.causal), (w.B, w.H, 1))
+
+        def quality(res):
+            out = {"sparsity": O.block_sparsity(res["cnt"], adm)}
+            skl, rows = [], []
+            for b in range(w.B):
+                for h in range(w.H):
+                    for i in range(sample.nqb):
+                        skl.append(decode_skips(res["bits"][b, h, i], res["cnt"][b, h, i]))
+                        rows.append(rows_per_block[i])
+            out["pv_skip_fraction"] = O.skip_fraction(skl, rows, 32)
+            out["rel_l1"] = O.rel_l1(res["o_rows"], Od)
+            return out
+
+        q_head = quality(head)
+        rows_all = sample.rows
+        n_rows = len(rows_all) * len(sample.heads)
+        t_stage1 = float(np.mean([r["t_stage1"] for r in sparse]))
+        t_stage2 = float(np.sum([r["t_stage2"] for r in sparse]))
+        t_all = float(np.sum([r["t_stage1"] + r["t_stage2"] for r in sparse]))
+        per_block = t_stage2 / (len(sample.heads) * len(sample.blocks))
+        flops = 4.0 * n_rows * w.N * w.D / (2.0 if w.causal else 1.0)
+        one_thread = flops / t_all
+        # the workers run one head each at a time: the sample's oracle time
+        # on `workers` cores is its single-thread time shared among them
+        seconds = t_all / workers
+        head_s = t_stage1 + per_block * sample.nqb
+        baseline = {
+            "value": round(flops / seconds / 1e12, 6),
+            "unit": "TFLOPS (dense-equivalent)",
+            "cores": workers,
+            "kind": "oracle",
+            "sample": (f"{sample.describe(w)}: fp64 numpy oracle, stage one for each sampled "
+                       f"head plus stage two for the sampled query blocks under the GPU's mask "
+                       f"and skip decisions; one head per task on {workers} worker processes "
+                       f"with one BLAS thread each; value = dense-equivalent FLOPs of the "
+                       f"sampled rows / (summed oracle seconds of the tasks / {workers}); "
+                       f"input generation not timed"),
+            "seconds": round(seconds, 3),
+            "wall_seconds_with_generation": round(wall_map, 3),
+            "one_thread_tflops": round(one_thread / 1e12, 6),
+            "os_cpu_count": os.cpu_count(),
+            "cpu_model": cpu_model(),
+            "blas_threads_per_worker": 1,
+            "seconds_per_head_one_thread": round(head_s, 3),
+            "extrapolated_full_workload_s": {
+                "value": round(head_s * w.B * w.H / workers, 1),
+                "note": "extrapolation, not measured: seconds per head on one thread (stage one "
+                        "+ every query block at the sampled per-block time) x B*H heads / "
+                        "worker processes (heads are independent)"},
+            "dense_fp64_leg": {"seconds": round(wall_dense, 3),
+                               "seconds_per_block_one_thread": round(
+                                   float(np.sum([d["t_dense"] for d in dense])) /
+                                   (len(sample.heads) * len(sample.blocks)), 4),
+                               "rows": n_rows},
+        }
+        vs = {
+            "max_abs_vs_oracle": O.max_abs(head["o32_rows"], Oo),
+            "rel_l1_vs_dense": q_head["rel_l1"],
+            "true_recall": float(np.mean([d["recall"] for d in dense])),
+            "predicted_kept_mass": {
+                "mean": float(np.mean(np.concatenate([r["pred_mass"] for r in sparse]))),
+                "min": float(np.min(np.concatenate([r["pred_mass"] for r in sparse])))},
+            "mask_rows_exact": f"{sum(r['mask_exact'] for r in sparse)} of "
+                               f"{len(sample.heads) * sample.nqb}",
+            "sparsity": q_head["sparsity"],
+            "pv_skip_fraction": q_head["pv_skip_fraction"],
+            "sample": sample.describe(w),
+        }
+        other_q = {name: quality(res) for name, res in others.items()}
+        reuse_q = {}
+        if reuse:
+            rs = reuse["sample"]
+            for kk, calls in reuse["o_rows"].items():
+                rels = []
+                for s, o_rows in enumerate(calls):
+                    dd = np.stack([drift[h][s] for h in rs.heads])
+                    rels.append(O.rel_l1(o_rows, dd))
+                reuse_q[kk] = rels
+        return baseline, vs, other_q, reuse_q
+
+
+# --------------------------------------------------------------------------
+# GPU legs (no oracle)
+# --------------------------------------------------------------------------
+def reuse_sweep(sa, torch, w, sample, n_steps=6, ks=(1, 3, 6), dtheta=0.05, threads=16):
     """Mask reuse across calls (sparse_attn_step): a seeded drifting
     sequence of n_steps inputs (synth Workload.drift_head, a stand-in for
     successive denoising steps), run with refresh_every = k for each k; per
-    k: mean time per call (stage one amortised), mean and worst rel-L1 vs
-    dense fp64 attention on sampled rows, and the number of refreshes."""
+    k: mean time per call (stage one amortised), the number of refreshes,
+    and each call's O on the sampled rows (rel-L1 against dense fp64
+    attention comes from the CPU-baseline leg)."""
     dev = torch.device("cuda:0")
     shape = (n_steps, 3, 1, w.H, w.N, w.D)
     xs = torch.empty(shape, dtype=torch.bfloat16, device=dev)
-    sample_heads = sorted({0, w.H // 2, w.H - 1})
-    host = {}
 
     def gen(h):
         return h, w.drift_head(0, h, n_steps, dtheta)
@@ -404,8 +690,6 @@ def reuse_sweep(sa, torch, w, oracle, n_steps=6, ks=(1, 3, 6), dtheta=0.05, thre
             for s in range(n_steps):
                 for t in range(3):
                     xs[s, t, 0, h].copy_(torch.from_numpy(seq[s][t]))
-            if h in sample_heads:
-                host[h] = seq
     p = sa.make_params(w.B, w.H, w.N, w.D, dtype=w.dtype, causal=w.causal, tau=w.tau,
                        lam=w.lam, rule=w.rule, prec=w.prec,
                        keep_prefix_kblocks=w.keep_prefix_kblocks)
@@ -417,17 +701,10 @@ def reuse_sweep(sa, torch, w, oracle, n_steps=6, ks=(1, 3, 6), dtheta=0.05, thre
     ws_p = torch.empty(max(pws, 1), dtype=torch.uint8, device=dev)
     ws_f = torch.empty(max(fws, 1), dtype=torch.uint8, device=dev)
     o = torch.empty((1, w.H, w.N, w.D), dtype=torch.bfloat16, device=dev)
-    blocks = sample_blocks(nqb, 8)
-    rows = np.concatenate([np.arange(i * 128, min(w.N, (i + 1) * 128)) for i in blocks])
-    sm = 1.0 / math.sqrt(w.D)
-    dense = {}
-    for h in sample_heads:
-        for s in range(n_steps):
-            dense[h, s], _ = oracle.dense_attention_head(*host[h][s], sm, w.causal, rows=rows)
-    out = []
+    out, o_rows = [], {}
     for k in ks:
         sched = sa.make_schedule(k, 0)
-        times, rels, refreshes = [], [], 0
+        times, refreshes, rows = [], 0, []
         for s in range(n_steps):
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record()
@@ -437,26 +714,22 @@ def reuse_sweep(sa, torch, w, oracle, n_steps=6, ks=(1, 3, 6), dtheta=0.05, thre
             torch.cuda.synchronize()
             times.append(e0.elapsed_time(e1))
             refreshes += sched.refreshed
-            og = o.float().cpu().numpy()[0]
-            num = sum(float(np.abs(og[h][rows] - dense[h, s]).sum()) for h in sample_heads)
-            den = sum(float(np.abs(dense[h, s]).sum()) for h in sample_heads)
-            rels.append(num / den)
+            rows.append(sample.take(torch, o))
+        o_rows[k] = rows
         out.append(dict(refresh_every=k, steps=n_steps, refreshes=refreshes,
-                        ms_per_call=round(float(np.mean(times)), 4),
-                        rel_l1_mean=round(float(np.mean(rels)), 6),
-                        rel_l1_max=round(float(np.max(rels)), 6)))
+                        ms_per_call=round(float(np.mean(times)), 4)))
     del xs
-    return out
+    return out, dict(sample=sample, n_steps=n_steps, dtheta=dtheta, o_rows=o_rows)
 
 
-def reorder_sweep(sa, torch, w, q, k, v, Q, K, V, oracle, measure_on, taus=(0.9, 0.95, 0.98),
-                  iters=4, reps=3, quant=None):
+def reorder_sweep(sa, torch, w, q, k, v, measure_on, taus=(0.9, 0.95, 0.98), iters=4, reps=3,
+                  quant=None):
     """Token reordering (sparse_attn_cluster + sparse_attn_permute) ahead of
     the two stages: per metric, the time of the clustering (NQB query and NKB
     key clusters per head, ``iters`` passes) and of the four row
-    permutations, then per tau the sparsity, P.V skip share, predict +
-    forward time and rel-L1 (dense fp64 on sampled rows, in the original row
-    order) of the pipeline run on the reordered tokens."""
+    permutations, then per tau the sparsity, P.V skip share and predict +
+    forward time of the pipeline run on the reordered tokens, with O
+    scattered back to the original rows for the CPU-baseline leg's rel-L1."""
     p = sa.make_params(w.B, w.H, w.N, w.D, dtype=w.dtype)
     nqb, nkb = sa.sparse_attn_mask_shape(p)
     dev = q.device
@@ -489,23 +762,21 @@ def reorder_sweep(sa, torch, w, q, k, v, Q, K, V, oracle, measure_on, taus=(0.9,
         permute_ms = e0.elapsed_time(e1)
         rows = []
         for tau in taus:
-            r, m = measure_on(qp, kp, vp, tau)
-            sa.sparse_attn_permute(p, r.o, pq, 1, o_back)
-            torch.cuda.synchronize()
-            rl, _ = rel_l1_sample(w, Q, K, V, o_back.float().cpu().numpy()[0], oracle)
-            rows.append(dict(tau=tau, sparsity=round(m["sparsity"], 5),
-                             pv_skip_fraction=round(m["skip"], 5), rel_l1=round(rl, 6),
+            r, m = measure_on(qp, kp, vp, tau, None, lambda rr: sa.sparse_attn_permute(
+                p, rr.o, pq, 1, o_back) or o_back, f"reorder_{metric}_tau{tau}")
+            rows.append(dict(tau=tau, key=f"reorder_{metric}_tau{tau}",
+                             sparsity=round(m["sparsity"], 5),
+                             pv_skip_fraction=round(m["skip"], 5),
                              predict_forward_ms=round(m["ms"], 4)))
             del r
         if quant is not None and metric == "interaction":
             for prec in ("i8fp8", "i4fp8"):
-                r, m = measure_on(qp, kp, vp, w.tau, prec)
-                sa.sparse_attn_permute(p, r.o, pq, 1, o_back)
-                torch.cuda.synchronize()
-                rl, _ = rel_l1_sample(w, Q, K, V, o_back.float().cpu().numpy()[0], oracle)
+                r, m = measure_on(qp, kp, vp, w.tau, prec, lambda rr: sa.sparse_attn_permute(
+                    p, rr.o, pq, 1, o_back) or o_back, f"reorder_{metric}_{prec}")
                 quant.append(dict(order="interaction clusters", prec=prec, tau=w.tau,
+                                  key=f"reorder_{metric}_{prec}",
                                   sparsity=round(m["sparsity"], 5),
-                                  pv_skip_fraction=round(m["skip"], 5), rel_l1=round(rl, 6),
+                                  pv_skip_fraction=round(m["skip"], 5),
                                   forward_ms=round(m["forward_ms"], 4)))
                 del r
         out.append(dict(metric=metric, clusters_q=nqb, clusters_k=nkb, iters=iters,
@@ -515,33 +786,6 @@ def reorder_sweep(sa, torch, w, q, k, v, Q, K, V, oracle, measure_on, taus=(0.9,
     return out
 
 
-def cpu_baseline(w, Q, K, V, tau, blocks, skip_rule="lambda", recall=1.0):
-    """The fp64 oracle as it stands, single-threaded, on head 0: stage one
-    for the whole head plus stage two for the first `blocks` query blocks."""
-    import oracle as O
-    from threadpoolctl import threadpool_limits
-    p = O.Params(causal=w.causal, tau=float(np.float32(tau)), lam=w.lam, rule=w.rule,
-                 keep_prefix_kblocks=w.keep_prefix_kblocks, skip_rule=skip_rule,
-                 recall=float(np.float32(recall)))
-    q, k, v = Q[0, 0], K[0, 0], V[0, 0]
-    with threadpool_limits(1):
-        t0 = time.perf_counter()
-        pred = O.predict_head(q, k, p)
-        kept = pred["kept"][:blocks]
-        if w.prec == "i8fp8":
-            O.sparse_attention_quant_head(q, k, v, kept, p)
-        else:
-            O.sparse_attention_head(q, k, v, kept, p)
-        dt = time.perf_counter() - t0
-    rows = min(w.N, blocks * 128)
-    flops = 4.0 * rows * w.N * w.D / (2.0 if w.causal else 1.0)
-    return {"value": flops / dt / 1e12, "unit": "TFLOPS (dense-equivalent)", "cores": 1,
-            "kind": "oracle", "seconds": dt,
-            "sample": f"head 0 of {w.H}: stage one for the whole head + stage two for "
-                      f"query blocks 0..{blocks - 1} ({rows} of {w.N} rows), fp64 numpy, "
-                      f"1 BLAS thread"}
-
-
 def main():
     args = parse()
     if args.gpus != 1:
@@ -549,12 +793,23 @@ def main():
               "shards by head with no communication, so multi-GPU figures are not "
               "measured here", file=sys.stderr)
         sys.exit(2)
+    from synth import make_workload
+    w = make_workload(args.workload)
+    leg = None
+    if not args.no_cpu_baseline and args.stage == "all":
+        # forked now, while nothing in this process has touched the GPU
+        leg = CpuBaselineLeg(cpu_cores())
+    try:
+        run(args, w, leg)
+    finally:
+        if leg is not None:
+            leg.close()
+
+
+def run(args, w, leg):
     import torch
     import block_mean_pool_amd as sa
-    import oracle
-    from synth import make_workload
 
-    w = make_workload(args.workload)
     print(f"[bench] generating {w.name} B={w.B} H={w.H} N={w.N} D={w.D}", file=sys.stderr,
           flush=True)
     t0 = time.perf_counter()
@@ -563,6 +818,7 @@ def main():
     tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
     dev = torch.device("cuda:0")
     q, k, v = (torch.from_numpy(x).to(tdt).to(dev) for x in (Q, K, V))
+    del Q, K, V
     dense = w.dense_flops()
 
     if args.stage == "cluster":
@@ -589,18 +845,23 @@ def main():
               flush=True)
         return
 
+    sample = Sample(w)
+    captures = {}  # name -> {"cnt", "bits", "o_rows"} for the CPU-baseline leg
+
     def measure(tau, steps, warmup, skip_rule=None, recall=None, rule=None, topk_blocks=0,
-                tensors=None, prec=None):
+                tensors=None, prec=None, o_view=None, key=None):
         qq, kk, vv = tensors or (q, k, v)
         r = Runner(sa, torch, w, qq, kk, vv, tau,
                    skip_rule=skip_rule or args.skip_rule,
                    recall=args.recall if recall is None else recall, rule=rule,
                    topk_blocks=topk_blocks, prec=prec)
         ms, pred_ms, fwd_ms, wall = r.time_steps(steps, warmup)
-        cnt, skipped = r.decisions()
+        o_rows = sample.take(torch, o_view(r) if o_view else r.o)
+        dec = r.decisions()
+        tiles, groups, skipped = executed_tiles(dec["cnt"], dec["bits"], w.N)
         adm = admissible_count(w, r.nqb, r.nkb)
-        tiles = int(cnt.sum())
-        groups = 4 * tiles
+        if key is not None:
+            captures[key] = dict(cnt=dec["cnt"], bits=dec["bits"], o_rows=o_rows)
         # executed MFMA work: Q.K^T on every kept tile, P.V on every group
         # that was not skipped (32 rows x 64 keys x D per group)
         flops = 2.0 * 128 * 64 * w.D * tiles + 2.0 * 32 * 64 * w.D * (groups - skipped)
@@ -615,91 +876,75 @@ def main():
     peak = PEAK_I8FP8_TOPS if w.prec == "i8fp8" else (
         PEAK_FP32_TFLOPS if w.dtype == "f32" else PEAK_BF16_TFLOPS)
     achieved = m["exec_flops"] / (m["forward_ms"] * 1e-3) / 1e12
-    O_gpu = r.o.float().cpu().numpy()[0]
-    rel, rel_sample = rel_l1_sample(w, Q, K, V, O_gpu, oracle)
+    head = r.decisions(sample)
+    head["o_rows"] = sample.take(torch, r.o)
+    pool_ms = r.time_pool(max(5, args.steps))
+    esz = 2 if w.dtype == "bf16" else 4
+    pool_bytes = (2.0 * w.B * w.H * w.N * w.D * esz +
+                  4.0 * w.B * w.H * (r.nqb + r.nkb) * w.D)
     print(f"[bench] {m['ms']:.3f} ms/step -> {value:.1f} dense-equiv TFLOPS; forward "
-          f"{m['forward_ms']:.3f} ms = {achieved:.1f} TFLOP/s executed", file=sys.stderr,
-          flush=True)
+          f"{m['forward_ms']:.3f} ms = {achieved:.1f} TFLOP/s executed; pool {pool_ms:.4f} ms = "
+          f"{pool_bytes / (pool_ms * 1e-3) / 1e9:.0f} GB/s", file=sys.stderr, flush=True)
 
-    sweep = []
-    recall_sweep = []
+    sweep, recall_sweep, topk_sweep = [], [], []
+    few = max(3, args.steps // 4)
+
+    def sweep_row(key, ms_, **fields):
+        return dict(**fields, key=key, sparsity=round(ms_["sparsity"], 5),
+                    pv_skip_fraction=round(ms_["skip"], 5), ms_per_step=round(ms_["ms"], 4),
+                    dense_equiv_tflops=round(dense / (ms_["ms"] * 1e-3) / 1e12, 2))
+
     if not args.no_sweep and w.name == "wan_video":
         for tau in (0.9, 0.95, 0.99):
-            rs, ms_ = measure(tau, max(3, args.steps // 4), 1)
-            o_s = rs.o.float().cpu().numpy()[0]
-            rl, _ = rel_l1_sample(w, Q, K, V, o_s, oracle)
-            sweep.append(dict(tau=tau, sparsity=round(ms_["sparsity"], 5),
-                              pv_skip_fraction=round(ms_["skip"], 5), rel_l1=round(rl, 6),
-                              ms_per_step=round(ms_["ms"], 4),
-                              dense_equiv_tflops=round(dense / (ms_["ms"] * 1e-3) / 1e12, 2)))
+            rs, ms_ = measure(tau, few, 1, key=f"tau{tau}")
+            sweep.append(sweep_row(f"tau{tau}", ms_, tau=tau))
             del rs
             print(f"[bench] sweep tau={tau}: {sweep[-1]}", file=sys.stderr, flush=True)
         # the recall skip rule (dynamic threshold from the cumulative energy)
         # against the static lambda, at the headline tau
         for rho in (0.99, 0.95, 0.9):
-            rs, ms_ = measure(w.tau, max(3, args.steps // 4), 1, skip_rule="recall", recall=rho)
-            o_s = rs.o.float().cpu().numpy()[0]
-            rl, _ = rel_l1_sample(w, Q, K, V, o_s, oracle)
-            recall_sweep.append(dict(recall=rho, tau=w.tau, sparsity=round(ms_["sparsity"], 5),
-                                     pv_skip_fraction=round(ms_["skip"], 5),
-                                     rel_l1=round(rl, 6), ms_per_step=round(ms_["ms"], 4),
-                                     dense_equiv_tflops=round(dense / (ms_["ms"] * 1e-3) / 1e12,
-                                                              2)))
+            key = f"recall{rho}"
+            rs, ms_ = measure(w.tau, few, 1, skip_rule="recall", recall=rho, key=key)
+            recall_sweep.append(sweep_row(key, ms_, recall=rho, tau=w.tau))
             del rs
             print(f"[bench] recall rule rho={rho}: {recall_sweep[-1]}", file=sys.stderr,
                   flush=True)
-
-    topk_sweep = []
-    if not args.no_sweep and w.name == "wan_video":
         # the fixed-budget top-k mask against the cumulative-mass cut: the
         # first budget matches the mean kept count of the headline tau
         mean_kept = int(round(m["tiles"] / (w.B * w.H * r.nqb)))
         for kb in (mean_kept, r.nkb // 2, r.nkb // 4):
-            rs, ms_ = measure(w.tau, max(3, args.steps // 4), 1, rule="topk", topk_blocks=kb)
-            o_s = rs.o.float().cpu().numpy()[0]
-            rl, _ = rel_l1_sample(w, Q, K, V, o_s, oracle)
-            topk_sweep.append(dict(topk_blocks=kb, sparsity=round(ms_["sparsity"], 5),
-                                   pv_skip_fraction=round(ms_["skip"], 5), rel_l1=round(rl, 6),
-                                   ms_per_step=round(ms_["ms"], 4),
-                                   dense_equiv_tflops=round(dense / (ms_["ms"] * 1e-3) / 1e12,
-                                                            2)))
+            key = f"topk{kb}"
+            rs, ms_ = measure(w.tau, few, 1, rule="topk", topk_blocks=kb, key=key)
+            topk_sweep.append(sweep_row(key, ms_, topk_blocks=kb))
             del rs
             print(f"[bench] top-k {kb}: {topk_sweep[-1]}", file=sys.stderr, flush=True)
 
-    reuse = []
+    reuse, reuse_cap = [], None
+    reorder, quant = [], []
     if not args.no_sweep and w.name == "wan_video":
         print("[bench] mask reuse across a drifting sequence", file=sys.stderr, flush=True)
-        reuse = reuse_sweep(sa, torch, w, oracle)
+        reuse, reuse_cap = reuse_sweep(sa, torch, w, Sample(w, 3, 8))
         for r_ in reuse:
             print(f"[bench] reuse {r_}", file=sys.stderr, flush=True)
-
-    reorder = []
-    quant = []
-    if not args.no_sweep and w.name == "wan_video":
         # INT8 and 4-bit Q.K^T (FP8 P.V) at the headline tau, contiguous order
         for prec in ("i8fp8", "i4fp8"):
-            rs, ms_ = measure(w.tau, max(3, args.steps // 4), 1, prec=prec)
-            rl, _ = rel_l1_sample(w, Q, K, V, rs.o.float().cpu().numpy()[0], oracle)
-            quant.append(dict(order="contiguous", prec=prec, tau=w.tau,
+            key = f"contiguous_{prec}"
+            rs, ms_ = measure(w.tau, few, 1, prec=prec, key=key)
+            quant.append(dict(order="contiguous", prec=prec, tau=w.tau, key=key,
                               sparsity=round(ms_["sparsity"], 5),
-                              pv_skip_fraction=round(ms_["skip"], 5), rel_l1=round(rl, 6),
+                              pv_skip_fraction=round(ms_["skip"], 5),
                               forward_ms=round(ms_["forward_ms"], 4)))
             del rs
         print("[bench] token reordering", file=sys.stderr, flush=True)
         reorder = reorder_sweep(
-            sa, torch, w, q, k, v, Q, K, V, oracle,
-            lambda qq, kk, vv, tau, prec=None: measure(tau, max(3, args.steps // 4), 1,
-                                                       tensors=(qq, kk, vv), prec=prec),
+            sa, torch, w, q, k, v,
+            lambda qq, kk, vv, tau, prec, o_view, key: measure(
+                tau, few, 1, tensors=(qq, kk, vv), prec=prec, o_view=o_view, key=key),
             quant=quant)
         for r_ in reorder:
             print(f"[bench] reorder {r_}", file=sys.stderr, flush=True)
         for r_ in quant:
             print(f"[bench] quantised Q.K^T {r_}", file=sys.stderr, flush=True)
-
-    cpu = None
-    if not args.no_cpu_baseline:
-        print("[bench] timing the CPU oracle sample", file=sys.stderr, flush=True)
-        cpu = cpu_baseline(w, Q, K, V, w.tau, args.cpu_blocks, args.skip_rule, args.recall)
 
     peaks, clock = None, None
     if not args.no_peaks:
@@ -726,12 +971,47 @@ def main():
         except Exception as e:  # noqa: BLE001
             print(f"[bench] reference peaks skipped: {e}", file=sys.stderr, flush=True)
 
+    cpu, vs_oracle = None, None
+    if leg is not None:
+        print(f"[bench] CPU-baseline leg: the oracle on {sample.describe(w)} with "
+              f"{leg.cores} worker processes", file=sys.stderr, flush=True)
+        pkw = dict(tau=w.tau, skip_rule=args.skip_rule,
+                   recall=args.recall if args.skip_rule == "recall" else 1.0, rule=w.rule,
+                   topk_blocks=0)
+        cpu, vs_oracle, other_q, reuse_q = leg.run(w, sample, head, captures, reuse_cap, pkw)
+        for row in sweep + recall_sweep + topk_sweep + quant:
+            row["rel_l1"] = _rd(other_q[row["key"]]["rel_l1"])
+            row["sparsity_oracle_metric"] = _rd(other_q[row["key"]]["sparsity"], 5)
+        for r_ in reorder:
+            for row in r_["by_tau"]:
+                row["rel_l1"] = _rd(other_q[row["key"]]["rel_l1"])
+        for r_ in reuse:
+            rels = reuse_q[r_["refresh_every"]]
+            r_["rel_l1_mean"] = _rd(np.mean(rels))
+            r_["rel_l1_max"] = _rd(np.max(rels))
+        print(f"[bench] CPU baseline {cpu['value']:.4g} TFLOPS on {cpu['cores']} cores; "
+              f"max-abs vs oracle {vs_oracle['max_abs_vs_oracle']:.3g}, true recall "
+              f"{vs_oracle['true_recall']:.4f}", file=sys.stderr, flush=True)
+    for rows in (sweep, recall_sweep, topk_sweep, quant):
+        for row in rows:
+            row.pop("key", None)
+    for r_ in reorder:
+        for row in r_["by_tau"]:
+            row.pop("key", None)
+
     kind = forward_kind(w)
     traffic = None
-    mt = MEASURED_TRAFFIC.get(w.name)
+    mt = MEASURED_TRAFFIC.get((kind, w.name))
     if mt and mt[0] == kernel_source_hash(kind):
         traffic = {"read_bytes": mt[1], "written_bytes": mt[2], "total_bytes": mt[1] + mt[2],
                    "source": "rocprofv3 FETCH_SIZE/WRITE_SIZE, copy-calibrated"}
+    pool_traffic = None
+    mt = MEASURED_TRAFFIC.get(("pool", w.name))
+    if mt and mt[0] == kernel_source_hash("pool"):
+        pool_traffic = {"read_bytes": mt[1], "written_bytes": mt[2],
+                        "total_bytes": mt[1] + mt[2],
+                        "source": "rocprofv3 FETCH_SIZE/WRITE_SIZE, copy-calibrated"}
+    pool_gbps = pool_bytes / (pool_ms * 1e-3) / 1e9
     out = {
         "metric": METRIC,
         "value": round(value, 3),
@@ -750,10 +1030,16 @@ def main():
                    "block_q": 128, "block_k": 64, "lambda_group_rows": 32,
                    "skip_rule": args.skip_rule,
                    **({"recall": args.recall} if args.skip_rule == "recall" else {})},
-        "sparsity": round(m["sparsity"], 5),
-        "pv_skip_fraction": round(m["skip"], 5),
-        "rel_l1_vs_dense": round(rel, 6),
-        "rel_l1_sample": rel_sample,
+        "sparsity": _rd(vs_oracle["sparsity"], 5) if vs_oracle else None,
+        "pv_skip_fraction": _rd(vs_oracle["pv_skip_fraction"], 5) if vs_oracle else None,
+        "rel_l1_vs_dense": _rd(vs_oracle["rel_l1_vs_dense"]) if vs_oracle else None,
+        "true_recall": _rd(vs_oracle["true_recall"]) if vs_oracle else None,
+        "predicted_kept_mass": ({k_: _rd(v_) for k_, v_ in
+                                 vs_oracle["predicted_kept_mass"].items()}
+                                if vs_oracle else None),
+        "max_abs_vs_oracle": _rd(vs_oracle["max_abs_vs_oracle"], 7) if vs_oracle else None,
+        "oracle_sample": vs_oracle["sample"] if vs_oracle else None,
+        "mask_rows_equal_to_oracle": vs_oracle["mask_rows_exact"] if vs_oracle else None,
         "predict_ms": round(m["predict_ms"], 4),
         "forward_ms": round(m["forward_ms"], 4),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
@@ -763,10 +1049,18 @@ def main():
                      "executed_flops_per_launch": m["exec_flops"],
                      "clock": clock,
                      "measured_peaks": peaks},
+        "roofline_predictor": {"bound": "hbm", "achieved": round(pool_gbps, 1),
+                               "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                               "frac": round(pool_gbps / PEAK_HBM_GBPS, 4),
+                               "traffic": pool_traffic, "kernel": POOL_KERNEL[0],
+                               "kernel_source_hash": kernel_source_hash("pool"),
+                               "bytes_per_launch": pool_bytes, "ms_per_launch": round(pool_ms, 5),
+                               "mask_kernel_ms": round(m["predict_ms"] - pool_ms, 4)},
         "tau_sweep": sweep,
         "recall_rule_sweep": recall_sweep,
         "topk_rule_sweep": topk_sweep,
         "mask_reuse": {"sequence": "6 calls, inputs cos(0.05 s) A + sin(0.05 s) B (seeded)",
+                       "rel_l1_sample": reuse_cap["sample"].describe(w) if reuse_cap else None,
                        "by_refresh_every": reuse},
         "token_reorder": reorder,
         "qk_precision": quant,

@@ -13,6 +13,7 @@ Entry points have the C names:
     sparse_attn_mask_shape(params) -> (nqb, nkb)
     sparse_attn_workspace_size(params) -> (predict_bytes, forward_bytes)
     sparse_attn_predict(params, q, k, mask, ws, stream=None)
+    sparse_attn_pool(params, q, k, ws, stream=None)
     sparse_attn_forward(params, q, k, v, mask, o, lse=None, skip_bits=None,
                         ws=None, stream=None)
     sparse_attn_step(params, schedule, q, k, v, mask, o, lse=None,
@@ -103,6 +104,7 @@ def _load():
         "sparse_attn_mask_shape": [P(SaParams), P(ctypes.c_int64), P(ctypes.c_int64)],
         "sparse_attn_workspace_size": [P(SaParams), P(ctypes.c_size_t), P(ctypes.c_size_t)],
         "sparse_attn_predict": [P(SaParams), vp, vp, P(SaMask), vp, ctypes.c_size_t, vp],
+        "sparse_attn_pool": [P(SaParams), vp, vp, vp, ctypes.c_size_t, vp],
         "sparse_attn_forward": [P(SaParams), vp, vp, vp, P(SaMask), vp, vp, vp, vp,
                                 ctypes.c_size_t, vp],
         "sparse_attn_info": [P(ctypes.c_int32), P(ctypes.c_int32)],
@@ -277,6 +279,17 @@ def sparse_attn_predict(p: SaParams, q, k, mask: SaMask, ws, stream=None, ws_byt
                                    _ptr(ws), nb, _stream(stream)), "sparse_attn_predict")
 
 
+def sparse_attn_pool(p: SaParams, q, k, ws, stream=None, ws_bytes=None):
+    """Stage one's block means alone, written to ``ws`` (a predict
+    workspace) in its layout: qbar float [B,H,NQB,D] at offset 0, kbar float
+    [B,H,NKB,D] at the next 256-byte boundary."""
+    _check_qkv(p, q=q, k=k)
+    _need(ws, "ws", ("uint8", "int8"))
+    nb = _nbytes(ws) if ws_bytes is None else ws_bytes
+    _check(lib.sparse_attn_pool(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(ws), nb,
+                                _stream(stream)), "sparse_attn_pool")
+
+
 def sparse_attn_forward(p: SaParams, q, k, v, mask: SaMask, o, lse=None, skip_bits=None,
                         ws=None, stream=None, ws_bytes=None):
     """Stage two.  Writes ``o`` (and ``lse`` / ``skip_bits`` when given)."""
@@ -373,7 +386,7 @@ def sparse_attn_permute(p: SaParams, x, perm, inverse, y, stream=None, elem_byte
 __all__ = [
     "SaParams", "SaMask", "SparseAttnError", "make_params", "make_mask",
     "sparse_attn_mask_shape", "sparse_attn_workspace_size", "sparse_attn_predict",
-    "sparse_attn_forward", "sparse_attn_info", "sparse_attn_status_str",
+    "sparse_attn_forward", "sparse_attn_pool", "sparse_attn_info", "sparse_attn_status_str",
     "SaClusterParams", "SaReorder", "make_cluster_params", "make_reorder",
     "sparse_attn_cluster_workspace_size", "sparse_attn_cluster", "sparse_attn_permute",
     "SaSchedule", "make_schedule", "sparse_attn_step",

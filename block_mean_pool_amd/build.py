@@ -5,8 +5,9 @@
 
 Every .hip file under csrc/ is compiled with hipcc for gfx950 and linked
 into one shared library next to this file; the benchmark's measurement
-helpers under probe/ go into a library of their own (libsa_probe.so), so the
-attention library's ABI holds only the method.  Packed-fp32 VALU
+helpers (probe/ beside bench.py) go into a library of their own
+(probe/libsa_probe.so), so the attention library's ABI holds only the
+method.  Packed-fp32 VALU
 instructions are disabled for all device code.
 """
 from __future__ import annotations
@@ -20,8 +21,9 @@ import tempfile
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libsparse_attn.so")
-PROBE_DIR = os.path.join(HERE, "probe")
-PROBE_LIB = os.path.join(HERE, "libsa_probe.so")
+# the benchmark's measurement helpers live beside bench.py, not in the package
+PROBE_DIR = os.path.join(os.path.dirname(HERE), "probe")
+PROBE_LIB = os.path.join(PROBE_DIR, "libsa_probe.so")
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

@@ -151,9 +151,11 @@ sa_status sparse_attn_workspace_size(const sa_params* p, size_t* predict_ws, siz
 namespace {
 
 // predict / forward with a dry-run mode that validates everything and
-// enqueues nothing (so a composite call can check all of its parts first)
+// enqueues nothing (so a composite call can check all of its parts first).
+// pool_only: stage one's block means alone (no mask arguments).
 sa_status predict_impl(const sa_params* p, const void* q, const void* k, const sa_mask* out,
-                       void* ws, size_t ws_bytes, void* stream, bool dry) {
+                       void* ws, size_t ws_bytes, void* stream, bool dry,
+                       bool pool_only = false) {
   sa::Geometry g;
   bool empty;
   sa_status st = check_params(p, &g, &empty);
@@ -161,7 +163,7 @@ sa_status predict_impl(const sa_params* p, const void* q, const void* k, const s
   if (empty) return ok();
   if (!q || !k) return fail(SA_ERR_INVALID_ARG, "q or k is NULL");
   if (!aligned16(q) || !aligned16(k)) return fail(SA_ERR_INVALID_ARG, "q/k not 16-byte aligned");
-  if (!out || !out->kept_idx || !out->kept_cnt)
+  if (!pool_only && (!out || !out->kept_idx || !out->kept_cnt))
     return fail(SA_ERR_INVALID_ARG, "mask output (kept_idx, kept_cnt) is NULL");
   const PredictLayout L = predict_layout(g);
   if (!ws || ws_bytes < L.total)
@@ -173,9 +175,9 @@ sa_status predict_impl(const sa_params* p, const void* q, const void* k, const s
   a.k = k;
   a.qbar = reinterpret_cast<float*>(static_cast<char*>(ws) + L.qbar);
   a.kbar = reinterpret_cast<float*>(static_cast<char*>(ws) + L.kbar);
-  a.kept_idx = out->kept_idx;
-  a.kept_cnt = out->kept_cnt;
-  a.block_prob = out->block_prob;
+  a.kept_idx = pool_only ? nullptr : out->kept_idx;
+  a.kept_cnt = pool_only ? nullptr : out->kept_cnt;
+  a.block_prob = pool_only ? nullptr : out->block_prob;
   a.causal = p->causal;
   a.rule = p->rule;
   a.keep_prefix = p->keep_prefix_kblocks;
@@ -186,6 +188,7 @@ sa_status predict_impl(const sa_params* p, const void* q, const void* k, const s
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = sa::launch_pool(a, s);
   if (e != hipSuccess) return fail(SA_ERR_HIP, "pool launch: %s", hipGetErrorString(e));
+  if (pool_only) return ok();
   e = sa::launch_mask(a, s);
   if (e != hipSuccess) return fail(SA_ERR_HIP, "mask launch: %s", hipGetErrorString(e));
   return ok();
@@ -254,6 +257,11 @@ extern "C" {
 sa_status sparse_attn_predict(const sa_params* p, const void* q, const void* k, const sa_mask* out,
                               void* ws, size_t ws_bytes, void* stream) {
   return predict_impl(p, q, k, out, ws, ws_bytes, stream, false);
+}
+
+sa_status sparse_attn_pool(const sa_params* p, const void* q, const void* k, void* ws,
+                           size_t ws_bytes, void* stream) {
+  return predict_impl(p, q, k, nullptr, ws, ws_bytes, stream, false, true);
 }
 
 sa_status sparse_attn_forward(const sa_params* p, const void* q, const void* k, const void* v,

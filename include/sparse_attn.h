@@ -180,6 +180,20 @@ SA_API sa_status sparse_attn_predict(const sa_params* p, const void* q, const vo
                               const sa_mask* out, void* ws, size_t ws_bytes,
                               void* stream);
 
+/* Stage one's first step alone: the block means qbar (query blocks of
+ * block_q rows) and kbar (key blocks of block_k rows), written to `ws` in
+ * the predict layout (sparse_attn_workspace_size), each the fp32 mean of
+ * its block's valid rows.  The SpargeAttn abstract's first stage predicts
+ * the attention map quickly; the iCATS abstract describes the prior work's
+ * estimate from query and key tokens grouped independently, of which a
+ * contiguous block is the simplest grouping.  This is the HBM-bound part of
+ * stage one (every element of Q and K read once), exposed for callers that
+ * reuse the means and for measuring it on its own; sparse_attn_predict
+ * runs it as its first step.  Arguments and errors as for
+ * sparse_attn_predict without the mask. */
+SA_API sa_status sparse_attn_pool(const sa_params* p, const void* q, const void* k, void* ws,
+                                  size_t ws_bytes, void* stream);
+
 /* Stage two.  For each query block, processes mask->kept_idx in list order
  * with an online softmax (running max m, running sum l).  For each group of
  * 32 consecutive rows (one wavefront) and each tile:

@@ -29,7 +29,7 @@ def test_probe_library_exports():
     """The benchmark's measurement helpers build into their own library,
     outside the attention library's ABI."""
     import os
-    path = os.path.join(os.path.dirname(sa.LIB_PATH), "libsa_probe.so")
+    path = os.path.join(os.path.dirname(os.path.dirname(sa.LIB_PATH)), "probe", "libsa_probe.so")
     probe = ctypes.CDLL(path)
     for n in ("sa_probe_clock", "sa_probe_clock_max_samples", "sa_probe_mfma",
               "sa_probe_mfma_chains"):
@@ -119,6 +119,26 @@ def test_invalid_params_rejected_before_launch(kw, code):
         sa.sparse_attn_forward(p, fake, fake, fake, mask, fake, ws=fake, ws_bytes=1 << 40,
                                stream=0)
     assert e.value.code == code
+    with pytest.raises(sa.SparseAttnError) as e:
+        sa.sparse_attn_pool(p, fake, fake, fake, ws_bytes=1 << 40, stream=0)
+    assert e.value.code == code
+
+
+def test_pool_validated_before_launch():
+    p = sa.make_params(1, 2, 1000, 128)
+    fake = 1 << 20  # never dereferenced: validation fails first
+    need = sa.sparse_attn_workspace_size(p)[0]
+    with pytest.raises(sa.SparseAttnError) as e:
+        sa.sparse_attn_pool(p, fake, fake, fake, ws_bytes=need - 1, stream=0)
+    assert e.value.code == sa.SA_ERR_WORKSPACE
+    with pytest.raises(sa.SparseAttnError) as e:
+        sa.sparse_attn_pool(p, fake + 8, fake, fake, ws_bytes=need, stream=0)
+    assert e.value.code == sa.SA_ERR_INVALID_ARG
+    with pytest.raises(sa.SparseAttnError) as e:
+        sa.sparse_attn_pool(p, 0, fake, fake, ws_bytes=need, stream=0)
+    assert e.value.code == sa.SA_ERR_INVALID_ARG
+    # an empty problem is a valid no-op
+    sa.sparse_attn_pool(sa.make_params(1, 2, 0, 128), 0, 0, 0, ws_bytes=0, stream=0)
 
 
 def test_step_schedule_validated_before_launch():

@@ -329,3 +329,35 @@ def test_empty_and_error_paths_on_gpu():
     assert e.value.code == sa.SA_ERR_WORKSPACE
     torch.cuda.synchronize()
     assert int(cnt.abs().sum()) == 0  # nothing ran
+
+
+@pytest.mark.parametrize("dtype,D,N", [("bf16", 128, 1000), ("f32", 64, 777)])
+def test_pool_entry_point_matches_predict(dtype, D, N):
+    """sparse_attn_pool writes the same block means as predict's first step,
+    bit for bit, in the predict workspace layout; and they match the
+    oracle's fp64 means."""
+    import block_mean_pool_amd as sa
+    w = Workload("pool_only", 502, 2, 3, N, D, dtype, grid=None, structure="gauss")
+    log(f"[case] pool entry point {dtype} D={D} N={N}")
+    Q, K, V = w.tensors()
+    r = gpu_harness.run(Q, K, V, dtype=dtype, forward=False)
+    p = sa.make_params(w.B, w.H, N, D, dtype=dtype)
+    pws, _ = sa.sparse_attn_workspace_size(p)
+    ws = torch.full((pws,), 0xA5, dtype=torch.uint8, device="cuda")
+    q, k = (gpu_harness.to_device(x, dtype) for x in (Q, K))
+    sa.sparse_attn_pool(p, q, k, ws)
+    torch.cuda.synchronize()
+    h = ws.cpu().numpy()
+    nqb, nkb = r["nqb"], r["nkb"]
+    nq_bytes = w.B * w.H * nqb * D * 4
+    koff = (nq_bytes + 255) // 256 * 256
+    qbar = h[:nq_bytes].view(np.float32).reshape(w.B, w.H, nqb, D)
+    kbar = h[koff:koff + w.B * w.H * nkb * D * 4].view(np.float32).reshape(w.B, w.H, nkb, D)
+    np.testing.assert_array_equal(qbar.view(np.uint32), r["qbar"].view(np.uint32))
+    np.testing.assert_array_equal(kbar.view(np.uint32), r["kbar"].view(np.uint32))
+    for b in range(w.B):
+        for hh in range(w.H):
+            np.testing.assert_allclose(qbar[b, hh], O.pool_means(Q[b, hh], 128), rtol=1e-5,
+                                       atol=1e-6)
+            np.testing.assert_allclose(kbar[b, hh], O.pool_means(K[b, hh], 64), rtol=1e-5,
+                                       atol=1e-6)
