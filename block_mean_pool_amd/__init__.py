@@ -237,8 +237,10 @@ def _check_outputs(p: SaParams, o, lse, skip_bits):
     bhn = max(p.B, 0) * max(p.H, 0) * max(p.N, 0)
     _need(lse, "lse", ("float32",), bhn)
     nqb, nkb = (p.N + 127) // 128, (p.N + 63) // 64
+    groups = 128 // (p.lambda_group_rows or 32) if p.lambda_group_rows in (0, 16, 32, 64, 128) \
+        else 4  # an unsupported G is rejected by the library
     _need(skip_bits, "skip_bits", ("int32", "uint32"),
-          max(p.B, 0) * max(p.H, 0) * nqb * 4 * ((nkb + 31) // 32))
+          max(p.B, 0) * max(p.H, 0) * nqb * groups * ((nkb + 31) // 32))
 
 
 def sparse_attn_mask_shape(p: SaParams):

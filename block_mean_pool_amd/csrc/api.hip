@@ -28,6 +28,7 @@ sa_status ok() {
 }
 
 constexpr size_t kAlign = 256;
+constexpr int kDefaultGroupRows = 32;  // one wavefront's rows
 size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -61,8 +62,10 @@ sa_status check_params(const sa_params* p, sa::Geometry* g, bool* empty) {
   if (!(p->sm_scale >= 0.f) || std::isinf(p->sm_scale))
     return fail(SA_ERR_INVALID_ARG, "sm_scale=%g", (double)p->sm_scale);
   if (p->keep_prefix_kblocks < 0) return fail(SA_ERR_INVALID_ARG, "keep_prefix_kblocks < 0");
-  if (p->lambda_group_rows != 0 && p->lambda_group_rows != 32)
-    return fail(SA_ERR_UNSUPPORTED, "lambda_group_rows=%d (supported: 32)", p->lambda_group_rows);
+  if (p->lambda_group_rows != 0 && p->lambda_group_rows != 16 && p->lambda_group_rows != 32 &&
+      p->lambda_group_rows != 64 && p->lambda_group_rows != 128)
+    return fail(SA_ERR_UNSUPPORTED, "lambda_group_rows=%d (supported: 16, 32, 64, 128)",
+                p->lambda_group_rows);
   if (p->N > 262144) return fail(SA_ERR_UNSUPPORTED, "N=%d > 262144", p->N);
   if (p->o_fp32 != 0 && p->o_fp32 != 1) return fail(SA_ERR_INVALID_ARG, "o_fp32=%d", p->o_fp32);
   const int64_t esz = p->dtype == SA_BF16 ? 2 : 4;
@@ -226,6 +229,7 @@ sa_status forward_impl(const sa_params* p, const void* q, const void* k, const v
   a.lambda = p->lambda;
   a.recall_on = p->skip_rule == SA_SKIP_RECALL;
   a.recall = p->recall;
+  a.group_rows = p->lambda_group_rows ? p->lambda_group_rows : kDefaultGroupRows;
   a.o_fp32 = p->o_fp32 || p->dtype == SA_F32;
   if (dry) return ok();
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -484,7 +488,7 @@ sa_status sparse_attn_permute(const sa_params* p, const void* x, const int32_t* 
 }
 
 sa_status sparse_attn_info(int32_t* default_group_rows, int32_t* version) {
-  if (default_group_rows) *default_group_rows = 32;
+  if (default_group_rows) *default_group_rows = kDefaultGroupRows;
   if (version) *version = SPARSE_ATTN_VERSION;
   return ok();
 }

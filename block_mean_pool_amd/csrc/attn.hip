@@ -3,9 +3,11 @@
 //
 // Stage two of the SpargeAttn abstract: an online softmax-aware filter that
 // costs nothing extra and skips more matrix products.  Reading: for each
-// kept tile, a wavefront (32 query rows) skips its P.V product when
-// max over its rows of (tile max - new running max) < lambda; m and l are
-// updated either way.  Tiles are processed in list order (the predictor's
+// kept tile, a group of G query rows (by default a wavefront's 32) skips its
+// P.V product when max over its rows of (tile max - new running max) <
+// lambda; m and l are updated either way.  G = 16 zeroes the P of the half
+// wavefront that skips; G = 64 and 128 OR the wavefronts' decisions through
+// LDS.  Tiles are processed in list order (the predictor's
 // sorted order), which fixes which tiles the filter can skip.
 //
 // Workgroup = one (batch, head, 128-row query block), 4 wavefronts x 32 rows.
@@ -118,6 +120,7 @@ __global__ __launch_bounds__(256, (sizeof(T) == 4 && D == 128) ? 1 : 2) void att
   using TL = Tile<T, D>;
   constexpr int NQF = TL::E == 2 ? TL::NKK : 2 * TL::NKK;  // 16-byte Q fragments
   __shared__ __align__(16) char smem[2 * TL::STAGE];
+  __shared__ uint32_t vote[4];  // G >= 64: 1 if wavefront w needs the tile's P.V
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6;
@@ -158,8 +161,8 @@ __global__ __launch_bounds__(256, (sizeof(T) == 4 && D == 128) ? 1 : 2) void att
   // base + e) and are picked with readlane; the next chunk is prefetched
   int lvec = lane < cnt ? lst[lane] : 0;
   int nvec = 64 + lane < cnt ? lst[64 + lane] : 0;
-  uint32_t* skip_out =
-      a.skip_bits ? a.skip_bits + ((size_t)wg * 4 + w) * a.skip_words : nullptr;
+  SkipOut<true> skip_out;
+  skip_out.init(a.skip_bits, wg, w, a.G, a.skip_words);
 
   f32x16 acc[TL::NDT];
 #pragma unroll
@@ -169,7 +172,6 @@ __global__ __launch_bounds__(256, (sizeof(T) == 4 && D == 128) ? 1 : 2) void att
   float m = -INFINITY;  // running max, log2 units
   float l = 0.f;        // this lane's share of the running sum
   float drop = 0.f;     // recall rule: energy this row has dropped (row total)
-  uint32_t skip_word = 0;
 
   // V^T transpose reads: this lane's source key (within a 16-key chunk, +8
   // for the second read) and d offset (within a 32-wide d tile)
@@ -220,8 +222,13 @@ __global__ __launch_bounds__(256, (sizeof(T) == 4 && D == 128) ? 1 : 2) void att
     mloc = xhalf_max(mloc);
     const float mloc2 = mloc * a.c2;
     const float mnew = fmaxf(m, mloc2);
-    bool do_pv = true;
-    if (!a.lam_off) do_pv = __any((mloc2 != -INFINITY) && (mloc2 - mnew >= a.lam2));
+    bool need = true;     // some row of the group needs the tile's P.V
+    uint32_t split = 0u;  // G = 16: the halves of the wavefront decide apart
+    if (!a.lam_off) {
+      const bool nl = (mloc2 != -INFINITY) && (mloc2 - mnew >= a.lam2);
+      need = wave_need(nl);
+      if (a.G == 16) split = half_split(nl);
+    }
     const float alpha = (mnew == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m - mnew);
     const float negm = (mnew == -INFINITY) ? 0.f : -mnew;
     float psum = 0.f;
@@ -235,11 +242,26 @@ __global__ __launch_bounds__(256, (sizeof(T) == 4 && D == 128) ? 1 : 2) void att
       }
     l = alpha * l + psum;
     m = mnew;
-    if (a.recall_on) {  // drop the tile if the row's dropped share stays <= 1 - recall
+    float E = 0.f;
+    if (a.recall_on) {  // drop the tile if the rows' dropped share stays <= 1 - recall
       drop *= alpha;
-      const float E = xhalf_sum(psum), L = xhalf_sum(l);
-      do_pv = __any(!(drop + E <= a.omr * L));
-      if (!do_pv) drop += E;
+      E = xhalf_sum(psum);
+      const bool nl = !(drop + E <= a.omr * xhalf_sum(l));
+      need = wave_need(nl);
+      split = a.G == 16 ? half_split(nl) : 0u;
+    }
+    if (a.G > 32) {  // the group's decision, voted through LDS
+      if (lane == 0) vote[w] = need ? 1u : 0u;
+      __syncthreads();
+      need = group_need(vote, w, a.G);
+    }
+    const bool keep = split ? split_keeps(split, l32) : need;
+    if (a.recall_on && !keep) drop += E;
+    if (split) {  // G = 16, one half skips: its P is zero
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[kt][r] = keep ? s[kt][r] : 0.f;
     }
     if (__any(alpha != 1.f)) {
 #pragma unroll
@@ -248,7 +270,7 @@ __global__ __launch_bounds__(256, (sizeof(T) == 4 && D == 128) ? 1 : 2) void att
         for (int r = 0; r < 16; ++r) acc[dt][r] *= alpha;
     }
 
-    if (do_pv) {
+    if (need) {
       // O^T += V^T P^T.  Chunk c of 16 keys uses p values [8 (c & 1), +8) of
       // sub-tile c >> 1: lane half hh holds keys 16 c + 8 (e / 4) + 4 hh +
       // e % 4 for e in [0, 8).
@@ -295,13 +317,7 @@ __global__ __launch_bounds__(256, (sizeof(T) == 4 && D == 128) ? 1 : 2) void att
       }
     }
 
-    if (skip_out) {
-      skip_word |= (do_pv ? 0u : 1u) << (t & 31);
-      if ((t & 31) == 31 || t + 1 == cnt) {
-        if (lane == 0) skip_out[t >> 5] = skip_word;
-        skip_word = 0;
-      }
-    }
+    skip_out.put(t, cnt, need, split, lane);
 
     if (t + 1 < cnt) st.store(smem + ((t + 1) & 1) * TL::STAGE, tid);
     if (((t + 1) & 63) == 0) {

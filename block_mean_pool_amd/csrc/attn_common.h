@@ -31,6 +31,102 @@ __device__ __forceinline__ float xhalf_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// Skip groups of G rows: 16 (half a wavefront), 32 (one wavefront), 64 (a
+// wavefront pair) or 128 (the whole query block).  `need_lane` holds for a
+// lane whose row needs the tile's P.V product; lanes l and l ^ 32 hold the
+// same row.  wave_need: some row of the wavefront needs it.  For G = 16,
+// half_split tells the halves apart: 0 when both halves decide alike
+// (both need it, or neither), else 1 (only rows 0-15 need it) or 2 (only
+// rows 16-31).
+__device__ __forceinline__ bool wave_need(bool need_lane) { return __any(need_lane); }
+__device__ __forceinline__ uint32_t half_split(bool need_lane) {
+  const uint64_t bal = __builtin_amdgcn_ballot_w64(need_lane);
+  const uint64_t lo = 0x0000ffff0000ffffull;
+  const bool a = (bal & lo) != 0, b = (bal & ~lo) != 0;
+  return a == b ? 0u : (a ? 1u : 2u);
+}
+// G >= 64: the group needs the product if one of its wavefronts does
+// (votes[w] = 1 when wavefront w needs it, published before a barrier).
+__device__ __forceinline__ bool group_need(const uint32_t* votes, int w, int G) {
+  const int per = G >> 5, g0 = w & ~(per - 1);  // per = 2 or 4
+  uint32_t any = 0;
+  for (int i = 0; i < per; ++i) any |= votes[g0 + i];
+  return any != 0u;
+}
+// Whether this lane's row (l32 = lane % 32) is kept by a half split.
+__device__ __forceinline__ bool split_keeps(uint32_t split, int l32) {
+  return (split >> (l32 >> 4)) & 1u;
+}
+
+// Edge-tile masking of a lane's 32 scores of a 64-key tile (first key key0):
+// score r of key half kt is key key0 + 32 kt + 8 (r / 4) + 4 hh + r % 4, set
+// to -inf past N, for rows past N, and (causal) after the lane's row.  The
+// per-score offsets are compile-time constants against one scalar and one
+// per-lane value, so no per-score lane offsets stay live.
+template <bool CAUSAL, typename F>
+__device__ __forceinline__ void mask_scores(F (&s)[2], int key0, int N, int hh, int qrow,
+                                            bool qvalid) {
+  const int lim = N - key0;  // offsets >= lim are keys past N
+  const int hh4 = 4 * hh;
+  const int dq = hh4 - (qrow - key0);  // causal: offset hh4 + c visible iff dq <= -c
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int c = 32 * kt + 8 * (r >> 2) + (r & 3);
+      const bool ok = qvalid && hh4 < lim - c && (!CAUSAL || dq <= -c);
+      s[kt][r] = ok ? s[kt][r] : -INFINITY;
+    }
+}
+
+// Skip-bit output of one wavefront: skip_bits is [rows of the mask,
+// 128 / G, words]; group slot g, list entry t -> bit t % 32 of word t / 32.
+// G = 16: a wavefront writes slots 2 w and 2 w + 1 (TWO kernels handle that
+// case; a TWO kernel with another G writes one slot); G = 32: slot w;
+// G >= 64: the group's first wavefront writes slot w / (G / 32), the others
+// nothing.  The words are wavefront-uniform (scalar registers).
+template <bool TWO>
+struct SkipOut {
+  uint32_t* out;  // the wavefront's first slot; null: nothing to write
+  int second;     // words from the first slot to the second (G = 16), else 0
+  uint32_t w0, w1;
+  __device__ void init(uint32_t* bits, int row, int w, int G, int words) {
+    out = nullptr;
+    second = G == 16 ? words : 0;
+    w0 = w1 = 0;
+    if (!bits) return;
+    uint32_t* base = bits + (size_t)row * (128 / G) * words;
+    if (G == 16) out = base + (size_t)(2 * w) * words;
+    else if (G == 32) out = base + (size_t)w * words;
+    else if ((w & ((G >> 5) - 1)) == 0) out = base + (size_t)(w >> (G == 64 ? 1 : 2)) * words;
+  }
+  // the final decision on list entry t (of cnt): `need` for the group, or
+  // (TWO) a half split (half_split) when the halves differ
+  __device__ void put(int t, int cnt, bool need, uint32_t split, int lane) {
+    if (!out) return;
+    bool s0 = !need, s1 = !need;  // skipped: rows 0-15, rows 16-31
+    if (TWO && split) {
+      s0 = split == 2u;
+      s1 = split == 1u;
+    }
+    w0 |= (s0 ? 1u : 0u) << (t & 31);
+    if (TWO) w1 |= (s1 ? 1u : 0u) << (t & 31);
+    if ((t & 31) == 31 || t + 1 == cnt) {
+      if (lane == 0) {
+        out[t >> 5] = w0;
+        if (TWO && second) out[second + (t >> 5)] = w1;
+      }
+      w0 = w1 = 0;
+    }
+  }
+};
+
+// Skip-group handling compiled into a forward kernel: one wavefront per
+// group (G = 32), half wavefronts (G = 16), or several wavefronts (G = 64,
+// 128; the count is a launch argument).
+enum GroupMode { kGroupWave = 0, kGroupHalf = 1, kGroupMulti = 2 };
+inline int group_mode(int G) { return G == 16 ? kGroupHalf : (G > 32 ? kGroupMulti : kGroupWave); }
+
 // The query block a workgroup runs.
 // * Default: consecutive ids stay on one XCD and one head (xcd_remap), so
 //   each XCD works through whole heads and the head's K and V are shared in
@@ -75,6 +171,7 @@ struct AttnArgs {
   int o_fp32;   // O stored as fp32
   int recall_on;  // recall skip rule instead of lambda
   float omr;      // 1 - recall
+  int G;          // rows per skip group: 16, 32, 64 or 128
 };
 
 template <typename T, int D>
@@ -126,6 +223,7 @@ inline AttnArgs make_args(const ForwardLaunch& f) {
   a.recall_on = f.recall_on;
   a.omr = 1.0f - f.recall;
   if (a.recall_on) a.lam_off = 1;
+  a.G = f.group_rows;
   return a;
 }
 

@@ -55,9 +55,14 @@ struct Soft {
 template <int I>
 using Int = std::integral_constant<int, I>;
 
-template <int D, bool CAUSAL, bool VOTE>
+template <int D, bool CAUSAL, bool VOTE, int GM>
 __global__ __launch_bounds__(256, 2) void attn_pipe_kernel(AttnArgs a) {
   static_assert(!(CAUSAL && VOTE), "the V vote is a non-causal schedule");
+  // skip groups: SPLIT = halves of a wavefront (G = 16); MULTI = several
+  // wavefronts (G = 64, 128), whose decision in the plain schedule is final
+  // only after the barrier that follows the wavefronts' votes (DEFER)
+  constexpr bool SPLIT = GM == kGroupHalf, MULTI = GM == kGroupMulti;
+  constexpr bool DEFER = MULTI && !VOTE;
   using TL = Tile<__bf16, D>;
   constexpr int RB = TL::RB, TB = TL::TBYTES;
   constexpr int NI = TB / 4096;  // DMA wave-instructions per tile per wave
@@ -68,8 +73,10 @@ __global__ __launch_bounds__(256, 2) void attn_pipe_kernel(AttnArgs a) {
   __shared__ __align__(16) char k1[TB];
   __shared__ __align__(16) char v0[TB];
   __shared__ __align__(16) char v1[TB];
-  // per tile parity and wavefront: 1 if the wavefront multiplies the tile's
-  // P.V (lambda rule, VOTE kernels); a tile no wavefront needs gets no V
+  // per tile parity and wavefront: 1 if the wavefront needs the tile's P.V.
+  // VOTE kernels publish the lambda decision one step early, and a tile no
+  // wavefront needs gets no V; groups of G > 32 rows decide by OR-ing their
+  // wavefronts' votes (published before a barrier)
   __shared__ __align__(16) uint32_t vote[2][4];
   auto kst = [&](auto s) -> char* {
     if constexpr (decltype(s)::value % 2 == 0) return k0;
@@ -117,9 +124,8 @@ __global__ __launch_bounds__(256, 2) void attn_pipe_kernel(AttnArgs a) {
   auto entry_key = [&](int e) {  // key of entry e < wbase + 64, or N past the list
     return e < cnt ? key_of(__builtin_amdgcn_readlane(win, e - wbase)) : a.N;
   };
-  uint32_t* skip_out =
-      a.skip_bits ? a.skip_bits + ((size_t)wg * 4 + w) * a.skip_words : nullptr;
-  uint32_t skip_word = 0;
+  SkipOut<SPLIT> skip_out;
+  skip_out.init(a.skip_bits, wg, w, a.G, a.skip_words);
 
   // buffer resources for K and V of this head (rows >= N read as zero)
   const uint32_t span = (uint32_t)((int64_t)(a.N - 1) * row_bytes + D * 2);
@@ -190,6 +196,8 @@ __global__ __launch_bounds__(256, 2) void attn_pipe_kernel(AttnArgs a) {
   for (int c = 0; c < 4; ++c) pf[c] = u32x4{0u, 0u, 0u, 0u};
   Soft ss{-INFINITY, 0.f, 1.f, 1.f, 0.f};
   bool pv_prev = false;
+  float pend_E = 0.f;     // DEFER, recall rule: the row's energy in the tile awaiting its vote
+  uint32_t sp_new = 0;    // SPLIT: the half split of the latest scalar part
   // VOTE kernels (chosen by the host for non-causal calls whose K and V
   // would stream from HBM; they also take the windowed workgroup order)
   // vote on each tile's V transfer: the lambda decision is known once
@@ -210,16 +218,7 @@ __global__ __launch_bounds__(256, 2) void attn_pipe_kernel(AttnArgs a) {
     // a select per score, not a branch: this file is built with SimplifyCFG's
     // sinking and hoisting off, which would leave `if (!ok)` as one branch per
     // score (a third more code; 4 % slower on the video workload)
-    if (need_mask) {
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = key0 + 32 * kt + 8 * (r >> 2) + 4 * hh + (r & 3);
-          const bool ok = qvalid && key < a.N && (!CAUSAL || key <= qrow);
-          s[kt][r] = ok ? s[kt][r] : -INFINITY;
-        }
-    }
+    if (need_mask) mask_scores<CAUSAL>(s, key0, a.N, hh, qrow, qvalid);
     float mloc = -INFINITY;
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
@@ -228,7 +227,12 @@ __global__ __launch_bounds__(256, 2) void attn_pipe_kernel(AttnArgs a) {
     mloc = xhalf_max(mloc) * a.c2;
     const float mnew = fmaxf(ss.m, mloc);
     bool do_pv = true;
-    if (!a.lam_off) do_pv = __any((mloc != -INFINITY) && (mloc - mnew >= a.lam2));
+    sp_new = 0u;
+    if (!a.lam_off) {
+      const bool nl = (mloc != -INFINITY) && (mloc - mnew >= a.lam2);
+      do_pv = wave_need(nl);
+      if constexpr (SPLIT) sp_new = half_split(nl);
+    }
     if (__any(mnew != ss.m)) {
       // 0 when m was -inf (nothing accumulated yet), 1 where m did not move
       const float f = (mnew == ss.m) ? 1.f : __builtin_amdgcn_exp2f(ss.m - mnew);
@@ -239,6 +243,26 @@ __global__ __launch_bounds__(256, 2) void attn_pipe_kernel(AttnArgs a) {
     }
     if (vote_on && lane == 0) vote[u & 1][w] = do_pv ? 1u : 0u;
     return do_pv;
+  };
+
+  // the final decision on entry tt (SPLIT: with its half split): the recall
+  // rule's dropped energy, the zero P of a skipping half wavefront, the skip
+  // bits, and whether the next step multiplies the tile's P.V
+  auto finish = [&](int tt, bool nd, uint32_t split, float E) {
+    if constexpr (SPLIT) {
+      const bool keep = split ? split_keeps(split, l32) : nd;
+      if (a.recall_on && !keep) ss.drop += E;
+      if (split) {  // the skipping half's rows multiply a zero P (acc + 0 = acc)
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) pf[c][e] = keep ? pf[c][e] : 0u;
+      }
+    } else {
+      if (a.recall_on && !nd) ss.drop += E;
+    }
+    skip_out.put(tt, cnt, nd, split, lane);
+    pv_prev = nd;
   };
 
   int kq0 = entry_key(0), kq1 = entry_key(1);  // keys of entries t, t + 1
@@ -255,7 +279,11 @@ __global__ __launch_bounds__(256, 2) void attn_pipe_kernel(AttnArgs a) {
     for (int kk = 0; kk < NKK; ++kk) sA[kt] = qk_mfma(kst(Int<0>{}), kt, kk, sA[kt]);
   }
   bool dpv_next = true;  // the lambda decision of the next tile (VOTE kernels)
-  if (VOTE && cnt > 0) dpv_next = scalar_part(sA, kq0, 0);
+  uint32_t dsp_next = 0u;
+  if (VOTE && cnt > 0) {
+    dpv_next = scalar_part(sA, kq0, 0);
+    dsp_next = sp_new;
+  }
   __syncthreads();  // stage 0 of K is refilled in iteration 0; entry 0's vote
 
   // one pipeline step for entry t with phase PH = t % 2
@@ -286,8 +314,17 @@ __global__ __launch_bounds__(256, 2) void attn_pipe_kernel(AttnArgs a) {
       if (need_v) dma(vrs, dv0, v_free, key_cur);
     };
 
+    if constexpr (DEFER) {
+      if (t > 0) finish(t - 1, group_need(vote[(t - 1) & 1], w, a.G), 0u, pend_E);
+    }
     bool do_pv = dpv_next;  // the lambda decision of tile t
-    if constexpr (!VOTE) do_pv = scalar_part(sc, key_cur, t);
+    uint32_t split = dsp_next;
+    if constexpr (!VOTE) {
+      do_pv = scalar_part(sc, key_cur, t);
+      split = sp_new;
+    } else if constexpr (MULTI) {
+      if (vote_on) do_pv = group_need(vote[t & 1], w, a.G);
+    }
     if (__any(ss.resc_a != 1.f)) {  // m grew at t - 1
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt)
@@ -350,23 +387,25 @@ __global__ __launch_bounds__(256, 2) void attn_pipe_kernel(AttnArgs a) {
     ss.l += psum;
 #pragma unroll
     for (int c = 0; c < 4; ++c) pf[c] = pn[c];
-    if (a.recall_on) {  // drop the tile if every row's dropped share stays <= 1 - recall
-      const float E = xhalf_sum(psum), L = xhalf_sum(ss.l);
-      do_pv = __any(!(ss.drop + E <= a.omr * L));
-      if (!do_pv) ss.drop += E;
+    float E = 0.f;
+    if (a.recall_on) {  // drop the tile if the rows' dropped share stays <= 1 - recall
+      E = xhalf_sum(psum);
+      const bool nl = !(ss.drop + E <= a.omr * xhalf_sum(ss.l));
+      do_pv = wave_need(nl);
+      if constexpr (SPLIT) split = half_split(nl);
     }
-
-    if (skip_out) {
-      skip_word |= (do_pv ? 0u : 1u) << (t & 31);
-      if ((t & 31) == 31 || t + 1 == cnt) {
-        if (lane == 0) skip_out[t >> 5] = skip_word;
-        skip_word = 0;
-      }
+    if constexpr (DEFER) {
+      if (lane == 0) vote[t & 1][w] = do_pv ? 1u : 0u;
+      pend_E = E;
+    } else {
+      finish(t, do_pv, split, E);
     }
-    pv_prev = do_pv;
     kq0 = kq1;
     kq1 = key_far;
-    if (VOTE && t + 1 < cnt) dpv_next = scalar_part(sn, kq0, t + 1);
+    if (VOTE && t + 1 < cnt) {
+      dpv_next = scalar_part(sn, kq0, t + 1);
+      dsp_next = sp_new;
+    }
     // the DMA issued above is what iteration t + 1 reads; the vote on its V
     __syncthreads();
   };
@@ -379,6 +418,7 @@ __global__ __launch_bounds__(256, 2) void attn_pipe_kernel(AttnArgs a) {
   if (t < cnt) step(Int<0>{}, t, sA, sB);
 
   if (cnt > 0) {
+    if constexpr (DEFER) finish(cnt - 1, group_need(vote[(cnt - 1) & 1], w, a.G), 0u, pend_E);
     if (__any(ss.resc_a != 1.f)) {
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt)
@@ -425,27 +465,40 @@ __global__ __launch_bounds__(256, 2) void attn_pipe_kernel(AttnArgs a) {
 // the windowed order -11.8 % (lambda = -5) and -15.3 % (lambda = -inf).  At
 // N = 32760 (134 MB, cache-resident either way) the variant measured
 // between -2 % and +1.6 % on different boxes, so the plain kernel stays.
+// The recall rule with groups of several wavefronts decides after each
+// tile's region, too late for the VOTE schedule's early vote: such calls
+// run the plain schedule.
 bool vote_pays(const ForwardLaunch& f) {
   const int64_t heads = std::min<int64_t>(8, (int64_t)f.g.B * f.g.H);
+  if (f.recall_on && f.group_rows > 32) return false;
   return !f.causal && heads * 2 * f.g.N * (int64_t)f.g.D * 2 > (int64_t)256 << 20;
 }
 
-template <int D>
+template <int D, int GM>
 hipError_t launch_pipe_t(const ForwardLaunch& f, hipStream_t s) {
   const AttnArgs a = make_args(f);
   if (f.causal)
-    hipLaunchKernelGGL((attn_pipe_kernel<D, true, false>), dim3(a.nwg), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((attn_pipe_kernel<D, true, false, GM>), dim3(a.nwg), dim3(256), 0, s, a);
   else if (vote_pays(f))
-    hipLaunchKernelGGL((attn_pipe_kernel<D, false, true>), dim3(a.nwg), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((attn_pipe_kernel<D, false, true, GM>), dim3(a.nwg), dim3(256), 0, s, a);
   else
-    hipLaunchKernelGGL((attn_pipe_kernel<D, false, false>), dim3(a.nwg), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((attn_pipe_kernel<D, false, false, GM>), dim3(a.nwg), dim3(256), 0, s, a);
   return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_pipe_d(const ForwardLaunch& f, hipStream_t s) {
+  switch (group_mode(f.group_rows)) {
+    case kGroupHalf: return launch_pipe_t<D, kGroupHalf>(f, s);
+    case kGroupMulti: return launch_pipe_t<D, kGroupMulti>(f, s);
+    default: return launch_pipe_t<D, kGroupWave>(f, s);
+  }
 }
 
 }  // namespace
 
 hipError_t launch_attn_pipe(const ForwardLaunch& f, hipStream_t s) {
-  return f.g.D == 128 ? launch_pipe_t<128>(f, s) : launch_pipe_t<64>(f, s);
+  return f.g.D == 128 ? launch_pipe_d<128>(f, s) : launch_pipe_d<64>(f, s);
 }
 
 }  // namespace sa

@@ -156,6 +156,7 @@ struct AttnQArgs {
   int o_fp32;
   int recall_on;  // recall skip rule instead of lambda
   float omr;      // 1 - recall
+  int G;          // rows per skip group: 16, 32, 64 or 128
 };
 
 typedef __attribute__((address_space(3))) void lds_void_q;
@@ -172,14 +173,21 @@ typedef int i32x8 __attribute__((ext_vector_type(8)));
 // factor 2^8 is folded into the exponent and into l: O = acc / l and lse are
 // unchanged.  P.V uses v_mfma_f32_32x32x64_f8f6f4 (all 64 keys of a tile in
 // one MFMA per 32 d-rows); each tile's product is added as acc += s_v * tmp.
-template <bool CAUSAL>
+template <bool CAUSAL, int GM>
 __global__ __launch_bounds__(256, 2) void attn_q_kernel(AttnQArgs a) {
+  // skip groups: SPLIT = halves of a wavefront (G = 16); DEFER = several
+  // wavefronts (G = 64, 128), final after the barrier that follows the votes
+  constexpr bool SPLIT = GM == attn::kGroupHalf, DEFER = GM == attn::kGroupMulti;
   constexpr int TK = 64 * D;  // K codes of a tile, 8 KiB
   constexpr int TV = D * 64;  // V^T codes of a tile, 8 KiB
   __shared__ __align__(16) char k0[TK];
   __shared__ __align__(16) char k1[TK];
   __shared__ __align__(16) char v0[TV];
   __shared__ __align__(16) char v1[TV];
+  // per tile parity and wavefront: 1 if the wavefront needs the tile's P.V;
+  // groups of G > 32 rows OR their wavefronts' votes, published before the
+  // barrier that ends the step
+  __shared__ __align__(16) uint32_t vote[2][4];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -217,9 +225,8 @@ __global__ __launch_bounds__(256, 2) void attn_q_kernel(AttnQArgs a) {
     const int j = __builtin_amdgcn_readlane(win, e - wbase);
     return (unsigned)j < (unsigned)a.nkb ? j : a.nkb;
   };
-  uint32_t* skip_out =
-      a.skip_bits ? a.skip_bits + ((size_t)wg * 4 + w) * a.skip_words : nullptr;
-  uint32_t skip_word = 0;
+  attn::SkipOut<SPLIT> skip_out;
+  skip_out.init(a.skip_bits, wg, w, a.G, a.skip_words);
 
   // K codes of the head: rows >= N read as zero; V^T codes: block nkb (an
   // empty tile) reads as zero
@@ -295,6 +302,24 @@ __global__ __launch_bounds__(256, 2) void attn_q_kernel(AttnQArgs a) {
   float m = -INFINITY, l = 0.f, rescale = 1.f, vsc_prev = 0.f;
   float drop = 0.f;  // recall rule: energy the row has dropped, same scale as l
   bool pv_prev = false;
+  float pend_E = 0.f;  // recall rule, G > 32: the row's energy in the tile awaiting its vote
+  // the final decision on entry tt (for G = 16 with a half split): dropped
+  // energy (recall rule), zero P codes of a skipping half wavefront, skip
+  // bits, and whether the next step multiplies the tile's P.V
+  auto finish = [&](int tt, bool nd, uint32_t split, float E) {
+    if constexpr (SPLIT) {
+      const bool keep = split ? attn::split_keeps(split, l32) : nd;
+      if (a.recall_on && !keep) drop += E;
+      if (split) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pf[e] = keep ? pf[e] : 0;
+      }
+    } else {
+      if (a.recall_on && !nd) drop += E;
+    }
+    skip_out.put(tt, cnt, nd, split, lane);
+    pv_prev = nd;
+  };
 
   int jq0 = entry_blk(0), jq1 = entry_blk(1);  // blocks of entries t, t + 1
 
@@ -326,6 +351,9 @@ __global__ __launch_bounds__(256, 2) void attn_q_kernel(AttnQArgs a) {
     const int j_far = entry_blk(t + 2);
     // K(t+2) into the stage of K(t); V(t) into the stage of V(t-2)
     dma(k_free, j_far, v_free, jq0);
+    if constexpr (DEFER) {
+      if (t > 0) finish(t - 1, attn::group_need(vote[(t - 1) & 1], w, a.G), 0u, pend_E);
+    }
     const int j_cur = jq0;
     const int key_cur = j_cur < a.nkb ? j_cur * 64 : a.N;
     const float csc = j_cur < a.nkb ? cq * skp[j_cur] : 0.f;
@@ -350,16 +378,7 @@ __global__ __launch_bounds__(256, 2) void attn_q_kernel(AttnQArgs a) {
     // a select per score, not a branch: this file is built with SimplifyCFG's
     // sinking and hoisting off, which would leave `if (!ok)` as one branch per
     // score (a third more code)
-    if (need_mask) {
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = key_cur + 32 * kt + 8 * (r >> 2) + 4 * hh + (r & 3);
-          const bool ok = qvalid && key < a.N && (!CAUSAL || key <= qrow);
-          x[kt][r] = ok ? x[kt][r] : -INFINITY;
-        }
-    }
+    if (need_mask) attn::mask_scores<CAUSAL>(x, key_cur, a.N, hh, qrow, qvalid);
     float xmax = -INFINITY;
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
@@ -370,7 +389,12 @@ __global__ __launch_bounds__(256, 2) void attn_q_kernel(AttnQArgs a) {
     const float mloc = xmax * csc;
     const float mnew = fmaxf(m, mloc);
     bool do_pv = true;
-    if (!a.lam_off) do_pv = __any((mloc != -INFINITY) && (mloc - mnew >= a.lam2));
+    uint32_t split = 0u;  // G = 16: the halves of the wavefront decide apart
+    if (!a.lam_off) {
+      const bool nl = (mloc != -INFINITY) && (mloc - mnew >= a.lam2);
+      do_pv = attn::wave_need(nl);
+      if constexpr (SPLIT) split = attn::half_split(nl);
+    }
     if (mnew != m) {
       const float f = (m == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m - mnew);
       l *= f;
@@ -433,20 +457,19 @@ __global__ __launch_bounds__(256, 2) void attn_q_kernel(AttnQArgs a) {
     l += psum;
     pf = pn;
     vsc_prev = vsc;
-    if (a.recall_on) {  // drop the tile if every row's dropped share stays <= 1 - recall
-      const float E = attn::xhalf_sum(psum), L = attn::xhalf_sum(l);
-      do_pv = __any(!(drop + E <= a.omr * L));
-      if (!do_pv) drop += E;
+    float E = 0.f;
+    if (a.recall_on) {  // drop the tile if the rows' dropped share stays <= 1 - recall
+      E = attn::xhalf_sum(psum);
+      const bool nl = !(drop + E <= a.omr * attn::xhalf_sum(l));
+      do_pv = attn::wave_need(nl);
+      if constexpr (SPLIT) split = attn::half_split(nl);
     }
-
-    if (skip_out) {
-      skip_word |= (do_pv ? 0u : 1u) << (t & 31);
-      if ((t & 31) == 31 || t + 1 == cnt) {
-        if (lane == 0) skip_out[t >> 5] = skip_word;
-        skip_word = 0;
-      }
+    if constexpr (DEFER) {
+      if (lane == 0) vote[t & 1][w] = do_pv ? 1u : 0u;
+      pend_E = E;
+    } else {
+      finish(t, do_pv, split, E);
     }
-    pv_prev = do_pv;
     jq0 = jq1;
     jq1 = j_far;
     __syncthreads();
@@ -460,6 +483,8 @@ __global__ __launch_bounds__(256, 2) void attn_q_kernel(AttnQArgs a) {
   if (t < cnt) step(std::integral_constant<int, 0>{}, t, sA, sB);
 
   if (cnt > 0) {
+    if constexpr (DEFER)
+      finish(cnt - 1, attn::group_need(vote[(cnt - 1) & 1], w, a.G), 0u, pend_E);
     if (__any(rescale != 1.f)) {
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt)
@@ -503,6 +528,14 @@ __global__ __launch_bounds__(256, 2) void attn_q_kernel(AttnQArgs a) {
   }
 }
 
+template <int GM>
+void launch_q(const AttnQArgs& a, bool causal, hipStream_t s) {
+  if (causal)
+    hipLaunchKernelGGL((attn_q_kernel<true, GM>), dim3(a.nwg), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL((attn_q_kernel<false, GM>), dim3(a.nwg), dim3(256), 0, s, a);
+}
+
 }  // namespace
 
 hipError_t launch_quant(const ForwardLaunch& f, hipStream_t s) {
@@ -542,10 +575,12 @@ hipError_t launch_attn_q(const ForwardLaunch& f, hipStream_t s) {
   a.recall_on = f.recall_on;
   a.omr = 1.0f - f.recall;
   if (a.recall_on) a.lam_off = 1;
-  if (f.causal)
-    hipLaunchKernelGGL((attn_q_kernel<true>), dim3(a.nwg), dim3(256), 0, s, a);
-  else
-    hipLaunchKernelGGL((attn_q_kernel<false>), dim3(a.nwg), dim3(256), 0, s, a);
+  a.G = f.group_rows;
+  switch (attn::group_mode(f.group_rows)) {
+    case attn::kGroupHalf: launch_q<attn::kGroupHalf>(a, f.causal, s); break;
+    case attn::kGroupMulti: launch_q<attn::kGroupMulti>(a, f.causal, s); break;
+    default: launch_q<attn::kGroupWave>(a, f.causal, s); break;
+  }
   return hipGetLastError();
 }
 

@@ -43,8 +43,8 @@
  *   SA_ERR_HIP reports a failed kernel launch.  No C++ exception crosses the
  *   ABI.  NaN/Inf inside Q, K, V are not checked and propagate.
  * - An empty problem (B, H or N equal to 0) is valid and enqueues nothing.
- * - Supported: D in {64, 128}; block_q = 128, block_k = 64; lambda group of
- *   32 rows (one wavefront's rows); N <= 262144 (4096 key blocks); one
+ * - Supported: D in {64, 128}; block_q = 128, block_k = 64; skip groups of
+ *   16, 32, 64 or 128 rows; N <= 262144 (4096 key blocks); one
  *   head's rows (N + 64) * stride_n elements under 2 GiB.  The
  *   quantised variants need dtype = SA_BF16 and D = 128.  Anything else
  *   returns SA_ERR_UNSUPPORTED.
@@ -117,7 +117,8 @@ typedef struct sa_params {
                                /* invalid                                      */
   float sm_scale;              /* softmax scale; 0 -> 1/sqrt(D)                */
   int32_t keep_prefix_kblocks; /* leading key blocks that are always kept      */
-  int32_t lambda_group_rows;   /* rows per skip group; 0 -> 32; only 32        */
+  int32_t lambda_group_rows;   /* rows G per skip group: 16, 32, 64 or 128;    */
+                               /* 0 -> 32 (one wavefront's rows)               */
   int32_t o_fp32;              /* 1: O is written as fp32 whatever `dtype` is; */
                                /* 0: O has `dtype` (bf16 O = the fp32 result  */
                                /* rounded to nearest even)                    */
@@ -196,7 +197,9 @@ SA_API sa_status sparse_attn_pool(const sa_params* p, const void* q, const void*
 
 /* Stage two.  For each query block, processes mask->kept_idx in list order
  * with an online softmax (running max m, running sum l).  For each group of
- * 32 consecutive rows (one wavefront) and each tile:
+ * G = lambda_group_rows consecutive rows of the block (counted from its
+ * first row; the SpargeAttn abstract's filter reads as a test per
+ * wavefront, G = 32, the default) and each tile:
  *   SA_SKIP_LAMBDA: delta = max over the group's rows of (tile max - new
  *     running max); when delta < lambda the group skips the tile's P.V
  *     product;
@@ -208,10 +211,12 @@ SA_API sa_status sparse_attn_pool(const sa_params* p, const void* q, const void*
  * m and l are updated either way.  Writes
  *   o          [B,H,N,D] dtype (fp32 if o_fp32): acc / l;
  *   lse        optional float [B,H,N]: m + log(l) in natural-log units;
- *   skip_bits  optional uint32 [B,H,NQB,4,ceil(NKB/32)]: bit (t % 32) of
- *              word t / 32 of group g is 1 when group g skipped the P.V
+ *   skip_bits  optional uint32 [B,H,NQB,128/G,ceil(NKB/32)]: bit (t % 32)
+ *              of word t / 32 of group g is 1 when group g skipped the P.V
  *              product of list entry t; only words that cover entries
  *              t < kept_cnt are written, with zero bits past kept_cnt.
+ *              Groups past the last row of a partial block hold no rows
+ *              and read as skipped.
  * Every kept_idx entry must be an admissible key block for its query block
  * (causal) and kept_cnt must lie in [1, NKB]; predict produces such masks.
  * `ws` must hold the forward workspace (none for SA_PREC_NATIVE). */

@@ -167,6 +167,7 @@ class Workload:
     skip_rule: str = "lambda"  # "lambda" or "recall" (stage-two skip rule)
     recall: float = 1.0        # target recall of the "recall" rule
     topk_blocks: int = 0       # budget of the "topk" mask rule
+    group_rows: int = 32       # rows G per skip group of stage two
 
     def head(self, b: int, h: int, n: Optional[int] = None):
         """(Q, K, V) float32 arrays [N, D] for one (b, h), rounded to the

@@ -19,7 +19,7 @@ def to_device(x: np.ndarray, dtype: str):
 def run(Q, K, V, *, dtype="bf16", causal=False, tau=0.95, lam=-5.0, rule="topcdf",
         prec="native", keep_prefix_kblocks=0, sm_scale=0.0, layout="bhnd",
         block_prob=True, want_lse=True, want_skips=True, forward=True,
-        skip_rule="lambda", recall=1.0, topk_blocks=0):
+        skip_rule="lambda", recall=1.0, topk_blocks=0, group_rows=32):
     """Q, K, V: float32 arrays [B, H, N, D] holding dtype-representable values.
     ``layout="bnhd"`` stores the tensors as [B, N, H, D] and passes strides."""
     B, H, N, D = Q.shape
@@ -35,7 +35,8 @@ def run(Q, K, V, *, dtype="bf16", causal=False, tau=0.95, lam=-5.0, rule="topcdf
         views = (q, k, v, o)
     kw = dict(dtype=dtype, causal=causal, tau=tau, lam=lam, rule=rule, prec=prec,
               keep_prefix_kblocks=keep_prefix_kblocks, sm_scale=sm_scale, strides=strides,
-              skip_rule=skip_rule, recall=recall, topk_blocks=topk_blocks)
+              skip_rule=skip_rule, recall=recall, topk_blocks=topk_blocks,
+              lambda_group_rows=group_rows)
     p = sa.make_params(B, H, N, D, **kw)
     p32 = sa.make_params(B, H, N, D, o_fp32=True, **kw)
     nqb, nkb = sa.sparse_attn_mask_shape(p)
@@ -52,7 +53,9 @@ def run(Q, K, V, *, dtype="bf16", causal=False, tau=0.95, lam=-5.0, rule="topcdf
         ws_f = torch.empty(max(fws, 1), dtype=torch.uint8, device=dev)
         lse = torch.full((B, H, N), float("nan"), dtype=torch.float32, device=dev) if want_lse else None
         nw = (nkb + 31) // 32
-        skips = torch.zeros((B, H, nqb, 4, nw), dtype=torch.int32, device=dev) if want_skips else None
+        slots = 128 // group_rows
+        skips = (torch.zeros((B, H, nqb, slots, nw), dtype=torch.int32, device=dev)
+                 if want_skips else None)
         # fp32 O: the computed result, compared with the oracle
         o32 = torch.empty(views[3].shape, dtype=torch.float32, device=dev)
         sa.sparse_attn_forward(p32, views[0], views[1], views[2], mask, o32, lse, skips, ws_f)
@@ -89,7 +92,7 @@ def run(Q, K, V, *, dtype="bf16", causal=False, tau=0.95, lam=-5.0, rule="topcdf
                         c = cnt[b, h, i]
                         t = np.arange(c)
                         bits = (sb[b, h, i][:, t // 32] >> (t % 32).astype(np.uint32)) & 1
-                        per.append(bits.T.astype(bool))  # [c, 4]
+                        per.append(bits.T.astype(bool))  # [c, 128 / G]
                     lists.append(per)
             out["skips"] = lists
         if prec in ("i8fp8", "i4fp8"):

@@ -89,7 +89,8 @@ def test_shapes_and_workspace():
     (dict(tau=float("nan")), sa.SA_ERR_INVALID_ARG),
     (dict(lam=float("nan")), sa.SA_ERR_INVALID_ARG),
     (dict(sm_scale=-1.0), sa.SA_ERR_INVALID_ARG),
-    (dict(lambda_group_rows=16), sa.SA_ERR_UNSUPPORTED),
+    (dict(lambda_group_rows=48), sa.SA_ERR_UNSUPPORTED),
+    (dict(lambda_group_rows=8), sa.SA_ERR_UNSUPPORTED),
     (dict(prec="i8fp8", dtype="f32"), sa.SA_ERR_UNSUPPORTED),
     (dict(prec="i4fp8", D=64), sa.SA_ERR_UNSUPPORTED),
     (dict(prec=3), sa.SA_ERR_INVALID_ARG),

@@ -72,6 +72,12 @@ def decode_skips(bits, cnt):
     ("wan_video", [0, 7], 4, dict(H=8, N=66000, grid=(22, 50, 60))),
     ("wan_video", [3], 4, dict(H=8, N=66000, grid=(22, 50, 60), skip_rule="recall",
                                recall=0.95)),
+    # skip groups of two wavefronts in the V-vote schedule, and the recall rule
+    # over the whole block (which the host runs in the plain schedule)
+    ("wan_video", [2], 4, dict(H=8, N=66000, grid=(22, 50, 60), group_rows=64)),
+    ("wan_video", [6], 4, dict(H=8, N=66000, grid=(22, 50, 60), skip_rule="recall",
+                               recall=0.95, group_rows=128)),
+    ("wan_video", [13], 4, dict(group_rows=16)),
 ])
 def test_fullsize_parity(name, heads, nblocks, over):
     w = dataclasses.replace(make_workload(name), **over)
@@ -84,7 +90,7 @@ def test_fullsize_parity(name, heads, nblocks, over):
     q, k, v = (torch.from_numpy(x).to(tdt).to(dev) for x in (Q, K, V))
     kw = dict(dtype=w.dtype, causal=w.causal, tau=w.tau, lam=w.lam, rule=w.rule, prec=w.prec,
               keep_prefix_kblocks=w.keep_prefix_kblocks, skip_rule=w.skip_rule,
-              recall=w.recall, topk_blocks=w.topk_blocks)
+              recall=w.recall, topk_blocks=w.topk_blocks, lambda_group_rows=w.group_rows)
     p = sa.make_params(w.B, w.H, w.N, w.D, **kw)
     p32 = sa.make_params(w.B, w.H, w.N, w.D, o_fp32=True, **kw)
     nqb, nkb = sa.sparse_attn_mask_shape(p)
@@ -94,7 +100,8 @@ def test_fullsize_parity(name, heads, nblocks, over):
     ws_p = torch.empty(pws, dtype=torch.uint8, device=dev)
     ws_f = torch.empty(max(fws, 1), dtype=torch.uint8, device=dev)
     nw = (nkb + 31) // 32
-    skips = torch.zeros((w.B, w.H, nqb, 4, nw), dtype=torch.int32, device=dev)
+    skips = torch.zeros((w.B, w.H, nqb, 128 // w.group_rows, nw), dtype=torch.int32,
+                        device=dev)
     o32 = torch.empty((w.B, w.H, w.N, w.D), dtype=torch.float32, device=dev)
     o = torch.empty_like(q)
     mask = sa.make_mask(idx, cnt)
@@ -136,7 +143,7 @@ def test_fullsize_parity(name, heads, nblocks, over):
                   keep_prefix_kblocks=w.keep_prefix_kblocks,
                   sm_scale=float(np.float32(1.0 / math.sqrt(w.D))),
                   skip_rule=w.skip_rule, recall=float(np.float32(w.recall)),
-                  topk_blocks=w.topk_blocks)
+                  topk_blocks=w.topk_blocks, G=w.group_rows)
     mode = w.prec if w.prec == "i8fp8" else w.dtype
     if heads is None:
         heads = list(range(w.H))
@@ -158,7 +165,7 @@ def test_fullsize_parity(name, heads, nblocks, over):
             blocks = sorted({0, nqb - 1, *rng.choice(nqb, size=nblocks - 2, replace=False).tolist()})
         sub_kept = [gk[i] if i in blocks else np.zeros(0, dtype=np.int64) for i in range(nqb)]
         gs = [decode_skips(bits_h[0, h, i], cnt_h[0, h, i]) if i in blocks
-              else np.zeros((0, 4), dtype=bool) for i in range(nqb)]
+              else np.zeros((0, 128 // w.group_rows), dtype=bool) for i in range(nqb)]
         deltas = []
         fn = O.sparse_attention_quant_head if w.prec == "i8fp8" else O.sparse_attention_head
         if w.skip_rule == "recall":

@@ -54,16 +54,16 @@ def stacked(w: Workload):
 def check_case(w: Workload, layout="bhnd", check_out=True):
     log(f"[case] {w.name} B={w.B} H={w.H} N={w.N} D={w.D} {w.dtype} causal={w.causal} "
         f"tau={w.tau} lam={w.lam} rule={w.rule} prec={w.prec} kp={w.keep_prefix_kblocks} "
-        f"skip={w.skip_rule}/{w.recall} layout={layout}")
+        f"skip={w.skip_rule}/{w.recall} G={w.group_rows} layout={layout}")
     Q, K, V = stacked(w)
     tau32 = float(np.float32(w.tau))
     lam32 = float(np.float32(w.lam))
     r = gpu_harness.run(Q, K, V, dtype=w.dtype, causal=w.causal, tau=w.tau, lam=w.lam,
                         rule=w.rule, prec=w.prec, keep_prefix_kblocks=w.keep_prefix_kblocks,
                         layout=layout, skip_rule=w.skip_rule, recall=w.recall,
-                        topk_blocks=w.topk_blocks)
+                        topk_blocks=w.topk_blocks, group_rows=w.group_rows)
     p = O.Params(BQ=128, BK=64, causal=w.causal, tau=tau32, lam=lam32, rule=w.rule,
-                 keep_prefix_kblocks=w.keep_prefix_kblocks, G=32,
+                 keep_prefix_kblocks=w.keep_prefix_kblocks, G=w.group_rows,
                  sm_scale=float(np.float32(1.0 / math.sqrt(w.D))),
                  skip_rule=w.skip_rule, recall=float(np.float32(w.recall)),
                  topk_blocks=w.topk_blocks)
@@ -204,6 +204,34 @@ CASES = [
     # lambda = -inf with a real mask: nothing skipped, every kept tile multiplied
     wl("lam_off_field", 128, 1, 2, 1000, 128, grid=(10, 10, 10), tau=0.9, lam=-math.inf),
     wl("lam_off_d64", 129, 2, 1, 515, 64, grid=(5, 103, 1), tau=0.9, lam=-math.inf),
+    # skip groups of 16 rows (half a wavefront), 64 (two) and 128 (the block),
+    # under both skip rules and in every forward kernel
+    wl("g16_field", 130, 1, 2, 1000, 128, grid=(10, 10, 10), tau=0.9, lam=-2.0,
+       group_rows=16),
+    wl("g16_recall_causal", 131, 1, 2, 777, 128, structure="lm", causal=True, tau=0.95,
+       skip_rule="recall", recall=0.9, group_rows=16),
+    wl("g64_field", 132, 2, 1, 1000, 128, grid=(10, 10, 10), tau=0.9, lam=-3.0,
+       group_rows=64),
+    wl("g64_recall", 133, 1, 2, 1000, 128, grid=(10, 10, 10), tau=0.95, skip_rule="recall",
+       recall=0.9, group_rows=64),
+    wl("g128_causal_d64", 134, 1, 2, 555, 64, structure="lm", causal=True, tau=0.9,
+       lam=-3.0, group_rows=128),
+    wl("g128_recall_d64", 135, 1, 2, 515, 64, grid=(5, 103, 1), tau=0.9, skip_rule="recall",
+       recall=0.8, group_rows=128),
+    wl("g16_fp32", 136, 1, 2, 300, 128, dtype="f32", grid=(3, 10, 10), tau=0.9, lam=-2.0,
+       group_rows=16),
+    wl("g64_fp32_recall", 137, 1, 2, 333, 128, dtype="f32", structure="lm", causal=True,
+       tau=0.9, skip_rule="recall", recall=0.9, group_rows=64),
+    wl("g128_fp32_d64", 138, 1, 2, 200, 64, dtype="f32", structure="lm", causal=True,
+       tau=0.95, lam=-2.0, group_rows=128),
+    wl("g16_quant", 139, 1, 2, 1000, 128, grid=(10, 10, 10), tau=0.95, lam=-2.0,
+       rule="energy", prec="i8fp8", group_rows=16),
+    wl("g64_quant_recall", 140, 1, 2, 800, 128, grid=(8, 10, 10), tau=0.9, prec="i8fp8",
+       skip_rule="recall", recall=0.9, group_rows=64),
+    wl("g128_quant4_causal", 141, 1, 1, 700, 128, structure="lm", causal=True, tau=0.9,
+       lam=-3.0, prec="i4fp8", group_rows=128),
+    wl("g16_quant_recall", 142, 1, 2, 800, 128, grid=(8, 10, 10), tau=0.9, prec="i8fp8",
+       skip_rule="recall", recall=0.9, group_rows=16),
 ]
 
 
@@ -244,6 +272,40 @@ def random_cases(n=16, seed=20261203):
 
 
 RANDOM_CASES = random_cases()
+
+
+def random_group_cases(n=8, seed=20261204):
+    """Seeded random cases with skip groups other than one wavefront."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for c in range(n):
+        quant = c % 4 == 3
+        D = 128 if quant else int(rng.choice([64, 128]))
+        dtype = "bf16" if quant else str(rng.choice(["bf16", "bf16", "f32"]))
+        causal = bool(rng.random() < 0.4)
+        N = int(rng.integers(130, 1100))
+        kw = dict(tau=float(rng.choice([0.8, 0.9, 0.95])),
+                  lam=float(rng.choice([-5.0, -2.0, -1.0])),
+                  prec=str(rng.choice(["i8fp8", "i4fp8"])) if quant else "native",
+                  skip_rule=str(rng.choice(["lambda", "recall"])),
+                  recall=float(rng.choice([0.8, 0.9])),
+                  group_rows=int(rng.choice([16, 64, 128])))
+        B, H = int(rng.integers(1, 3)), int(rng.integers(1, 3))
+        if causal:
+            w = wl(f"random_g_{c}", 300 + c, B, H, N, D, dtype=dtype, structure="lm",
+                   causal=True, **kw)
+        else:
+            w = wl(f"random_g_{c}", 300 + c, B, H, N, D, dtype=dtype, grid=(N, 1, 1), **kw)
+        out.append(w)
+    return out
+
+
+RANDOM_GROUP_CASES = random_group_cases()
+
+
+@pytest.mark.parametrize("w", RANDOM_GROUP_CASES, ids=[c.name for c in RANDOM_GROUP_CASES])
+def test_parity_random_groups(w):
+    check_case(w)
 
 
 @pytest.mark.parametrize("w", RANDOM_CASES, ids=[c.name for c in RANDOM_CASES])

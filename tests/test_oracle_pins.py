@@ -216,6 +216,23 @@ def test_sparse_attention_matches_brute(causal, lam):
     assert [s.tolist() for s in sk] == esk
 
 
+@pytest.mark.parametrize("G", [2, 8, 16])
+@pytest.mark.parametrize("causal", [False, True])
+def test_sparse_attention_groups_match_brute(G, causal):
+    """Skip groups of a quarter, the whole and twice the query block (the last
+    is one group per block, as G = 128 with 128-row blocks), against the
+    scalar brute force, on a ragged N."""
+    q, k, v = rand_qkv(12, 37, 3, scale=2.0)
+    p = O.Params(BQ=8, BK=4, causal=causal, tau=0.8, lam=-0.5, G=G)
+    pr = O.predict_head(q, k, p)
+    got, _, sk = O.sparse_attention_head(q, k, v, pr["kept"], p)
+    exp, esk = brute.attention(q.tolist(), k.tolist(), v.tolist(),
+                               [list(x) for x in pr["kept"]], 8, 4, causal, -0.5, G)
+    np.testing.assert_allclose(got, np.array(exp), atol=1e-12, rtol=0)
+    assert [s.tolist() for s in sk] == esk
+    assert all(s.shape[1] == (8 + G - 1) // G for s in sk)
+
+
 def test_sparse_attention_force_skip_matches_brute():
     q, k, v = rand_qkv(11, 40, 3, scale=2.0)
     p = O.Params(BQ=8, BK=4, tau=0.9, lam=-math.inf, G=4)
