@@ -14,6 +14,7 @@ Entry points have the C names:
     sparse_attn_workspace_size(params) -> (predict_bytes, forward_bytes)
     sparse_attn_predict(params, q, k, mask, ws, stream=None)
     sparse_attn_pool(params, q, k, ws, stream=None)
+    sparse_attn_predict_noalloc(params, q, k, mask, stream=None)
     sparse_attn_forward(params, q, k, v, mask, o, lse=None, skip_bits=None,
                         ws=None, stream=None)
     sparse_attn_step(params, schedule, q, k, v, mask, o, lse=None,
@@ -105,6 +106,7 @@ def _load():
         "sparse_attn_workspace_size": [P(SaParams), P(ctypes.c_size_t), P(ctypes.c_size_t)],
         "sparse_attn_predict": [P(SaParams), vp, vp, P(SaMask), vp, ctypes.c_size_t, vp],
         "sparse_attn_pool": [P(SaParams), vp, vp, vp, ctypes.c_size_t, vp],
+        "sparse_attn_predict_noalloc": [P(SaParams), vp, vp, P(SaMask), vp],
         "sparse_attn_forward": [P(SaParams), vp, vp, vp, P(SaMask), vp, vp, vp, vp,
                                 ctypes.c_size_t, vp],
         "sparse_attn_info": [P(ctypes.c_int32), P(ctypes.c_int32)],
@@ -281,6 +283,16 @@ def sparse_attn_predict(p: SaParams, q, k, mask: SaMask, ws, stream=None, ws_byt
                                    _ptr(ws), nb, _stream(stream)), "sparse_attn_predict")
 
 
+def sparse_attn_predict_noalloc(p: SaParams, q, k, mask: SaMask, stream=None):
+    """Stage one with the library's static scratch instead of a caller
+    workspace (for callers that cannot allocate; problems whose predict
+    workspace exceeds 64 MiB are rejected)."""
+    _check_qkv(p, q=q, k=k)
+    _check(lib.sparse_attn_predict_noalloc(ctypes.byref(p), _ptr(q), _ptr(k),
+                                           ctypes.byref(mask), _stream(stream)),
+           "sparse_attn_predict_noalloc")
+
+
 def sparse_attn_pool(p: SaParams, q, k, ws, stream=None, ws_bytes=None):
     """Stage one's block means alone, written to ``ws`` (a predict
     workspace) in its layout: qbar float [B,H,NQB,D] at offset 0, kbar float
@@ -388,7 +400,8 @@ def sparse_attn_permute(p: SaParams, x, perm, inverse, y, stream=None, elem_byte
 __all__ = [
     "SaParams", "SaMask", "SparseAttnError", "make_params", "make_mask",
     "sparse_attn_mask_shape", "sparse_attn_workspace_size", "sparse_attn_predict",
-    "sparse_attn_forward", "sparse_attn_pool", "sparse_attn_info", "sparse_attn_status_str",
+    "sparse_attn_forward", "sparse_attn_pool", "sparse_attn_predict_noalloc",
+    "sparse_attn_info", "sparse_attn_status_str",
     "SaClusterParams", "SaReorder", "make_cluster_params", "make_reorder",
     "sparse_attn_cluster_workspace_size", "sparse_attn_cluster", "sparse_attn_permute",
     "SaSchedule", "make_schedule", "sparse_attn_step",

@@ -6,9 +6,19 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "sa_internal.h"
 #include "../../include/sparse_attn.h"
+
+// Scratch of sparse_attn_predict_noalloc: the predict workspace (the block
+// means) for callers that cannot allocate device memory.  Each GPU the
+// library runs on holds one copy for the life of the process.  Host code
+// never passes this name to a kernel or a copy: on the host it is only a
+// stand-in for the symbol, and each device's address comes from
+// hipGetSymbolAddress (noalloc_scratch below).
+constexpr size_t kNoAllocScratchBytes = size_t(64) << 20;
+static __device__ __align__(256) char scratch[kNoAllocScratchBytes];
 
 namespace {
 
@@ -320,6 +330,59 @@ sa_status sparse_attn_step(const sa_params* p, sa_schedule* sched, const void* q
   sched->refreshed = refresh ? 1 : 0;
   sched->step += 1;
   return ok();
+}
+
+}  // extern "C"
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_dev[kMaxDevices] = {};  // per device: the address of `scratch` there
+
+// The device address of `scratch` on the current device, looked up once per
+// device (with that device current) and kept.
+sa_status noalloc_scratch(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(SA_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(SA_ERR_UNSUPPORTED, "device %d (the no-alloc scratch serves devices 0..%d)", dev,
+                kMaxDevices - 1);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr)
+      return fail(SA_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev,
+                  hipGetErrorString(e));
+    g_scratch_dev[dev] = ptr;
+  }
+  *out = g_scratch_dev[dev];
+  return SA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+sa_status sparse_attn_predict_noalloc(const sa_params* p, const void* q, const void* k,
+                                      const sa_mask* out, void* stream) {
+  sa::Geometry g;
+  bool empty;
+  sa_status st = check_params(p, &g, &empty);
+  if (st) return st;
+  if (empty) return ok();
+  const size_t need = predict_layout(g).total;
+  if (need > kNoAllocScratchBytes)
+    return fail(SA_ERR_WORKSPACE,
+                "sparse_attn_predict_noalloc needs %zu bytes of scratch, more than the %zu of "
+                "its static scratch; call sparse_attn_predict with a workspace",
+                need, kNoAllocScratchBytes);
+  void* ws = nullptr;
+  st = noalloc_scratch(&ws);
+  if (st) return st;
+  return predict_impl(p, q, k, out, ws, kNoAllocScratchBytes, stream, false);
 }
 
 }  // extern "C"

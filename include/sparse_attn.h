@@ -181,6 +181,22 @@ SA_API sa_status sparse_attn_predict(const sa_params* p, const void* q, const vo
                               const sa_mask* out, void* ws, size_t ws_bytes,
                               void* stream);
 
+/* sparse_attn_predict for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same stage one, with the workspace taken from a static
+ * scratch array inside the library (64 MiB per GPU, held until the process
+ * ends; the address of each GPU's copy is looked up once, on the first call
+ * on that device).  The caller still passes Q, K and the mask.  Problems
+ * whose predict workspace (sparse_attn_workspace_size) exceeds 64 MiB are
+ * rejected with SA_ERR_WORKSPACE before anything is enqueued.  The call
+ * allocates nothing.  All calls on one GPU share its scratch: calls that
+ * overlap on one GPU (on different streams, or from different threads
+ * without ordering) race, and the block means of a call are overwritten by
+ * the next one.  Arguments and errors otherwise as for sparse_attn_predict. */
+SA_API sa_status sparse_attn_predict_noalloc(const sa_params* p, const void* q,
+                                             const void* k, const sa_mask* out,
+                                             void* stream);
+
 /* Stage one's first step alone: the block means qbar (query blocks of
  * block_q rows) and kbar (key blocks of block_k rows), written to `ws` in
  * the predict layout (sparse_attn_workspace_size), each the fp32 mean of
