@@ -22,6 +22,7 @@ Entry points have the C names:
     sparse_attn_cluster_workspace_size(params, cluster_params) -> bytes
     sparse_attn_cluster(params, cluster_params, q, k, reorder, ws, stream=None)
     sparse_attn_permute(params, x, perm, inverse, y, stream=None)
+    sparse_attn_check_mask(params, kept_idx_host, kept_cnt_host) -> -1
     sparse_attn_info() -> (default_group_rows, version)
     sparse_attn_status_str(code) -> str
     sparse_attn_last_error() -> str
@@ -34,7 +35,10 @@ import os
 from typing import Optional
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libsparse_attn.so")
+# SA_LIBRARY names another build of the same library (the host-sanitizer
+# build the CPU tests run the boundary checks against); by default the
+# in-tree build
+LIB_PATH = os.environ.get("SA_LIBRARY") or os.path.join(HERE, "libsparse_attn.so")
 HEADER = os.path.join(os.path.dirname(HERE), "include", "sparse_attn.h")
 
 SA_OK, SA_ERR_INVALID_ARG, SA_ERR_UNSUPPORTED, SA_ERR_WORKSPACE, SA_ERR_HIP = range(5)
@@ -107,6 +111,7 @@ def _load():
         "sparse_attn_predict": [P(SaParams), vp, vp, P(SaMask), vp, ctypes.c_size_t, vp],
         "sparse_attn_pool": [P(SaParams), vp, vp, vp, ctypes.c_size_t, vp],
         "sparse_attn_predict_noalloc": [P(SaParams), vp, vp, P(SaMask), vp],
+        "sparse_attn_check_mask": [P(SaParams), vp, vp, P(ctypes.c_int64)],
         "sparse_attn_forward": [P(SaParams), vp, vp, vp, P(SaMask), vp, vp, vp, vp,
                                 ctypes.c_size_t, vp],
         "sparse_attn_info": [P(ctypes.c_int32), P(ctypes.c_int32)],
@@ -259,6 +264,24 @@ def sparse_attn_workspace_size(p: SaParams):
     return a.value, b.value
 
 
+def sparse_attn_check_mask(p: SaParams, kept_idx, kept_cnt):
+    """Checks a mask held in host memory (numpy int32 arrays [B,H,NQB,NKB]
+    and [B,H,NQB]).  Returns -1 when it is valid; raises SparseAttnError
+    naming the first offending row otherwise."""
+    import numpy as np
+    idx = np.ascontiguousarray(kept_idx, dtype=np.int32)
+    cnt = np.ascontiguousarray(kept_cnt, dtype=np.int32)
+    nqb, nkb = sparse_attn_mask_shape(p)
+    rows = max(p.B, 0) * max(p.H, 0) * nqb
+    if idx.size != rows * nkb or cnt.size != rows:
+        raise ValueError(f"mask arrays hold {idx.size} / {cnt.size} entries, expected "
+                         f"{rows * nkb} / {rows}")
+    bad = ctypes.c_int64(-1)
+    _check(lib.sparse_attn_check_mask(ctypes.byref(p), idx.ctypes.data, cnt.ctypes.data,
+                                      ctypes.byref(bad)), "sparse_attn_check_mask")
+    return bad.value
+
+
 def sparse_attn_info():
     g, v = ctypes.c_int32(), ctypes.c_int32()
     _check(lib.sparse_attn_info(ctypes.byref(g), ctypes.byref(v)), "sparse_attn_info")
@@ -401,7 +424,7 @@ __all__ = [
     "SaParams", "SaMask", "SparseAttnError", "make_params", "make_mask",
     "sparse_attn_mask_shape", "sparse_attn_workspace_size", "sparse_attn_predict",
     "sparse_attn_forward", "sparse_attn_pool", "sparse_attn_predict_noalloc",
-    "sparse_attn_info", "sparse_attn_status_str",
+    "sparse_attn_check_mask", "sparse_attn_info", "sparse_attn_status_str",
     "SaClusterParams", "SaReorder", "make_cluster_params", "make_reorder",
     "sparse_attn_cluster_workspace_size", "sparse_attn_cluster", "sparse_attn_permute",
     "SaSchedule", "make_schedule", "sparse_attn_step",

@@ -49,6 +49,34 @@ PER_FILE_FLAGS = {
 }
 
 
+# The host-sanitizer build: the same library with AddressSanitizer and
+# UndefinedBehaviorSanitizer on the host code only (each -fsanitize flag is
+# scoped to the host pass; device code is built as usual), for the CPU tests
+# of the C ABI's host layer.  It needs the compiler's ASan runtime preloaded
+# (asan_runtime()) when loaded into an uninstrumented process.
+SAN_LIB = os.path.join(HERE, "libsparse_attn_san.so")
+SAN_FLAGS = ["-g", "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+             "-Xarch_host", "-fno-omit-frame-pointer", "-Xarch_host", "-fno-sanitize-recover=all"]
+SAN_LINK = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+            "-Xarch_host", "-shared-libsan"]
+
+
+def asan_runtime() -> str:
+    """Path of the compiler's shared ASan runtime (to preload)."""
+    import glob
+    root = os.path.join(os.path.dirname(os.path.dirname(HIPCC)), "lib", "llvm", "lib", "clang")
+    hits = sorted(glob.glob(os.path.join(root, "*", "lib", "linux", "libclang_rt.asan-x86_64.so")))
+    if not hits:
+        raise FileNotFoundError(f"no libclang_rt.asan-x86_64.so under {root}")
+    return hits[-1]
+
+
+def build_sanitized(verbose: bool = False, jobs: int = 8) -> str:
+    """Builds SAN_LIB (host code under ASan + UBSan).  Returns its path."""
+    _build_lib(sources(CSRC), SAN_LIB, verbose, jobs, extra=SAN_FLAGS, link_extra=SAN_LINK)
+    return SAN_LIB
+
+
 def sources(folder=CSRC):
     return sorted(os.path.join(folder, f) for f in os.listdir(folder) if f.endswith(".hip"))
 
@@ -60,15 +88,15 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
     return LIB
 
 
-def _build_lib(srcs, lib, verbose, jobs):
+def _build_lib(srcs, lib, verbose, jobs, extra=(), link_extra=()):
     """Compiles srcs (in parallel) and links them into lib."""
     objdir = tempfile.mkdtemp(prefix="sa_build_")
     try:
         procs, objs = [], []
         for src in srcs:
             obj = os.path.join(objdir, os.path.basename(src) + ".o")
-            cmd = [HIPCC, *FLAGS, *PER_FILE_FLAGS.get(os.path.basename(src), []), "-c", src,
-                   "-o", obj]
+            cmd = [HIPCC, *FLAGS, *PER_FILE_FLAGS.get(os.path.basename(src), []), *extra, "-c",
+                   src, "-o", obj]
             if verbose:
                 print(" ".join(cmd), flush=True)
             procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE,
@@ -79,7 +107,7 @@ def _build_lib(srcs, lib, verbose, jobs):
         for p in procs:
             _wait(p)
         tmp = lib + ".tmp"
-        cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
+        cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *link_extra, "-o", tmp, *objs]
         if verbose:
             print(" ".join(cmd), flush=True)
         out = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)

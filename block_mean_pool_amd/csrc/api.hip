@@ -2,11 +2,14 @@
 // validation, workspace layout, launch of the gfx950 kernels on the caller's
 // stream, and error reporting.  Nothing is enqueued unless every check
 // passes; no exception crosses the ABI.
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <mutex>
+#include <vector>
 
 #include "sa_internal.h"
 #include "../../include/sparse_attn.h"
@@ -163,6 +166,54 @@ sa_status sparse_attn_workspace_size(const sa_params* p, size_t* predict_ws, siz
 
 namespace {
 
+// The mask rules of sparse_attn_check_mask, on host copies of the mask.
+sa_status check_mask_host(const sa::Geometry& g, const sa_params* p, const int32_t* idx,
+                          const int32_t* cnt, int64_t* bad_row) {
+  std::vector<uint8_t> seen(g.nkb);
+  const int64_t rows = (int64_t)g.B * g.H * g.nqb;
+  for (int64_t row = 0; row < rows; ++row) {
+    const int i = (int)(row % g.nqb);
+    const int first_row = i * 128, last_row = std::min(g.N, first_row + 128) - 1;
+    // admissible key blocks: all, or (causal) those whose first key <= last_row
+    const int n_adm = p->causal ? last_row / 64 + 1 : g.nkb;
+    auto forced = [&](int j) {
+      const int last_key = std::min(g.N, j * 64 + 64) - 1;
+      return j < p->keep_prefix_kblocks || (p->causal && last_key >= first_row);
+    };
+    int n_forced = 0;
+    for (int j = 0; j < n_adm; ++j) n_forced += forced(j);
+    if (bad_row) *bad_row = row;
+    const int c = cnt[row];
+    if (c < std::max(1, n_forced) || c > n_adm)
+      return fail(SA_ERR_INVALID_ARG, "mask row %lld: kept_cnt %d outside [%d, %d]",
+                  (long long)row, c, std::max(1, n_forced), n_adm);
+    std::fill(seen.begin(), seen.end(), 0);
+    const int32_t* lst = idx + row * g.nkb;
+    for (int t = 0; t < c; ++t) {
+      const int j = lst[t];
+      if (j < 0 || j >= n_adm)
+        return fail(SA_ERR_INVALID_ARG, "mask row %lld entry %d: key block %d not admissible",
+                    (long long)row, t, j);
+      if (seen[j]) return fail(SA_ERR_INVALID_ARG, "mask row %lld: key block %d repeated",
+                               (long long)row, j);
+      seen[j] = 1;
+      if (forced(j) != (t < n_forced))
+        return fail(SA_ERR_INVALID_ARG, "mask row %lld entry %d: the %d forced blocks do not "
+                    "come first", (long long)row, t, n_forced);
+    }
+  }
+  if (bad_row) *bad_row = -1;
+  return SA_OK;
+}
+
+// Opt-in validation of the mask forward receives: with the environment
+// variable SA_CHECK_MASK set to 1, forward copies the mask to the host (a
+// synchronisation on the stream) and checks it before any launch.
+bool check_mask_requested() {
+  const char* e = std::getenv("SA_CHECK_MASK");
+  return e && e[0] == '1';
+}
+
 // predict / forward with a dry-run mode that validates everything and
 // enqueues nothing (so a composite call can check all of its parts first).
 // pool_only: stage one's block means alone (no mask arguments).
@@ -242,6 +293,20 @@ sa_status forward_impl(const sa_params* p, const void* q, const void* k, const v
   a.group_rows = p->lambda_group_rows ? p->lambda_group_rows : kDefaultGroupRows;
   a.o_fp32 = p->o_fp32 || p->dtype == SA_F32;
   if (dry) return ok();
+  if (check_mask_requested()) {
+    const size_t rows = (size_t)g.B * g.H * g.nqb;
+    std::vector<int32_t> hidx(rows * g.nkb), hcnt(rows);
+    hipStream_t cs = static_cast<hipStream_t>(stream);
+    hipError_t e = hipMemcpyAsync(hcnt.data(), mask->kept_cnt, rows * sizeof(int32_t),
+                                  hipMemcpyDeviceToHost, cs);
+    if (e == hipSuccess)
+      e = hipMemcpyAsync(hidx.data(), mask->kept_idx, hidx.size() * sizeof(int32_t),
+                         hipMemcpyDeviceToHost, cs);
+    if (e == hipSuccess) e = hipStreamSynchronize(cs);
+    if (e != hipSuccess) return fail(SA_ERR_HIP, "mask check copy: %s", hipGetErrorString(e));
+    st = check_mask_host(g, p, hidx.data(), hcnt.data(), nullptr);
+    if (st) return st;
+  }
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e;
   if (p->prec != SA_PREC_NATIVE) {
@@ -548,6 +613,19 @@ sa_status sparse_attn_permute(const sa_params* p, const void* x, const int32_t* 
   hipError_t e = sa::launch_permute(a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(SA_ERR_HIP, "permute launch: %s", hipGetErrorString(e));
   return ok();
+}
+
+sa_status sparse_attn_check_mask(const sa_params* p, const int32_t* kept_idx,
+                                 const int32_t* kept_cnt, int64_t* bad_row) {
+  if (bad_row) *bad_row = -1;
+  sa::Geometry g;
+  bool empty;
+  sa_status st = check_params(p, &g, &empty);
+  if (st) return st;
+  if (empty) return ok();
+  if (!kept_idx || !kept_cnt) return fail(SA_ERR_INVALID_ARG, "kept_idx or kept_cnt is NULL");
+  st = check_mask_host(g, p, kept_idx, kept_cnt, bad_row);
+  return st ? st : ok();
 }
 
 sa_status sparse_attn_info(int32_t* default_group_rows, int32_t* version) {

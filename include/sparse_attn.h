@@ -357,6 +357,22 @@ SA_API sa_status sparse_attn_permute(const sa_params* p, const void* x, const in
                                      int32_t inverse, int32_t elem_bytes, void* y,
                                      void* stream);
 
+/* Host.  Checks a mask held in host memory (copies of kept_idx
+ * [B,H,NQB,NKB] and kept_cnt [B,H,NQB]) against the rules forward relies on:
+ * for every query block i, kept_cnt in [max(1, |F_i|), |A_i|]; the first
+ * kept_cnt entries distinct admissible key blocks (A_i: all, or under
+ * causality those whose first key is not after the block's last row); the
+ * |F_i| forced blocks (the keep_prefix_kblocks leading blocks, and under
+ * causality the blocks that reach the diagonal) first.  Masks from
+ * sparse_attn_predict pass; the check is for masks built or edited by the
+ * caller.  Returns SA_ERR_INVALID_ARG naming the first offending row (its
+ * flat index [B,H,NQB] in *bad_row, -1 if none; bad_row may be NULL).  With
+ * the environment variable SA_CHECK_MASK=1, sparse_attn_forward and
+ * sparse_attn_step run the same check on their device mask before any
+ * launch (copying it to the host, which synchronises the stream). */
+SA_API sa_status sparse_attn_check_mask(const sa_params* p, const int32_t* kept_idx,
+                                        const int32_t* kept_cnt, int64_t* bad_row);
+
 /* Host.  Library defaults and version (either pointer may be NULL). */
 SA_API sa_status sparse_attn_info(int32_t* default_group_rows, int32_t* version);
 

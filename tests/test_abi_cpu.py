@@ -7,6 +7,7 @@ import ctypes
 import math
 import re
 
+import numpy as np
 import pytest
 
 import block_mean_pool_amd as sa
@@ -283,3 +284,60 @@ def test_cluster_and_permute_pointer_errors():
                            sa.make_reorder(None, None), None, stream=0)
     sa.sparse_attn_permute(sa.make_params(1, 2, 0, 128), None, None, 0, None, stream=0,
                            elem_bytes=2)
+
+
+def _pack(lists, nkb):
+    idx = np.full((len(lists), nkb), -1, dtype=np.int32)
+    cnt = np.zeros(len(lists), dtype=np.int32)
+    for i, lst in enumerate(lists):
+        idx[i, :len(lst)] = lst
+        cnt[i] = len(lst)
+    return idx, cnt
+
+
+@pytest.mark.parametrize("causal,keep", [(False, 0), (True, 0), (False, 2), (True, 1)])
+def test_check_mask_accepts_predicted_masks_and_names_bad_rows(causal, keep):
+    import oracle as O
+    rng = np.random.default_rng(31)
+    N, D = 1000, 64
+    Q, K = (rng.standard_normal((N, D)) for _ in range(2))
+    pred = O.predict_head(Q, K, O.Params(causal=causal, tau=0.9, keep_prefix_kblocks=keep))
+    p = sa.make_params(1, 1, N, D, causal=causal, keep_prefix_kblocks=keep)
+    nqb, nkb = sa.sparse_attn_mask_shape(p)
+    idx, cnt = _pack(pred["kept"], nkb)
+    assert sa.sparse_attn_check_mask(p, idx, cnt) == -1
+    F = pred["forced"]
+    i = nqb - 2
+    lst = [int(x) for x in pred["kept"][i]]
+    nf = int(F[i].sum())
+    adm = pred["adm"][i]
+    bad = {"count zero": (lst[:0], None), "repeat": (lst + [lst[-1]], None),
+           "out of range": (lst[:-1] + [nkb], None), "negative": (lst[:-1] + [-1], None)}
+    if causal:
+        bad["future block"] = (lst[:-1] + [int(np.flatnonzero(~adm)[0])], None)
+        bad["too many"] = (list(np.flatnonzero(adm)) + [int(np.flatnonzero(~adm)[0])], None)
+    if nf >= 1 and len(lst) > nf:
+        bad["forced not first"] = (lst[nf:nf + 1] + lst[:nf] + lst[nf + 1:], None)
+        bad["forced missing"] = ([j for j in lst if not F[i, j]] or lst[nf:], None)
+    for why, (new, _) in bad.items():
+        lists = [list(x) for x in pred["kept"]]
+        lists[i] = new
+        bidx, bcnt = _pack(lists, nkb) if len(new) <= nkb else (None, None)
+        if bidx is None:
+            continue
+        with pytest.raises(sa.SparseAttnError) as e:
+            sa.sparse_attn_check_mask(p, bidx, bcnt)
+        assert e.value.code == sa.SA_ERR_INVALID_ARG, why
+        assert f"row {i}" in sa.sparse_attn_last_error(), why
+
+
+def test_check_mask_rows_count_batch_and_heads():
+    p = sa.make_params(2, 3, 300, 128)
+    nqb, nkb = sa.sparse_attn_mask_shape(p)
+    idx = np.tile(np.arange(nkb, dtype=np.int32), (2, 3, nqb, 1))
+    cnt = np.full((2, 3, nqb), nkb, dtype=np.int32)
+    assert sa.sparse_attn_check_mask(p, idx, cnt) == -1
+    cnt[1, 2, 1] = 0  # the last row of the last head of the second batch
+    with pytest.raises(sa.SparseAttnError):
+        sa.sparse_attn_check_mask(p, idx, cnt)
+    assert f"row {1 * 3 * nqb + 2 * nqb + 1}" in sa.sparse_attn_last_error()

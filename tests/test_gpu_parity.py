@@ -423,3 +423,34 @@ def test_pool_entry_point_matches_predict(dtype, D, N):
                                        atol=1e-6)
             np.testing.assert_allclose(kbar[b, hh], O.pool_means(K[b, hh], 64), rtol=1e-5,
                                        atol=1e-6)
+
+
+def test_forward_mask_check_on_request(monkeypatch):
+    """SA_CHECK_MASK=1: forward copies its device mask to the host and
+    refuses a mask that breaks the rules before any launch; a predicted mask
+    passes and gives the same output as without the check."""
+    import block_mean_pool_amd as sa
+    w = Workload("mask_check", 503, 1, 2, 1000, 128, "bf16", structure="lm", causal=True,
+                 tau=0.9)
+    log("[case] forward mask check on request")
+    Q, K, V = w.tensors()
+    q, k, v = (gpu_harness.to_device(x, "bf16") for x in (Q, K, V))
+    p = sa.make_params(w.B, w.H, w.N, w.D, causal=True, tau=0.9, lam=-5.0)
+    nqb, nkb = sa.sparse_attn_mask_shape(p)
+    pws, _ = sa.sparse_attn_workspace_size(p)
+    idx = torch.full((1, w.H, nqb, nkb), -1, dtype=torch.int32, device="cuda")
+    cnt = torch.zeros((1, w.H, nqb), dtype=torch.int32, device="cuda")
+    mask = sa.make_mask(idx, cnt)
+    sa.sparse_attn_predict(p, q, k, mask, torch.empty(pws, dtype=torch.uint8, device="cuda"))
+    o0, o1 = torch.empty_like(q), torch.empty_like(q)
+    sa.sparse_attn_forward(p, q, k, v, mask, o0)
+    monkeypatch.setenv("SA_CHECK_MASK", "1")
+    sa.sparse_attn_forward(p, q, k, v, mask, o1)
+    torch.cuda.synchronize()
+    assert torch.equal(o0, o1)
+    # query block 0 of head 1 may see key blocks 0 and 1 only: name block 5
+    idx[0, 1, 0, 0] = 5
+    with pytest.raises(sa.SparseAttnError) as e:
+        sa.sparse_attn_forward(p, q, k, v, mask, o1)
+    assert e.value.code == sa.SA_ERR_INVALID_ARG
+    assert f"row {nqb}" in sa.sparse_attn_last_error()
