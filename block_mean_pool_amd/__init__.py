@@ -43,7 +43,7 @@ HEADER = os.path.join(os.path.dirname(HERE), "include", "sparse_attn.h")
 
 SA_OK, SA_ERR_INVALID_ARG, SA_ERR_UNSUPPORTED, SA_ERR_WORKSPACE, SA_ERR_HIP = range(5)
 SA_F32, SA_BF16 = 0, 1
-SA_PREC_NATIVE, SA_PREC_I8_FP8, SA_PREC_I4_FP8 = 0, 1, 2
+SA_PREC_NATIVE, SA_PREC_I8_FP8, SA_PREC_I4_FP8, SA_PREC_I8_MXFP8 = 0, 1, 2, 3
 SA_RULE_TOPCDF, SA_RULE_ENERGY, SA_RULE_TOPK = 0, 1, 2
 SA_SKIP_LAMBDA, SA_SKIP_RECALL = 0, 1
 SA_METRIC_FEATURE, SA_METRIC_INTERACTION = 0, 1
@@ -165,7 +165,8 @@ def make_params(B, H, N, D, *, dtype="bf16", causal=False, tau=0.95, lam=-math.i
     return SaParams(
         B, H, N, D, block_q, block_k, int(bool(causal)),
         {"f32": SA_F32, "bf16": SA_BF16}[dtype] if isinstance(dtype, str) else int(dtype),
-        {"native": SA_PREC_NATIVE, "i8fp8": SA_PREC_I8_FP8, "i4fp8": SA_PREC_I4_FP8}[prec] if isinstance(prec, str) else int(prec),
+        {"native": SA_PREC_NATIVE, "i8fp8": SA_PREC_I8_FP8, "i4fp8": SA_PREC_I4_FP8,
+         "i8mxfp8": SA_PREC_I8_MXFP8}[prec] if isinstance(prec, str) else int(prec),
         {"topcdf": SA_RULE_TOPCDF, "energy": SA_RULE_ENERGY, "topk": SA_RULE_TOPK}[rule]
         if isinstance(rule, str) else int(rule),
         float(tau), float(lam), float(sm_scale), int(keep_prefix_kblocks),

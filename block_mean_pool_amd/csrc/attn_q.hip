@@ -9,6 +9,9 @@
 //         search page reports INT4 attention after token reordering; gfx950
 //         has no INT4 MFMA, so 4-bit codes run on the INT8 one);
 //   V:    one scale per key block = absmax / 448, code = e4m3(x / scale);
+//         or (the power-of-two variant) 2^e with e the smallest integer such
+//         that absmax <= 448 * 2^e, the E8M0 block scale of the OCP
+//         microscaling formats, which the scaled MFMA applies in hardware;
 //   P:    e4m3(2^8 p), the product rescaled by scale_v * 2^-8; the running
 //         sum l uses the unquantised p.
 //
@@ -106,7 +109,14 @@ __global__ __launch_bounds__(256) void quant_kernel(ForwardLaunch f) {
       }
     }
   } else {
-    const float scale = amax > 0.f ? __fdiv_rn(amax, 448.0f) : 1.0f;
+    float scale = amax > 0.f ? __fdiv_rn(amax, 448.0f) : 1.0f;
+    if (f.v_pow2) {
+      // amax = fr 2^E with fr in [0.5, 1); 448 = 0.875 * 2^9: the smallest
+      // 2^e with amax <= 448 * 2^e is 2^(E - 9) if fr <= 0.875, else 2^(E - 8)
+      int E = 0;
+      const float fr = frexpf(amax, &E);
+      scale = amax > 0.f ? ldexpf(1.0f, fr <= 0.875f ? E - 9 : E - 8) : 1.0f;
+    }
     if (tid == 0) f.sv[bh * g.nkb + blk] = scale;
     // rows ro + 16 it (it < 4) of this key block; transposed into LDS,
     // key k = 32 t + 8 g + 4 h + e at position 32 h + 16 t + 4 g + e: the
@@ -173,8 +183,16 @@ typedef int i32x8 __attribute__((ext_vector_type(8)));
 // factor 2^8 is folded into the exponent and into l: O = acc / l and lse are
 // unchanged.  P.V uses v_mfma_f32_32x32x64_f8f6f4 (all 64 keys of a tile in
 // one MFMA per 32 d-rows); each tile's product is added as acc += s_v * tmp.
-template <bool CAUSAL, int GM>
+//
+// PM (precision mode): 0 = absmax / 448 V scales; 1 and 2 = power-of-two V
+// scales, applied by the scaled MFMA, which then accumulates into acc
+// directly; these modes normalise O by the sum of the quantised weights (the
+// mode's reading), summed by one more scaled MFMA per tile with an all-ones
+// operand instead of 31 adds per lane.  Mode 2 (the recall rule) still sums
+// the unquantised weights on the VALU for the rule's energies.
+template <bool CAUSAL, int GM, int PM>
 __global__ __launch_bounds__(256, 2) void attn_q_kernel(AttnQArgs a) {
+  constexpr bool VP2 = PM != 0, ROWSUM_VALU = PM != 1;
   // skip groups: SPLIT = halves of a wavefront (G = 16); DEFER = several
   // wavefronts (G = 64, 128), final after the barrier that follows the votes
   constexpr bool SPLIT = GM == attn::kGroupHalf, DEFER = GM == attn::kGroupMulti;
@@ -279,6 +297,16 @@ __global__ __launch_bounds__(256, 2) void attn_q_kernel(AttnQArgs a) {
     return __builtin_amdgcn_mfma_i32_32x32x32_i8(__builtin_bit_cast(i32x4, kv),
                                                  __builtin_bit_cast(i32x4, qf[kk]), acc_s, 0, 0, 0);
   };
+  // VP2 (power-of-two V scales): the MFMA applies the V scale (E8M0 = the
+  // fp32 exponent field of 2^e) and accumulates into acc directly
+  auto pv_mfma_acc = [&](const char* vbuf, int dt, const i32x8& pb, f32x16 acc_o,
+                         int vexp) {
+    const u32x4 lo = *reinterpret_cast<const u32x4*>(vbuf + vro0 + 32 * dt * 64);
+    const u32x4 hi = *reinterpret_cast<const u32x4*>(vbuf + vro1 + 32 * dt * 64);
+    const i32x8 va{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                   (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va, pb, acc_o, 0, 0, 0, vexp, 0, 127);
+  };
   auto pv_mfma = [&](const char* vbuf, int dt, const i32x8& pb) {
     const u32x4 lo = *reinterpret_cast<const u32x4*>(vbuf + vro0 + 32 * dt * 64);
     const u32x4 hi = *reinterpret_cast<const u32x4*>(vbuf + vro1 + 32 * dt * 64);
@@ -300,6 +328,13 @@ __global__ __launch_bounds__(256, 2) void attn_q_kernel(AttnQArgs a) {
 #pragma unroll
   for (int e = 0; e < 8; ++e) pf[e] = 0;
   float m = -INFINITY, l = 0.f, rescale = 1.f, vsc_prev = 0.f;
+  int vexp_prev = 0;  // VP2: E8M0 of the previous tile's V scale
+  f32x16 lacc;        // VP2: running sum of the quantised weights (every row alike)
+#pragma unroll
+  for (int r = 0; r < 16; ++r) lacc[r] = 0.f;
+  i32x8 ones;  // e4m3 1.0 in every byte: the all-ones operand of the row sums
+#pragma unroll
+  for (int e = 0; e < 8; ++e) ones[e] = 0x38383838;
   float drop = 0.f;  // recall rule: energy the row has dropped, same scale as l
   bool pv_prev = false;
   float pend_E = 0.f;  // recall rule, G > 32: the row's energy in the tile awaiting its vote
@@ -358,6 +393,7 @@ __global__ __launch_bounds__(256, 2) void attn_q_kernel(AttnQArgs a) {
     const int key_cur = j_cur < a.nkb ? j_cur * 64 : a.N;
     const float csc = j_cur < a.nkb ? cq * skp[j_cur] : 0.f;
     const float vsc = j_cur < a.nkb ? svp[j_cur] : 0.f;
+    const int vexp = (int)(__float_as_uint(vsc) >> 23);  // VP2: 2^e -> e + 127
 
     if (__any(rescale != 1.f)) {  // m grew at t - 1
 #pragma unroll
@@ -401,6 +437,10 @@ __global__ __launch_bounds__(256, 2) void attn_q_kernel(AttnQArgs a) {
       drop *= f;
       rescale = f;
       m = mnew;
+      if constexpr (VP2) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) lacc[r] *= f;
+      }
     }
     // 2^8 P = exp2(csc * x + cb), cb = 8 - m
     const float cb = (m == -INFINITY) ? 0.f : 8.f - m;
@@ -414,9 +454,13 @@ __global__ __launch_bounds__(256, 2) void attn_q_kernel(AttnQArgs a) {
     // chunk c: P.V of tile t-1 for d rows 32c..32c+31, Q.K^T of tile t+1 for
     // kk = c (both key halves), softmax of this lane's scores 8c .. 8c+7
     auto chunk_pv = [&](int c) {
-      const f32x16 tmp = pv_mfma(v_prev, c, pf);
+      if constexpr (VP2) {
+        acc[c] = pv_mfma_acc(v_prev, c, pf, acc[c], vexp_prev);
+      } else {
+        const f32x16 tmp = pv_mfma(v_prev, c, pf);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[c][r] = fmaf(vsc_prev, tmp[r], acc[c][r]);
+        for (int r = 0; r < 16; ++r) acc[c][r] = fmaf(vsc_prev, tmp[r], acc[c][r]);
+      }
     };
     auto chunk_qk = [&](int c) {
       sn[0] = qk_mfma(k_next, 0, c, sn[0]);
@@ -427,7 +471,8 @@ __global__ __launch_bounds__(256, 2) void attn_q_kernel(AttnQArgs a) {
       float p[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) p[e] = __builtin_amdgcn_exp2f(fmaf(x[kt][r0 + e], csc, cb));
-      psum += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+      if constexpr (ROWSUM_VALU)
+        psum += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
       // the first conversion of each word writes its low half; the second
       // overwrites the high half, so the word's old contents do not matter
       int lo, hi;  // defined by empty asm: no instruction, no zeroing move
@@ -456,7 +501,12 @@ __global__ __launch_bounds__(256, 2) void attn_q_kernel(AttnQArgs a) {
     }
     l += psum;
     pf = pn;
+    // VP2: the row sums of this tile's quantised weights (before a half
+    // split zeroes any codes of pf: the skipped mass stays in the sum)
+    if constexpr (VP2)
+      lacc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ones, pn, lacc, 0, 0, 0, 127, 0, 127);
     vsc_prev = vsc;
+    vexp_prev = vexp;
     float E = 0.f;
     if (a.recall_on) {  // drop the tile if the rows' dropped share stays <= 1 - recall
       E = attn::xhalf_sum(psum);
@@ -495,15 +545,20 @@ __global__ __launch_bounds__(256, 2) void attn_q_kernel(AttnQArgs a) {
       const char* vlast = ((cnt - 1) & 1) ? v1 : v0;
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt) {
-        const f32x16 tmp = pv_mfma(vlast, dt, pf);
+        if constexpr (VP2) {
+          acc[dt] = pv_mfma_acc(vlast, dt, pf, acc[dt], vexp_prev);
+        } else {
+          const f32x16 tmp = pv_mfma(vlast, dt, pf);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc[dt][r] = fmaf(vsc_prev, tmp[r], acc[dt][r]);
+          for (int r = 0; r < 16; ++r) acc[dt][r] = fmaf(vsc_prev, tmp[r], acc[dt][r]);
+        }
       }
     }
   }
 
-  // epilogue: O = acc / l (both carry the factor 2^8); lse = (m + log2 l - 8) ln 2
-  l = attn::xhalf_sum(l);
+  // epilogue: O = acc / l (both carry the factor 2^8); lse = (m + log2 l - 8) ln 2;
+  // VP2 normalises by the quantised weights' sum (each lane holds its row's)
+  l = VP2 ? lacc[0] : attn::xhalf_sum(l);
   if (qvalid) {
     const float inv = l > 0.f ? 1.f / l : 0.f;
     const int oe = a.o_fp32 ? 4 : 2;
@@ -528,12 +583,21 @@ __global__ __launch_bounds__(256, 2) void attn_q_kernel(AttnQArgs a) {
   }
 }
 
-template <int GM>
+template <int GM, int PM>
 void launch_q(const AttnQArgs& a, bool causal, hipStream_t s) {
   if (causal)
-    hipLaunchKernelGGL((attn_q_kernel<true, GM>), dim3(a.nwg), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((attn_q_kernel<true, GM, PM>), dim3(a.nwg), dim3(256), 0, s, a);
   else
-    hipLaunchKernelGGL((attn_q_kernel<false, GM>), dim3(a.nwg), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((attn_q_kernel<false, GM, PM>), dim3(a.nwg), dim3(256), 0, s, a);
+}
+
+// precision mode: 0 absmax / 448 V scales; power-of-two V scales with the
+// lambda rule (1) or the recall rule (2)
+template <int GM>
+void launch_q(const AttnQArgs& a, bool causal, bool v_pow2, hipStream_t s) {
+  if (!v_pow2) launch_q<GM, 0>(a, causal, s);
+  else if (a.recall_on) launch_q<GM, 2>(a, causal, s);
+  else launch_q<GM, 1>(a, causal, s);
 }
 
 }  // namespace
@@ -577,9 +641,9 @@ hipError_t launch_attn_q(const ForwardLaunch& f, hipStream_t s) {
   if (a.recall_on) a.lam_off = 1;
   a.G = f.group_rows;
   switch (attn::group_mode(f.group_rows)) {
-    case attn::kGroupHalf: launch_q<attn::kGroupHalf>(a, f.causal, s); break;
-    case attn::kGroupMulti: launch_q<attn::kGroupMulti>(a, f.causal, s); break;
-    default: launch_q<attn::kGroupWave>(a, f.causal, s); break;
+    case attn::kGroupHalf: launch_q<attn::kGroupHalf>(a, f.causal, f.v_pow2, s); break;
+    case attn::kGroupMulti: launch_q<attn::kGroupMulti>(a, f.causal, f.v_pow2, s); break;
+    default: launch_q<attn::kGroupWave>(a, f.causal, f.v_pow2, s); break;
   }
   return hipGetLastError();
 }

@@ -47,6 +47,7 @@ struct ForwardLaunch {
   float recall;              // target recall rho (recall rule)
   int group_rows;            // rows per skip group G: 16, 32, 64 or 128
   int qmax;                  // quantised variant: Q/K code range [-qmax, qmax]
+  int v_pow2;                // quantised variant: power-of-two V scales
   // quantised variant: workspace buffers
   int8_t* qc;                // [B,H,N,D]
   int8_t* kc;                // [B,H,N,D]

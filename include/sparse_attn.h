@@ -83,8 +83,12 @@ enum { SA_F32 = 0, SA_BF16 = 1 };
  * K codes (scale absmax/7, codes in [-7, 7]), the INT4 attention the PARO
  * abstract (huggingface-mirror search page) reports after token
  * reordering; gfx950 has no INT4 MFMA, so the codes run on the INT8 MFMA and
- * the mode changes accuracy, not speed. */
-enum { SA_PREC_NATIVE = 0, SA_PREC_I8_FP8 = 1, SA_PREC_I4_FP8 = 2 };
+ * the mode changes accuracy, not speed.  SA_PREC_I8_MXFP8 is SA_PREC_I8_FP8
+ * with a power-of-two V scale per key block: 2^e with e the smallest integer
+ * such that absmax <= 448 * 2^e (the E8M0 block scale of the OCP
+ * microscaling formats; the pages fix no V scale), V codes e4m3(V / 2^e); the
+ * scaled FP8 MFMA applies it in hardware, so the mode is the faster one. */
+enum { SA_PREC_NATIVE = 0, SA_PREC_I8_FP8 = 1, SA_PREC_I4_FP8 = 2, SA_PREC_I8_MXFP8 = 3 };
 /* Mask rule of stage one.  TOPCDF: P-hat = softmax of the block scores over
  * the admissible key blocks.  ENERGY: P-hat_j proportional to
  * n_j * exp(s_j), n_j the number of keys in block j (a cumulative-energy
@@ -107,7 +111,7 @@ typedef struct sa_params {
   int32_t causal;              /* 1: key c visible to row r only if c <= r     */
   int32_t dtype;               /* SA_F32 | SA_BF16                             */
   int32_t prec;                /* SA_PREC_NATIVE | SA_PREC_I8_FP8 |            */
-                               /* SA_PREC_I4_FP8                               */
+                               /* SA_PREC_I4_FP8 | SA_PREC_I8_MXFP8            */
   int32_t rule;                /* SA_RULE_TOPCDF | SA_RULE_ENERGY |            */
                                /* SA_RULE_TOPK                                 */
   float tau;                   /* cumulative-mass target in (0, 1]; >= 1 keeps */
@@ -153,7 +157,7 @@ SA_API sa_status sparse_attn_mask_shape(const sa_params* p, int64_t* nqb, int64_
  * pointer may be NULL).  Layouts (offsets rounded up to 256 bytes):
  *   predict: qbar float [B,H,NQB,D], then kbar float [B,H,NKB,D] -- the
  *            block means, left in place after the call.
- *   forward, SA_PREC_I8_FP8 and SA_PREC_I4_FP8: Q codes int8 [B,H,N,D], K
+ *   forward, the quantised precisions: Q codes int8 [B,H,N,D], K
  *            codes int8 [B,H,N,D] (in [-7, 7] for SA_PREC_I4_FP8),
  *            V codes e4m3 [B,H,NKB,D,64] (each key block stored transposed,
  *            keys permuted: byte (d, p) of block j holds key

@@ -57,6 +57,8 @@ from .quant import (  # noqa: F401
     int8_quantize_blocks,
     int_quantize_blocks,
     fp8_quantize_v_blocks,
+    pow2_scale,
+    fp8_quantize_v_blocks_pow2,
     sparse_attention_quant_head,
 )
 from .schedule import step_plan, sequence_head, call_tau, dense_params  # noqa: F401

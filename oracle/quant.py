@@ -20,6 +20,17 @@ fix no format, so the readings are:
   with bias 7, 3 mantissa bits, no infinities, largest finite 448, smallest
   normal 2^-6, subnormals k * 2^-9.  Conversion rounds to nearest, ties to
   even, and saturates finite overflow to +-448.
+* V with a power-of-two scale (``v_pow2``, the SA_PREC_I8_MXFP8 mode): the
+  per-key-block scale is 2^e with e the smallest integer such that
+  absmax <= 448 * 2^e (1 when the block is all zero), the E8M0 block scale
+  of the OCP microscaling formats; code = e4m3(x / 2^e), an exact division.
+  The pages fix no V scale, so this is an equally plain reading of "V in FP8
+  e4m3" that the gfx950 scaled MFMA can apply in hardware.  In this mode the
+  output is normalised by the sum of the quantised weights, O = sum of
+  2^-8 e4m3(2^8 P) s_v V~ over sum of 2^-8 e4m3(2^8 P) (kept tiles, skipped
+  P.V included), so O is exactly a weighted average of the quantised V rows
+  with the weights the product uses; the recall rule's energies stay the
+  unquantised P.
 * Stage one (pooling, scores, mask) uses the unquantised inputs.
 * 4-bit Q.K^T (``qmax = 7``): the PARO abstract on the search page reports
   INT4 attention once tokens are reordered.  Reading: the same per-block
@@ -112,22 +123,56 @@ def fp8_quantize_v_blocks(V, bk: int):
     return vals, scales
 
 
+def pow2_scale(amax: float, top: float = 448.0) -> float:
+    """The smallest power of two s = 2^e with amax <= top * s (1 for amax = 0),
+    found by exact comparisons against top * 2^e."""
+    if amax == 0.0:
+        return 1.0
+    _, E = math.frexp(amax / top)
+    e = E
+    while amax <= top * math.ldexp(1.0, e - 1):
+        e -= 1
+    while amax > top * math.ldexp(1.0, e):
+        e += 1
+    return math.ldexp(1.0, e)
+
+
+def fp8_quantize_v_blocks_pow2(V, bk: int):
+    """Per-key-block e4m3 values of V with power-of-two scales (pow2_scale of
+    the block's absmax).  Returns (values float64 on the e4m3 grid [N, d],
+    scales float32 [NKB])."""
+    V = np.asarray(V, dtype=np.float32)
+    N, d = V.shape
+    nb = n_blocks(N, bk)
+    vals = np.zeros((N, d), dtype=np.float64)
+    scales = np.zeros(nb, dtype=np.float32)
+    for b in range(nb):
+        blk = V[b * bk:min(N, (b + 1) * bk)].astype(np.float64)
+        s = pow2_scale(float(np.abs(blk).max()))
+        vals[b * bk:min(N, (b + 1) * bk)] = e4m3_round(blk / s)   # exact division
+        scales[b] = s
+    return vals, scales
+
+
 def sparse_attention_quant_head(Q, K, V, kept: List[np.ndarray], p: Params,
                                 force_skip: Optional[List[np.ndarray]] = None,
-                                deltas: Optional[list] = None, qmax: int = 127):
+                                deltas: Optional[list] = None, qmax: int = 127,
+                                v_pow2: bool = False):
     """Quantised stage two: the same online softmax, processing order and
     skip rule as the unquantised oracle, with
     S = sm * s_q(i) * s_k(j) * (Qcode . Kcode)  (exact integer dot product) and
     the P.V term  s_v(j) * 2^-8 * sum_c e4m3(2^8 * P) * Vcode.
     ``deltas`` collects the group statistics and the skip rule (lambda or
     recall) is applied as in the unquantised oracle.  ``qmax`` = 127 for
-    INT8 Q/K codes, 7 for 4-bit ones.
+    INT8 Q/K codes, 7 for 4-bit ones; ``v_pow2`` takes V's scales from
+    fp8_quantize_v_blocks_pow2 and normalises O (and lse) by the running sum
+    of the quantised weights.
     Returns (O, lse, skips)."""
     N, d = np.asarray(Q).shape
     sm = p.sm(d)
     qc, qs = int_quantize_blocks(Q, p.BQ, qmax)
     kc, ks = int_quantize_blocks(K, p.BK, qmax)
-    vq, vs = fp8_quantize_v_blocks(V, p.BK)
+    vq, vs = (fp8_quantize_v_blocks_pow2 if v_pow2 else fp8_quantize_v_blocks)(V, p.BK)
     qc = qc.astype(np.int64)
     kc = kc.astype(np.int64)
     n_groups = (p.BQ + p.G - 1) // p.G
@@ -139,6 +184,7 @@ def sparse_attention_quant_head(Q, K, V, kept: List[np.ndarray], p: Params,
         nr = len(rows)
         m = np.full(nr, -np.inf)
         l = np.zeros(nr)
+        lq = np.zeros(nr)     # v_pow2: running sum of the quantised weights
         acc = np.zeros((nr, d))
         drop = np.zeros(nr)
         sk = np.zeros((len(lst), n_groups), dtype=bool)
@@ -161,6 +207,7 @@ def sparse_attention_quant_head(Q, K, V, kept: List[np.ndarray], p: Params,
             drop = alpha * drop
             acc = alpha[:, None] * acc
             Pq = e4m3_round(P * 256.0) / 256.0
+            lq = alpha * lq + Pq.sum(axis=1)
             delta_r = np.where(np.isfinite(mloc), mloc - safe, -np.inf)
             for g in range(n_groups):
                 gr = slice(g * p.G, min(nr, (g + 1) * p.G))
@@ -177,11 +224,13 @@ def sparse_attention_quant_head(Q, K, V, kept: List[np.ndarray], p: Params,
         skips.append(sk)
         if deltas is not None:
             deltas.append(dl)
-        ok = l > 0
-        O[rows[ok]] = acc[ok] / l[ok, None]
-        lse[rows[ok]] = m[ok] + np.log(l[ok])
+        ln = lq if v_pow2 else l
+        ok = ln > 0
+        O[rows[ok]] = acc[ok] / ln[ok, None]
+        lse[rows[ok]] = m[ok] + np.log(ln[ok])
     return O, lse, skips
 
 
 __all__ = ["e4m3_round", "e4m3_encode", "int8_quantize_blocks", "int_quantize_blocks",
-           "fp8_quantize_v_blocks", "sparse_attention_quant_head", "math"]
+           "fp8_quantize_v_blocks", "pow2_scale", "fp8_quantize_v_blocks_pow2",
+           "sparse_attention_quant_head", "math"]

@@ -94,10 +94,12 @@ def predict(Q, K, BQ, BK, causal, tau, rule="topcdf", keep_prefix=0, sm=None):
 
 
 def attention(Q, K, V, lists, BQ, BK, causal, lam, G, sm=None,
-              score=None, pv=None, force_skip=None):
+              score=None, pv=None, force_skip=None, weight=None):
     """Online-softmax attention over each query block's list, one row and
     one key at a time.  ``score(r, c)`` and ``pv(r, c, p)`` may override the
-    logit and the P.V contribution (vector over d)."""
+    logit and the P.V contribution (vector over d); ``weight(p)`` what a
+    probability adds to the normaliser of O (p itself by default; the skip
+    rule always sees the plain running sum)."""
     n, d = len(Q), len(Q[0])
     if sm is None:
         sm = 1.0 / math.sqrt(d)
@@ -113,6 +115,7 @@ def attention(Q, K, V, lists, BQ, BK, causal, lam, G, sm=None,
         rows = list(range(i * BQ, min(n, (i + 1) * BQ)))
         m = {r: -math.inf for r in rows}
         l = {r: 0.0 for r in rows}
+        ln = {r: 0.0 for r in rows}   # the normaliser of O
         acc = {r: [0.0] * d for r in rows}
         ngroups = nblk(BQ, G)
         sk_i = []
@@ -134,6 +137,7 @@ def attention(Q, K, V, lists, BQ, BK, causal, lam, G, sm=None,
                 P[r] = {c: (0.0 if S[r][c] == -math.inf else
                             math.exp(S[r][c] - mnew[r])) for c in cols}
                 l[r] = alpha * l[r] + sum(P[r].values())
+                ln[r] = alpha * ln[r] + sum((weight(x) if weight else x) for x in P[r].values())
                 acc[r] = [alpha * a for a in acc[r]]
             flags = []
             for g in range(ngroups):
@@ -156,7 +160,7 @@ def attention(Q, K, V, lists, BQ, BK, causal, lam, G, sm=None,
             sk_i.append(flags)
         skips.append(sk_i)
         for r in rows:
-            O[r] = [a / l[r] for a in acc[r]] if l[r] > 0 else [0.0] * d
+            O[r] = [a / ln[r] for a in acc[r]] if ln[r] > 0 else [0.0] * d
     return O, skips
 
 

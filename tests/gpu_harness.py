@@ -95,7 +95,7 @@ def run(Q, K, V, *, dtype="bf16", causal=False, tau=0.95, lam=-5.0, rule="topcdf
                         per.append(bits.T.astype(bool))  # [c, 128 / G]
                     lists.append(per)
             out["skips"] = lists
-        if prec in ("i8fp8", "i4fp8"):
+        if prec in ("i8fp8", "i4fp8", "i8mxfp8"):
             wf = ws_f.cpu().numpy()
             bh = B * H
             def rup(x):

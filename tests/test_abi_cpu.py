@@ -94,7 +94,9 @@ def test_shapes_and_workspace():
     (dict(lambda_group_rows=8), sa.SA_ERR_UNSUPPORTED),
     (dict(prec="i8fp8", dtype="f32"), sa.SA_ERR_UNSUPPORTED),
     (dict(prec="i4fp8", D=64), sa.SA_ERR_UNSUPPORTED),
-    (dict(prec=3), sa.SA_ERR_INVALID_ARG),
+    (dict(prec=4), sa.SA_ERR_INVALID_ARG),
+    (dict(prec="i8mxfp8", dtype="f32"), sa.SA_ERR_UNSUPPORTED),
+    (dict(prec="i8mxfp8", D=64), sa.SA_ERR_UNSUPPORTED),
     (dict(keep_prefix_kblocks=-1), sa.SA_ERR_INVALID_ARG),
     (dict(N=300000), sa.SA_ERR_UNSUPPORTED),
     (dict(strides=(0, 0, 100)), sa.SA_ERR_INVALID_ARG),

@@ -32,7 +32,7 @@ import oracle as O  # noqa: E402
 from synth import make_workload, round_to_bf16  # noqa: E402
 import compare  # noqa: E402
 
-SKIP_TOL = {"bf16": 1e-3, "f32": 1e-4, "i8fp8": 1e-3}
+SKIP_TOL = {"bf16": 1e-3, "f32": 1e-4, "i8fp8": 1e-3, "i8mxfp8": 1e-3}
 
 
 def log(*a):
@@ -64,6 +64,7 @@ def decode_skips(bits, cnt):
     ("hunyuan_video", [7, 19], 8, {}),
     ("lm_causal", [0, 31], 5, {}),
     ("quant_long", [5], 4, {}),
+    ("quant_long", [12], 4, dict(prec="i8mxfp8")),
     ("wan_video", [11], 4, dict(skip_rule="recall", recall=0.95)),
     ("lm_causal", [9], 4, dict(skip_rule="recall", recall=0.9)),
     # K and V of eight heads (270 MB) exceed the Infinity Cache: the forward
@@ -144,7 +145,7 @@ def test_fullsize_parity(name, heads, nblocks, over):
                   sm_scale=float(np.float32(1.0 / math.sqrt(w.D))),
                   skip_rule=w.skip_rule, recall=float(np.float32(w.recall)),
                   topk_blocks=w.topk_blocks, G=w.group_rows)
-    mode = w.prec if w.prec == "i8fp8" else w.dtype
+    mode = w.prec if w.prec in ("i8fp8", "i8mxfp8") else w.dtype
     if heads is None:
         heads = list(range(w.H))
     rng = np.random.default_rng(7)
@@ -167,7 +168,11 @@ def test_fullsize_parity(name, heads, nblocks, over):
         gs = [decode_skips(bits_h[0, h, i], cnt_h[0, h, i]) if i in blocks
               else np.zeros((0, 128 // w.group_rows), dtype=bool) for i in range(nqb)]
         deltas = []
-        fn = O.sparse_attention_quant_head if w.prec == "i8fp8" else O.sparse_attention_head
+        if mode == "bf16" or mode == "f32":
+            fn = O.sparse_attention_head
+        else:
+            def fn(*args, **kw):
+                return O.sparse_attention_quant_head(*args, v_pow2=w.prec == "i8mxfp8", **kw)
         if w.skip_rule == "recall":
             Oref, _, _ = fn(qh, kh, vh, sub_kept, op, force_skip=gs, deltas=deltas)
             ns, mis, sf = compare.compare_recall_skips([gs[i] for i in blocks],

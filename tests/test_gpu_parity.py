@@ -34,7 +34,8 @@ from synth import Workload, make_workload, round_to_bf16  # noqa: E402
 import compare  # noqa: E402
 import gpu_harness  # noqa: E402
 
-SKIP_TOL = {"bf16": 1e-3, "f32": 1e-4, "i8fp8": 1e-3, "i4fp8": 1e-3}
+SKIP_TOL = {"bf16": 1e-3, "f32": 1e-4, "i8fp8": 1e-3, "i4fp8": 1e-3, "i8mxfp8": 1e-3}
+QUANT = ("i8fp8", "i4fp8", "i8mxfp8")
 RECALL_TOL = 1e-4  # relative slack of the recall rule (fp32 sums vs fp64)
 
 
@@ -67,7 +68,8 @@ def check_case(w: Workload, layout="bhnd", check_out=True):
                  sm_scale=float(np.float32(1.0 / math.sqrt(w.D))),
                  skip_rule=w.skip_rule, recall=float(np.float32(w.recall)),
                  topk_blocks=w.topk_blocks)
-    mode = w.prec if w.prec in ("i8fp8", "i4fp8") else w.dtype
+    mode = w.prec if w.prec in QUANT else w.dtype
+    v_pow2 = w.prec == "i8mxfp8"
     qmax = 7 if w.prec == "i4fp8" else 127
     worst = 0.0
     n_rows = n_exact = 0
@@ -92,9 +94,9 @@ def check_case(w: Workload, layout="bhnd", check_out=True):
                 continue
             gk = r["kept"][hid]
             gs = r["skips"][hid]
-            if mode in ("i8fp8", "i4fp8"):
+            if mode in QUANT:
                 def fn(*args, **kw):
-                    return O.sparse_attention_quant_head(*args, qmax=qmax, **kw)
+                    return O.sparse_attention_quant_head(*args, qmax=qmax, v_pow2=v_pow2, **kw)
             else:
                 fn = O.sparse_attention_head
             if w.skip_rule == "recall":
@@ -120,14 +122,15 @@ def check_case(w: Workload, layout="bhnd", check_out=True):
                                               round_to_bf16(r["O"][b, h]))
             fin = np.isfinite(lse_ref)
             np.testing.assert_allclose(r["lse"][b, h][fin], lse_ref[fin], atol=1e-3, rtol=0)
-            if mode in ("i8fp8", "i4fp8"):
+            if mode in QUANT:
                 qc, qs = O.int_quantize_blocks(q, 128, qmax)
                 kc, ks = O.int_quantize_blocks(k, 64, qmax)
                 np.testing.assert_array_equal(r["qc"][b, h], qc)
                 np.testing.assert_array_equal(r["kc"][b, h], kc)
                 np.testing.assert_array_equal(r["sq"][b, h], qs)
                 np.testing.assert_array_equal(r["sk"][b, h], ks)
-                vq, vs = O.fp8_quantize_v_blocks(v, 64)
+                vq, vs = (O.fp8_quantize_v_blocks_pow2 if v_pow2 else
+                          O.fp8_quantize_v_blocks)(v, 64)
                 np.testing.assert_array_equal(r["sv"][b, h], vs)
                 codes = np.zeros((r["nkb"] * 64, w.D), dtype=np.uint8)
                 codes[:w.N] = O.e4m3_encode(vq)
@@ -232,6 +235,19 @@ CASES = [
        lam=-3.0, prec="i4fp8", group_rows=128),
     wl("g16_quant_recall", 142, 1, 2, 800, 128, grid=(8, 10, 10), tau=0.9, prec="i8fp8",
        skip_rule="recall", recall=0.9, group_rows=16),
+    # power-of-two V scales applied by the scaled FP8 MFMA
+    wl("mx_energy", 143, 1, 2, 1000, 128, grid=(10, 10, 10), tau=0.95, lam=-5.0,
+       rule="energy", prec="i8mxfp8"),
+    wl("mx_causal", 144, 1, 1, 700, 128, structure="lm", causal=True, tau=0.9, lam=-5.0,
+       prec="i8mxfp8"),
+    wl("mx_recall", 145, 2, 1, 800, 128, grid=(8, 10, 10), tau=0.9, prec="i8mxfp8",
+       skip_rule="recall", recall=0.9),
+    wl("mx_g64", 146, 1, 2, 900, 128, grid=(9, 10, 10), tau=0.9, lam=-2.0, prec="i8mxfp8",
+       group_rows=64),
+    wl("mx_g16_causal", 147, 1, 2, 555, 128, structure="lm", causal=True, tau=0.95,
+       lam=-2.0, prec="i8mxfp8", group_rows=16),
+    wl("mx_lam_off", 148, 1, 2, 1000, 128, grid=(10, 10, 10), tau=0.9, lam=-math.inf,
+       prec="i8mxfp8"),
 ]
 
 
@@ -352,7 +368,7 @@ def test_dense_identity_on_gpu():
 def test_positive_lambda_zeroes_output():
     w = wl("lam_pos", 111, 1, 2, 500, 128, grid=(5, 10, 10), tau=0.9, lam=0.5)
     Q, K, V = stacked(w)
-    for prec in ("native", "i8fp8", "i4fp8"):
+    for prec in ("native", "i8fp8", "i4fp8", "i8mxfp8"):
         log(f"[case] lambda > 0, {prec}")
         r = gpu_harness.run(Q, K, V, tau=0.9, lam=0.5, prec=prec)
         assert np.all(r["O"] == 0.0)

@@ -177,3 +177,112 @@ def test_int4_quant_attention_matches_brute():
     o8, _, _ = O.sparse_attention_quant_head(q, k, v, pr["kept"], p)
     ref, _, _ = O.sparse_attention_head(q, k, v, pr["kept"], p)
     assert np.abs(got - ref).mean() > np.abs(o8 - ref).mean()
+
+
+def _pow2_brute(amax):
+    """Smallest 2^e (integer e) with amax <= 448 * 2^e, by enumeration."""
+    if amax == 0:
+        return 1.0
+    for e in range(-200, 200):
+        if amax <= 448.0 * 2.0 ** e:
+            return 2.0 ** e
+    raise AssertionError(amax)
+
+
+def test_pow2_scale_hand_values_and_enumeration():
+    assert O.pow2_scale(448.0) == 1.0
+    assert O.pow2_scale(np.nextafter(np.float32(448.0), np.float32(1e9))) == 2.0
+    assert O.pow2_scale(224.0) == 0.5
+    assert O.pow2_scale(np.nextafter(np.float32(224.0), np.float32(1e9))) == 1.0
+    assert O.pow2_scale(3.5) == 2.0 ** -7       # 448 * 2^-7 = 3.5 exactly
+    assert O.pow2_scale(3.6) == 2.0 ** -6
+    assert O.pow2_scale(0.0) == 1.0
+    rng = np.random.default_rng(21)
+    for a in np.concatenate([rng.lognormal(0, 6, 400), 448.0 * 2.0 ** rng.integers(-60, 60, 50)]):
+        a = float(np.float32(a))
+        assert O.pow2_scale(a) == _pow2_brute(a), a
+
+
+def test_pow2_v_blocks_range_grid_and_round_trip():
+    rng = np.random.default_rng(22)
+    V = (rng.standard_normal((200, 16)) * rng.lognormal(0, 2, (200, 1))).astype(np.float32)
+    vals, s = O.fp8_quantize_v_blocks_pow2(V, 64)
+    for b in range(4):
+        blk = V[b * 64:(b + 1) * 64]
+        e = math.log2(float(s[b]))
+        assert e == int(e)                                     # a power of two
+        r = float(np.abs(blk).max()) / float(s[b])
+        assert 224.0 < r <= 448.0
+        q = vals[b * 64:(b + 1) * 64]
+        assert np.all(O.e4m3_round(q) == q) and np.abs(q).max() <= 448.0
+        np.testing.assert_array_equal(q, O.e4m3_round(blk.astype(np.float64) / float(s[b])))
+    # values on the e4m3 grid times a power of two come back exactly
+    grid = O.e4m3_round(rng.uniform(-448, 448, (64, 8)))
+    grid[0, 0] = 448.0
+    X = (grid * 2.0 ** -5).astype(np.float32)
+    vals, s = O.fp8_quantize_v_blocks_pow2(X, 64)
+    assert s[0] == 2.0 ** -5
+    np.testing.assert_array_equal(vals, grid)
+
+
+def test_pow2_quant_attention_matches_brute():
+    rng = np.random.default_rng(23)
+    N, d, BQ, BK, G = 36, 4, 8, 4, 4
+    q = rng.standard_normal((N, d)).astype(np.float32) * 2
+    k = rng.standard_normal((N, d)).astype(np.float32) * 2
+    v = rng.standard_normal((N, d)).astype(np.float32)
+    for causal in (False, True):
+        p = O.Params(BQ=BQ, BK=BK, causal=causal, tau=0.8, lam=-1.0, G=G)
+        pr = O.predict_head(q, k, p)
+        got, _, sk = O.sparse_attention_quant_head(q, k, v, pr["kept"], p, v_pow2=True)
+        qc, qs = O.int8_quantize_blocks(q, BQ)
+        kc, ks = O.int8_quantize_blocks(k, BK)
+        sv = [_pow2_brute(float(np.abs(v[j * BK:(j + 1) * BK]).max())) for j in range(N // BK)]
+        sm = 1 / math.sqrt(d)
+
+        def score(r, c):
+            dot = sum(int(qc[r, e]) * int(kc[c, e]) for e in range(d))
+            return sm * float(qs[r // BQ]) * float(ks[c // BK]) * dot
+
+        def pv(r, c, pval):
+            pq = float(O.e4m3_round(np.array([pval * 256.0]))[0]) / 256.0
+            s = sv[c // BK]
+            return [s * pq * float(O.e4m3_round(np.array([float(v[c, e]) / s]))[0])
+                    for e in range(d)]
+
+        def weight(pval):  # the quantised weight normalises O
+            return float(O.e4m3_round(np.array([pval * 256.0]))[0]) / 256.0
+
+        exp, esk = brute.attention(q.tolist(), k.tolist(), v.tolist(),
+                                   [list(x) for x in pr["kept"]], BQ, BK, causal, -1.0, G,
+                                   score=score, pv=pv, weight=weight)
+        np.testing.assert_allclose(got, np.array(exp), atol=1e-12)
+        assert [s.tolist() for s in sk] == esk
+        # the V codes differ from the absmax / 448 reading; both stay within
+        # e4m3's resolution (1/16 relative) of the unquantised result
+        o8, _, _ = O.sparse_attention_quant_head(q, k, v, pr["kept"], p)
+        ref, _, _ = O.sparse_attention_head(q, k, v, pr["kept"], p)
+        assert not np.array_equal(got, o8)
+        for o in (got, o8):
+            assert np.abs(o - ref).max() <= np.abs(v).max() / 8
+
+
+def test_pow2_output_is_a_weighted_average_of_quantised_values():
+    """With lambda = -inf nothing is skipped, and in the power-of-two mode O
+    is a convex combination of the quantised V rows s_v V~: each output lies
+    within their range; the absmax / 448 mode normalises by the unquantised
+    sum instead, which the quantised weights need not match."""
+    rng = np.random.default_rng(24)
+    N, d = 256, 8
+    q, k = (rng.standard_normal((N, d)).astype(np.float32) * 2 for _ in range(2))
+    v = rng.standard_normal((N, d)).astype(np.float32)
+    p = O.Params(BQ=32, BK=16, tau=1.0, lam=-math.inf, G=8)
+    kept = O.predict_head(q, k, p)["kept"]
+    got, _, _ = O.sparse_attention_quant_head(q, k, v, kept, p, v_pow2=True)
+    vq, vs = O.fp8_quantize_v_blocks_pow2(v, 16)
+    deq = vq * np.repeat(vs.astype(np.float64), 16)[:, None]
+    assert np.all(got <= deq.max(axis=0) + 1e-12) and np.all(got >= deq.min(axis=0) - 1e-12)
+    # all-equal V rows: the weighted average returns them exactly
+    vc = np.tile(np.float32([0.5, -1.25, 3.0, 0.0, 2.0, -4.0, 1.0, 0.125]), (N, 1))
+    got, _, _ = O.sparse_attention_quant_head(q, k, vc, kept, p, v_pow2=True)
+    np.testing.assert_allclose(got, np.tile(vc[0], (N, 1)), rtol=0, atol=1e-12)
