@@ -49,9 +49,15 @@ METRIC = "dense-equiv attention TFLOPS + sparsity at fixed rel-L1, N=32760 H=40 
 # keyed by the hash of the kernel sources it was measured on: a changed
 # kernel reports null until it is measured again.
 MEASURED_TRAFFIC = {
-    # (kernel kind, workload) -> (source hash, bytes read, bytes written)
-    ("bf16", "wan_video"): ("a94fdf35de14c2f0", 111_185_240_064, 387_946_496),
-    ("bf16", "hunyuan_video"): ("a94fdf35de14c2f0", 983_599_722_112, 800_134_400),
+    # (kernel kind, workload, Q.K^T mode) -> (source hash, bytes read, bytes written)
+    ("bf16", "wan_video", "native"): ("e1e239ac1510fab0", 111_700_397_824, 335_466_560),
+    ("bf16", "hunyuan_video", "native"): ("e1e239ac1510fab0", 984_093_566_080, 731_489_152),
+    ("i8fp8", "quant_long", "i8fp8"): ("68bf9f2bed75a20b", 96_750_356_992, 268_435_456),
+    ("i8fp8", "quant_long", "i8mxfp8"): ("68bf9f2bed75a20b", 96_720_460_288, 268_435_456),
+    ("pool", "wan_video", "native"): ("4c1ce0d8f8ed753a", 670_999_168, 15_728_640),
+    ("pool", "hunyuan_video", "native"): ("4c1ce0d8f8ed753a", 1_463_054_592, 34_308_096),
+    ("pool", "quant_long", "i8fp8"): ("4c1ce0d8f8ed753a", 536_934_272, 12_582_912),
+    ("pool", "quant_long", "i8mxfp8"): ("4c1ce0d8f8ed753a", 536_937_088, 12_582_912),
 }
 # the forward kernel that dominates each kind of workload, and its sources;
 # "pool" is the predictor's HBM-bound first step
@@ -82,6 +88,9 @@ def parse():
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--skip-rule", default="lambda", choices=("lambda", "recall"),
                     help="stage-two skip rule of the timed configuration")
+    ap.add_argument("--prec", default=None, choices=QUANT_PRECS,
+                    help="quantised Q.K^T mode of a quantised workload (default: the "
+                         "workload's own)")
     ap.add_argument("--recall", type=float, default=0.95,
                     help="target recall of the recall skip rule")
     ap.add_argument("--no-peaks", action="store_true",
@@ -97,8 +106,14 @@ def parse():
     return ap.parse_args()
 
 
+# quantised Q.K^T modes that run attn_q_kernel: INT8 codes with absmax/448
+# FP8 V scales, and INT8 codes with power-of-two V scales applied by the
+# scaled FP8 MFMA
+QUANT_PRECS = ("i8fp8", "i8mxfp8")
+
+
 def forward_kind(w):
-    return "i8fp8" if w.prec == "i8fp8" else w.dtype
+    return "i8fp8" if w.prec in QUANT_PRECS else w.dtype
 
 
 def _build_module():
@@ -504,8 +519,9 @@ def _oracle_sparse_task(task):
     t1 = time.perf_counter()
     sub_kept = [kept[i] if i in blocks else np.zeros(0, dtype=np.int64) for i in range(nqb)]
     sub_skip = [skips[i] if i in blocks else np.zeros((0, 4), dtype=bool) for i in range(nqb)]
-    if w.prec == "i8fp8":
-        Ob, _, _ = O.sparse_attention_quant_head(q, k, v, sub_kept, p, force_skip=sub_skip)
+    if w.prec in QUANT_PRECS:
+        Ob, _, _ = O.sparse_attention_quant_head(q, k, v, sub_kept, p, force_skip=sub_skip,
+                                                 v_pow2=w.prec == "i8mxfp8")
     else:
         Ob, _, _ = O.sparse_attention_head(q, k, v, sub_kept, p, force_skip=sub_skip)
     t2 = time.perf_counter()
@@ -770,7 +786,7 @@ def reorder_sweep(sa, torch, w, q, k, v, measure_on, taus=(0.9, 0.95, 0.98), ite
                              predict_forward_ms=round(m["ms"], 4)))
             del r
         if quant is not None and metric == "interaction":
-            for prec in ("i8fp8", "i4fp8"):
+            for prec in ("i8fp8", "i8mxfp8", "i4fp8"):
                 r, m = measure_on(qp, kp, vp, w.tau, prec, lambda rr: sa.sparse_attn_permute(
                     p, rr.o, pq, 1, o_back) or o_back, f"reorder_{metric}_{prec}")
                 quant.append(dict(order="interaction clusters", prec=prec, tau=w.tau,
@@ -795,6 +811,12 @@ def main():
         sys.exit(2)
     from synth import make_workload
     w = make_workload(args.workload)
+    if args.prec is not None:
+        if w.prec not in QUANT_PRECS:
+            print(f"--prec applies to quantised workloads; {w.name} computes in {w.dtype}",
+                  file=sys.stderr)
+            sys.exit(2)
+        w = make_workload(args.workload, prec=args.prec)
     leg = None
     if not args.no_cpu_baseline and args.stage == "all":
         # forked now, while nothing in this process has touched the GPU
@@ -873,7 +895,7 @@ def run(args, w, leg):
           file=sys.stderr, flush=True)
     r, m = measure(w.tau, args.steps, args.warmup)
     value = dense / (m["ms"] * 1e-3) / 1e12
-    peak = PEAK_I8FP8_TOPS if w.prec == "i8fp8" else (
+    peak = PEAK_I8FP8_TOPS if w.prec in QUANT_PRECS else (
         PEAK_FP32_TFLOPS if w.dtype == "f32" else PEAK_BF16_TFLOPS)
     achieved = m["exec_flops"] / (m["forward_ms"] * 1e-3) / 1e12
     head = r.decisions(sample)
@@ -927,7 +949,7 @@ def run(args, w, leg):
         for r_ in reuse:
             print(f"[bench] reuse {r_}", file=sys.stderr, flush=True)
         # INT8 and 4-bit Q.K^T (FP8 P.V) at the headline tau, contiguous order
-        for prec in ("i8fp8", "i4fp8"):
+        for prec in ("i8fp8", "i8mxfp8", "i4fp8"):
             key = f"contiguous_{prec}"
             rs, ms_ = measure(w.tau, few, 1, prec=prec, key=key)
             quant.append(dict(order="contiguous", prec=prec, tau=w.tau, key=key,
@@ -945,6 +967,23 @@ def run(args, w, leg):
             print(f"[bench] reorder {r_}", file=sys.stderr, flush=True)
         for r_ in quant:
             print(f"[bench] quantised Q.K^T {r_}", file=sys.stderr, flush=True)
+
+    if not args.no_sweep and w.prec in QUANT_PRECS:
+        # the other quantised mode on the same workload
+        for prec in QUANT_PRECS:
+            if prec == w.prec:
+                continue
+            key = f"workload_{prec}"
+            rs, ms_ = measure(w.tau, few, 1, prec=prec, key=key)
+            tops = ms_["exec_flops"] / (ms_["forward_ms"] * 1e-3) / 1e12
+            quant.append(dict(order="contiguous", prec=prec, tau=w.tau, key=key,
+                              sparsity=round(ms_["sparsity"], 5),
+                              pv_skip_fraction=round(ms_["skip"], 5),
+                              forward_ms=round(ms_["forward_ms"], 4),
+                              executed_tops=round(tops, 1),
+                              frac=round(tops / PEAK_I8FP8_TOPS, 4)))
+            del rs
+            print(f"[bench] quantised Q.K^T {quant[-1]}", file=sys.stderr, flush=True)
 
     peaks, clock = None, None
     if not args.no_peaks:
@@ -1001,12 +1040,12 @@ def run(args, w, leg):
 
     kind = forward_kind(w)
     traffic = None
-    mt = MEASURED_TRAFFIC.get((kind, w.name))
+    mt = MEASURED_TRAFFIC.get((kind, w.name, w.prec))
     if mt and mt[0] == kernel_source_hash(kind):
         traffic = {"read_bytes": mt[1], "written_bytes": mt[2], "total_bytes": mt[1] + mt[2],
                    "source": "rocprofv3 FETCH_SIZE/WRITE_SIZE, copy-calibrated"}
     pool_traffic = None
-    mt = MEASURED_TRAFFIC.get(("pool", w.name))
+    mt = MEASURED_TRAFFIC.get(("pool", w.name, w.prec))
     if mt and mt[0] == kernel_source_hash("pool"):
         pool_traffic = {"read_bytes": mt[1], "written_bytes": mt[2],
                         "total_bytes": mt[1] + mt[2],
@@ -1023,13 +1062,14 @@ def run(args, w, leg):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "i8/fp8" if w.prec == "i8fp8" else w.dtype,
+        "dtype": "i8/fp8" if w.prec in QUANT_PRECS else w.dtype,
         "data": data_description(w),
         "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "D": w.D,
                    "causal": w.causal, "tau": w.tau, "lambda": w.lam, "rule": w.rule,
                    "block_q": 128, "block_k": 64, "lambda_group_rows": 32,
                    "skip_rule": args.skip_rule,
-                   **({"recall": args.recall} if args.skip_rule == "recall" else {})},
+                   **({"recall": args.recall} if args.skip_rule == "recall" else {}),
+                   **({"qk_precision": w.prec} if w.prec in QUANT_PRECS else {})},
         "sparsity": _rd(vs_oracle["sparsity"], 5) if vs_oracle else None,
         "pv_skip_fraction": _rd(vs_oracle["pv_skip_fraction"], 5) if vs_oracle else None,
         "rel_l1_vs_dense": _rd(vs_oracle["rel_l1_vs_dense"]) if vs_oracle else None,

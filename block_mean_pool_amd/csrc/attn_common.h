@@ -62,19 +62,22 @@ __device__ __forceinline__ bool split_keeps(uint32_t split, int l32) {
 // score r of key half kt is key key0 + 32 kt + 8 (r / 4) + 4 hh + r % 4, set
 // to -inf past N, for rows past N, and (causal) after the lane's row.  The
 // per-score offsets are compile-time constants against one scalar and one
-// per-lane value, so no per-score lane offsets stay live.
+// per-lane value, so no per-score lane offsets stay live.  A row past N gets
+// a lane offset beyond every limit (N <= 2^18) instead of a separate test:
+// `qvalid && ...` became exec-masked code that wrote the masked scores to
+// new registers, and the unmasked path then copied all 32 scores to match.
 template <bool CAUSAL, typename F>
 __device__ __forceinline__ void mask_scores(F (&s)[2], int key0, int N, int hh, int qrow,
                                             bool qvalid) {
   const int lim = N - key0;  // offsets >= lim are keys past N
-  const int hh4 = 4 * hh;
+  const int hh4 = qvalid ? 4 * hh : (1 << 30);
   const int dq = hh4 - (qrow - key0);  // causal: offset hh4 + c visible iff dq <= -c
 #pragma unroll
   for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int c = 32 * kt + 8 * (r >> 2) + (r & 3);
-      const bool ok = qvalid && hh4 < lim - c && (!CAUSAL || dq <= -c);
+      const bool ok = hh4 < lim - c && (!CAUSAL || dq <= -c);
       s[kt][r] = ok ? s[kt][r] : -INFINITY;
     }
 }

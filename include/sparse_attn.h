@@ -59,7 +59,7 @@
 extern "C" {
 #endif
 
-#define SPARSE_ATTN_VERSION 7
+#define SPARSE_ATTN_VERSION 8
 
 #if defined(__GNUC__)
 #define SA_API __attribute__((visibility("default")))

@@ -75,7 +75,7 @@ def test_shapes_and_workspace():
     assert fw == 2 * bh * 65536 * 128 + bh * 1024 * 128 * 64 + bh * 512 * 4 + 2 * bh * 1024 * 4
     q4 = sa.make_params(1, 16, 65536, 128, prec="i4fp8", rule="energy")
     assert sa.sparse_attn_workspace_size(q4)[1] == fw
-    assert sa.sparse_attn_info() == (32, 7)
+    assert sa.sparse_attn_info() == (32, 8)
     assert sa.sparse_attn_status_str(3) == "SA_ERR_WORKSPACE"
     assert sa.sparse_attn_status_str(99) == "SA_ERR_UNKNOWN"
     p = sa.make_params(2, 3, 0, 64)

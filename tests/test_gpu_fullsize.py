@@ -79,6 +79,9 @@ def decode_skips(bits, cnt):
     ("wan_video", [6], 4, dict(H=8, N=66000, grid=(22, 50, 60), skip_rule="recall",
                                recall=0.95, group_rows=128)),
     ("wan_video", [13], 4, dict(group_rows=16)),
+    # half-wavefront groups and four-wavefront groups in the V-vote schedule
+    ("wan_video", [4], 4, dict(H=8, N=66000, grid=(22, 50, 60), group_rows=16)),
+    ("wan_video", [1], 4, dict(H=8, N=66000, grid=(22, 50, 60), group_rows=128)),
 ])
 def test_fullsize_parity(name, heads, nblocks, over):
     w = dataclasses.replace(make_workload(name), **over)
