@@ -50,14 +50,14 @@ METRIC = "dense-equiv attention TFLOPS + sparsity at fixed rel-L1, N=32760 H=40 
 # kernel reports null until it is measured again.
 MEASURED_TRAFFIC = {
     # (kernel kind, workload, Q.K^T mode) -> (source hash, bytes read, bytes written)
-    ("bf16", "wan_video", "native"): ("e1e239ac1510fab0", 111_700_397_824, 335_466_560),
-    ("bf16", "hunyuan_video", "native"): ("e1e239ac1510fab0", 984_093_566_080, 731_489_152),
-    ("i8fp8", "quant_long", "i8fp8"): ("68bf9f2bed75a20b", 96_750_356_992, 268_435_456),
-    ("i8fp8", "quant_long", "i8mxfp8"): ("68bf9f2bed75a20b", 96_720_460_288, 268_435_456),
-    ("pool", "wan_video", "native"): ("4c1ce0d8f8ed753a", 670_999_168, 15_728_640),
-    ("pool", "hunyuan_video", "native"): ("4c1ce0d8f8ed753a", 1_463_054_592, 34_308_096),
-    ("pool", "quant_long", "i8fp8"): ("4c1ce0d8f8ed753a", 536_934_272, 12_582_912),
-    ("pool", "quant_long", "i8mxfp8"): ("4c1ce0d8f8ed753a", 536_937_088, 12_582_912),
+    ("bf16", "wan_video", "native"): ("0887a8417af52975", 111_727_592_064, 335_467_200),
+    ("bf16", "hunyuan_video", "native"): ("0887a8417af52975", 984_076_220_928, 731_489_312),
+    ("i8fp8", "quant_long", "i8fp8"): ("6ca5dd8bc36e0476", 96_770_212_352, 268_435_456),
+    ("i8fp8", "quant_long", "i8mxfp8"): ("6ca5dd8bc36e0476", 96_730_270_336, 268_435_456),
+    ("pool", "wan_video", "native"): ("4c1ce0d8f8ed753a", 671_001_856, 15_728_640),
+    ("pool", "hunyuan_video", "native"): ("4c1ce0d8f8ed753a", 1_463_053_440, 34_308_096),
+    ("pool", "quant_long", "i8fp8"): ("4c1ce0d8f8ed753a", 536_935_808, 12_582_912),
+    ("pool", "quant_long", "i8mxfp8"): ("4c1ce0d8f8ed753a", 536_936_576, 12_582_912),
 }
 # the forward kernel that dominates each kind of workload, and its sources;
 # "pool" is the predictor's HBM-bound first step
