@@ -256,6 +256,31 @@ def test_parity_small(w):
     check_case(w)
 
 
+# one partial block of every kind, and the first sizes past a key block and a
+# query block, for each kernel family: (dtype, D, causal, Q.K^T mode, G)
+TINY_FAMILIES = [("bf16", 128, False, "native", 32), ("bf16", 64, True, "native", 32),
+                 ("f32", 64, False, "native", 32), ("f32", 128, True, "native", 32),
+                 ("bf16", 128, False, "i8fp8", 32), ("bf16", 128, True, "i8mxfp8", 32),
+                 ("bf16", 128, False, "native", 16), ("bf16", 128, True, "native", 64)]
+TINY_N = (1, 7, 64, 65, 129)
+
+
+@pytest.mark.parametrize("fam", TINY_FAMILIES, ids=lambda f: "-".join(map(str, f)))
+@pytest.mark.parametrize("N", TINY_N)
+def test_tiny_sequences(fam, N):
+    dtype, D, causal, prec, G = fam
+    w = wl(f"tiny_n{N}", 150 + N, 1, 2, N, D, dtype=dtype, structure="gauss", causal=causal,
+           tau=0.9, lam=-5.0, prec=prec, group_rows=G)
+    r = check_case(w)
+    if N == 1 and prec == "native":
+        # one key: its weight is exactly 1, so O is V and lse the one score
+        Q, K, V = stacked(w)
+        np.testing.assert_array_equal(r["O"][0, :, 0], V[0, :, 0])
+        sm = np.float32(1.0 / math.sqrt(D))
+        lse = (sm * (Q[0, :, 0].astype(np.float64) * K[0, :, 0]).sum(axis=-1))
+        np.testing.assert_allclose(r["lse"][0, :, 0], lse, atol=1e-4, rtol=0)
+
+
 def random_cases(n=16, seed=20261203):
     """Seeded random combinations of the parameters the hand-picked cases fix
     one at a time: head dimension, causality, input type, Q.K^T precision,
