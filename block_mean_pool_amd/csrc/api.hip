@@ -59,8 +59,8 @@ sa_status check_params(const sa_params* p, sa::Geometry* g, bool* empty) {
   if (p->prec != SA_PREC_NATIVE && p->prec != SA_PREC_I8_FP8 && p->prec != SA_PREC_I4_FP8 &&
       p->prec != SA_PREC_I8_MXFP8)
     return fail(SA_ERR_INVALID_ARG, "prec=%d", p->prec);
-  if (p->prec != SA_PREC_NATIVE && (p->dtype != SA_BF16 || p->D != 128))
-    return fail(SA_ERR_UNSUPPORTED, "INT8/INT4/FP8 variants need bf16 inputs and D=128");
+  if (p->prec != SA_PREC_NATIVE && p->dtype != SA_BF16)
+    return fail(SA_ERR_UNSUPPORTED, "INT8/INT4/FP8 variants need bf16 inputs");
   if (p->rule != SA_RULE_TOPCDF && p->rule != SA_RULE_ENERGY && p->rule != SA_RULE_TOPK)
     return fail(SA_ERR_INVALID_ARG, "rule=%d", p->rule);
   if (p->rule == SA_RULE_TOPK && p->topk_blocks < 1)

@@ -18,7 +18,8 @@
 // quant_kernel: one workgroup per Q block, K block or V block; the block is
 // read once into registers, its absmax reduced, and its codes written.  V
 // codes are written per key block transposed ([D][64] bytes) through LDS, so
-// the attention kernel stages V^T with plain 16-byte copies.
+// the attention kernel stages V^T with plain 16-byte copies.  Both kernels
+// take the head dimension D (64 or 128) as a template parameter.
 // attn_q_kernel: the same tiling, online softmax and per-wavefront lambda
 // test as the bf16 kernel, with v_mfma_i32_32x32x32_i8 for S^T = K Q^T and
 // v_mfma_f32_32x32x64_f8f6f4 (e4m3 x e4m3) for O^T += V^T P^T.
@@ -29,8 +30,6 @@
 namespace sa {
 namespace {
 
-constexpr int D = 128;
-
 __device__ __forceinline__ float block_max(float v, float* scratch) {
   v = wave_max(v);
   const int w = threadIdx.x >> 6;
@@ -39,14 +38,18 @@ __device__ __forceinline__ float block_max(float v, float* scratch) {
   return fmaxf(fmaxf(scratch[0], scratch[1]), fmaxf(scratch[2], scratch[3]));
 }
 
-// Q: 128-row blocks, K and V: 64-row blocks.  D = 128 bf16 = 16 chunks of
-// 16 B per row; thread -> chunk tid % 16, rows tid / 16 + 16 * it.
+// Q: 128-row blocks, K and V: 64-row blocks.  A row of D bf16 is CPR = D / 8
+// chunks of 16 B; thread -> chunk tid % CPR, rows tid / CPR + RPI * it.
+template <int D>
 __global__ __launch_bounds__(256) void quant_kernel(ForwardLaunch f) {
+  constexpr int CPR = D / 8;       // 16-byte chunks per row
+  constexpr int RPI = 256 / CPR;   // rows per pass of the workgroup
+  constexpr int NIT = 128 / RPI;   // passes over a query block
   __shared__ float scratch[4];
   __shared__ __align__(16) uint8_t vt_tile[D * 64];
   const Geometry& g = f.g;
   const int tid = threadIdx.x;
-  const int c = tid & 15, ro = tid >> 4;
+  const int c = tid % CPR, ro = tid / CPR;
   const int nq = g.B * g.H * g.nqb;
   const int nk = g.B * g.H * g.nkb;
   int id = blockIdx.x;
@@ -74,11 +77,11 @@ __global__ __launch_bounds__(256) void quant_kernel(ForwardLaunch f) {
                       (int64_t)b * g.sb + (int64_t)h * g.sh;
   const int r0 = blk * bs, r1 = min(g.N, r0 + bs);
 
-  u32x4 buf[8];
+  u32x4 buf[NIT];
   float amax = 0.f;
 #pragma unroll
-  for (int it = 0; it < 8; ++it) {
-    const int r = r0 + ro + 16 * it;
+  for (int it = 0; it < NIT; ++it) {
+    const int r = r0 + ro + RPI * it;
     buf[it] = u32x4{0u, 0u, 0u, 0u};
     if (r < r1) buf[it] = *reinterpret_cast<const u32x4*>(src + (int64_t)r * g.sn + c * 8);
 #pragma unroll
@@ -93,8 +96,8 @@ __global__ __launch_bounds__(256) void quant_kernel(ForwardLaunch f) {
     int8_t* dst = (kind == 0 ? f.qc : f.kc) + (size_t)bh * g.N * D;
     if (tid == 0) (kind == 0 ? f.sq : f.sk)[bh * (kind == 0 ? g.nqb : g.nkb) + blk] = scale;
 #pragma unroll
-    for (int it = 0; it < 8; ++it) {
-      const int r = r0 + ro + 16 * it;
+    for (int it = 0; it < NIT; ++it) {
+      const int r = r0 + ro + RPI * it;
       if (r < r1) {
         uint32_t packed[2] = {0u, 0u};
 #pragma unroll
@@ -118,13 +121,13 @@ __global__ __launch_bounds__(256) void quant_kernel(ForwardLaunch f) {
       scale = amax > 0.f ? ldexpf(1.0f, fr <= 0.875f ? E - 9 : E - 8) : 1.0f;
     }
     if (tid == 0) f.sv[bh * g.nkb + blk] = scale;
-    // rows ro + 16 it (it < 4) of this key block; transposed into LDS,
-    // key k = 32 t + 8 g + 4 h + e at position 32 h + 16 t + 4 g + e: the
+    // rows ro + RPI it (it < 64 / RPI) of this key block; transposed into
+    // LDS, key k = 32 t + 8 g + 4 h + e at position 32 h + 16 t + 4 g + e: the
     // order of a 32x32 MFMA accumulator lane's keys, so that a lane's 32 P
     // codes and the 32 V codes it multiplies are both contiguous
 #pragma unroll
-    for (int it = 0; it < 4; ++it) {
-      const int rr = ro + 16 * it;  // key within block
+    for (int it = 0; it < 64 / RPI; ++it) {
+      const int rr = ro + RPI * it;  // key within block
       const int pos = 32 * ((rr >> 2) & 1) + 16 * (rr >> 5) + 4 * ((rr >> 3) & 3) + (rr & 3);
 #pragma unroll
       for (int e = 0; e < 8; e += 2) {
@@ -138,9 +141,9 @@ __global__ __launch_bounds__(256) void quant_kernel(ForwardLaunch f) {
     }
     __syncthreads();
     uint8_t* dst = f.vt + ((size_t)bh * g.nkb + blk) * D * 64;
-    // 8 KB tile = 512 chunks of 16 B, two per thread
+    // a D x 64-byte tile = D * 4 chunks of 16 B, D / 64 per thread
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
+    for (int s = 0; s < D / 64; ++s) {
       const int ch = tid + 256 * s;
       *reinterpret_cast<u32x4*>(dst + ch * 16) = *reinterpret_cast<const u32x4*>(vt_tile + ch * 16);
     }
@@ -190,14 +193,19 @@ typedef int i32x8 __attribute__((ext_vector_type(8)));
 // mode's reading), summed by one more scaled MFMA per tile with an all-ones
 // operand instead of 31 adds per lane.  Mode 2 (the recall rule) still sums
 // the unquantised weights on the VALU for the rule's energies.
-template <bool CAUSAL, int GM, int PM>
+template <int D, bool CAUSAL, int GM, int PM>
 __global__ __launch_bounds__(256, 2) void attn_q_kernel(AttnQArgs a) {
   constexpr bool VP2 = PM != 0, ROWSUM_VALU = PM != 1;
+  // 32-wide d chunks: the K extent of one INT8 Q.K^T MFMA, and the d rows of
+  // one FP8 P.V MFMA; a region of four chunks issues the MFMAs of one d chunk
+  // every CSTEP chunks (every chunk at D = 128, every other one at D = 64)
+  constexpr int NKK = D / 32, CSTEP = 4 / NKK;
+  constexpr int NI = 64 * D / 4096;  // DMA instructions per tile and wavefront
   // skip groups: SPLIT = halves of a wavefront (G = 16); DEFER = several
   // wavefronts (G = 64, 128), final after the barrier that follows the votes
   constexpr bool SPLIT = GM == attn::kGroupHalf, DEFER = GM == attn::kGroupMulti;
-  constexpr int TK = 64 * D;  // K codes of a tile, 8 KiB
-  constexpr int TV = D * 64;  // V^T codes of a tile, 8 KiB
+  constexpr int TK = 64 * D;  // K codes of a tile, D * 64 bytes
+  constexpr int TV = D * 64;  // V^T codes of a tile, D * 64 bytes
   __shared__ __align__(16) char k0[TK];
   __shared__ __align__(16) char k1[TK];
   __shared__ __align__(16) char v0[TV];
@@ -222,9 +230,9 @@ __global__ __launch_bounds__(256, 2) void attn_q_kernel(AttnQArgs a) {
   const bool wave_partial = wrow0 + 32 > a.N;
   const int8_t* qc = a.qc + (size_t)bh * a.N * D;
 
-  u32x4 qf[4];  // Q codes, d = 32 kk + 16 hh + [0, 16) of row qrow
+  u32x4 qf[NKK];  // Q codes, d = 32 kk + 16 hh + [0, 16) of row qrow
 #pragma unroll
-  for (int kk = 0; kk < 4; ++kk)
+  for (int kk = 0; kk < NKK; ++kk)
     qf[kk] = qvalid ? *reinterpret_cast<const u32x4*>(qc + (int64_t)qrow * D + 32 * kk + 16 * hh)
                     : u32x4{0u, 0u, 0u, 0u};
   const float cq = a.c2 * a.sq[wg];
@@ -254,27 +262,30 @@ __global__ __launch_bounds__(256, 2) void attn_q_kernel(AttnQArgs a) {
       const_cast<uint8_t*>(a.vt + (size_t)bh * a.nkb * TV), (short)0, (int)(a.nkb * TV),
       0x00020000);
 
-  // DMA: wave-instruction n (0, 1) of wave w fills bytes [(4 n + w) KiB,
-  // +1 KiB) of a tile, lane e 16 bytes at e * 16.  K: LDS row r (128 B),
-  // position p holds global chunk p ^ swk(r), swk(r) = (r >> 1) & 7; V^T:
-  // LDS row d (64 B), position p holds chunk p ^ swv(d), swv(d) = (d >> 2) & 3.
-  // Instruction n is 32 K rows / 64 V rows further on, which leaves both
-  // permutations unchanged.
-  auto swk = [](int r) { return (r >> 1) & 7; };
+  // DMA: wave-instruction n (< NI) of wave w fills bytes [(4 n + w) KiB,
+  // +1 KiB) of a tile, lane e 16 bytes at e * 16.  K: LDS row r (D bytes),
+  // position p holds global chunk p ^ swk(r), swk(r) = (r >> 1) & 7 at
+  // D = 128 and (r >> 2) & 3 at D = 64, so that the 16 rows a K operand read
+  // touches at one chunk index fall on distinct banks; V^T: LDS row d (64 B),
+  // position p holds chunk p ^ swv(d), swv(d) = (d >> 2) & 3.  Instruction n
+  // is 32 K rows / 64 V rows further on, which leaves both permutations
+  // unchanged.
+  auto swk = [](int r) { return D == 128 ? (r >> 1) & 7 : (r >> 2) & 3; };
   auto swv = [](int d) { return (d >> 2) & 3; };
   uint32_t dk0, dv0;
   {
     const int pos = w * 1024 + lane * 16;
-    const int r = pos >> 7, pk = (pos & 127) >> 4;
+    const int r = pos >> (D == 128 ? 7 : 6), pk = (pos & (D - 1)) >> 4;
     dk0 = (uint32_t)(r * D + ((pk ^ swk(r)) << 4));
     const int d = pos >> 6, pv = (pos & 63) >> 4;
     dv0 = (uint32_t)(d * 64 + ((pv ^ swv(d)) << 4));
   }
   // LDS read bases: K row l32 (+32 kt), chunk 2 kk + hh; V^T row l32
   // (+32 dt), chunks 2 hh and 2 hh + 1
-  uint32_t kro[4];
+  uint32_t kro[NKK];
 #pragma unroll
-  for (int kk = 0; kk < 4; ++kk) kro[kk] = (uint32_t)(l32 * D + (((2 * kk + hh) ^ swk(l32)) << 4));
+  for (int kk = 0; kk < NKK; ++kk)
+    kro[kk] = (uint32_t)(l32 * D + (((2 * kk + hh) ^ swk(l32)) << 4));
   const uint32_t vro0 = (uint32_t)(l32 * 64 + (((2 * hh) ^ swv(l32)) << 4));
   const uint32_t vro1 = (uint32_t)(l32 * 64 + (((2 * hh + 1) ^ swv(l32)) << 4));
 
@@ -284,7 +295,7 @@ __global__ __launch_bounds__(256, 2) void attn_q_kernel(AttnQArgs a) {
     const uint32_t kb = (uint32_t)blk * 64u * D + dk0;
     const uint32_t vb = (uint32_t)vblk * TV + dv0;
 #pragma unroll
-    for (int n = 0; n < 2; ++n) {
+    for (int n = 0; n < NI; ++n) {
       __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_void_q*)(kdst + (4 * n + w) * 1024), 16,
                                                kb + n * 4096, 0, 0, 0);
       if (vdst)
@@ -318,9 +329,9 @@ __global__ __launch_bounds__(256, 2) void attn_q_kernel(AttnQArgs a) {
     return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va, pb, z, 0, 0, 0, 0, 0, 0);
   };
 
-  f32x16 acc[4];
+  f32x16 acc[NKK];
 #pragma unroll
-  for (int dt = 0; dt < 4; ++dt)
+  for (int dt = 0; dt < NKK; ++dt)
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[dt][r] = 0.f;
   i32x16 sA[2], sB[2];
@@ -367,7 +378,7 @@ __global__ __launch_bounds__(256, 2) void attn_q_kernel(AttnQArgs a) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) sA[kt][r] = 0;
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) sA[kt] = qk_mfma(k0, kt, kk, sA[kt]);
+    for (int kk = 0; kk < NKK; ++kk) sA[kt] = qk_mfma(k0, kt, kk, sA[kt]);
   }
   __syncthreads();
 
@@ -397,7 +408,7 @@ __global__ __launch_bounds__(256, 2) void attn_q_kernel(AttnQArgs a) {
 
     if (__any(rescale != 1.f)) {  // m grew at t - 1
 #pragma unroll
-      for (int dt = 0; dt < 4; ++dt)
+      for (int dt = 0; dt < NKK; ++dt)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[dt][r] *= rescale;
       rescale = 1.f;
@@ -451,20 +462,21 @@ __global__ __launch_bounds__(256, 2) void attn_q_kernel(AttnQArgs a) {
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) sn[kt][r] = 0;
-    // chunk c: P.V of tile t-1 for d rows 32c..32c+31, Q.K^T of tile t+1 for
-    // kk = c (both key halves), softmax of this lane's scores 8c .. 8c+7
-    auto chunk_pv = [&](int c) {
+    // chunk c: softmax of this lane's scores 8c .. 8c+7; and, for c a
+    // multiple of CSTEP (u = c / CSTEP), P.V of tile t-1 for d rows
+    // 32u..32u+31 and Q.K^T of tile t+1 for kk = u (both key halves)
+    auto chunk_pv = [&](int u) {  // d rows 32 u .. 32 u + 31
       if constexpr (VP2) {
-        acc[c] = pv_mfma_acc(v_prev, c, pf, acc[c], vexp_prev);
+        acc[u] = pv_mfma_acc(v_prev, u, pf, acc[u], vexp_prev);
       } else {
-        const f32x16 tmp = pv_mfma(v_prev, c, pf);
+        const f32x16 tmp = pv_mfma(v_prev, u, pf);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc[c][r] = fmaf(vsc_prev, tmp[r], acc[c][r]);
+        for (int r = 0; r < 16; ++r) acc[u][r] = fmaf(vsc_prev, tmp[r], acc[u][r]);
       }
     };
-    auto chunk_qk = [&](int c) {
-      sn[0] = qk_mfma(k_next, 0, c, sn[0]);
-      sn[1] = qk_mfma(k_next, 1, c, sn[1]);
+    auto chunk_qk = [&](int u) {  // d chunk kk = u
+      sn[0] = qk_mfma(k_next, 0, u, sn[0]);
+      sn[1] = qk_mfma(k_next, 1, u, sn[1]);
     };
     auto chunk_soft = [&](int c) {
       const int kt = c >> 1, r0 = 8 * (c & 1);
@@ -488,14 +500,16 @@ __global__ __launch_bounds__(256, 2) void attn_q_kernel(AttnQArgs a) {
     if (pv_prev) {
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        chunk_pv(c);
-        chunk_qk(c);
+        if (c % CSTEP == 0) {
+          chunk_pv(c / CSTEP);
+          chunk_qk(c / CSTEP);
+        }
         chunk_soft(c);
       }
     } else {
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        chunk_qk(c);
+        if (c % CSTEP == 0) chunk_qk(c / CSTEP);
         chunk_soft(c);
       }
     }
@@ -537,14 +551,14 @@ __global__ __launch_bounds__(256, 2) void attn_q_kernel(AttnQArgs a) {
       finish(cnt - 1, attn::group_need(vote[(cnt - 1) & 1], w, a.G), 0u, pend_E);
     if (__any(rescale != 1.f)) {
 #pragma unroll
-      for (int dt = 0; dt < 4; ++dt)
+      for (int dt = 0; dt < NKK; ++dt)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[dt][r] *= rescale;
     }
     if (pv_prev) {  // P.V of the last entry, V in stage (cnt - 1) % 2
       const char* vlast = ((cnt - 1) & 1) ? v1 : v0;
 #pragma unroll
-      for (int dt = 0; dt < 4; ++dt) {
+      for (int dt = 0; dt < NKK; ++dt) {
         if constexpr (VP2) {
           acc[dt] = pv_mfma_acc(vlast, dt, pf, acc[dt], vexp_prev);
         } else {
@@ -565,7 +579,7 @@ __global__ __launch_bounds__(256, 2) void attn_q_kernel(AttnQArgs a) {
     char* orow = static_cast<char*>(a.o) +
                  ((int64_t)b * a.sb + (int64_t)h * a.sh + (int64_t)qrow * a.sn) * oe;
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
+    for (int dt = 0; dt < NKK; ++dt)
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
         const int d = 32 * dt + 8 * g4 + 4 * hh;
@@ -583,21 +597,30 @@ __global__ __launch_bounds__(256, 2) void attn_q_kernel(AttnQArgs a) {
   }
 }
 
-template <int GM, int PM>
+template <int D, int GM, int PM>
 void launch_q(const AttnQArgs& a, bool causal, hipStream_t s) {
   if (causal)
-    hipLaunchKernelGGL((attn_q_kernel<true, GM, PM>), dim3(a.nwg), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((attn_q_kernel<D, true, GM, PM>), dim3(a.nwg), dim3(256), 0, s, a);
   else
-    hipLaunchKernelGGL((attn_q_kernel<false, GM, PM>), dim3(a.nwg), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((attn_q_kernel<D, false, GM, PM>), dim3(a.nwg), dim3(256), 0, s, a);
 }
 
 // precision mode: 0 absmax / 448 V scales; power-of-two V scales with the
 // lambda rule (1) or the recall rule (2)
-template <int GM>
+template <int D, int GM>
 void launch_q(const AttnQArgs& a, bool causal, bool v_pow2, hipStream_t s) {
-  if (!v_pow2) launch_q<GM, 0>(a, causal, s);
-  else if (a.recall_on) launch_q<GM, 2>(a, causal, s);
-  else launch_q<GM, 1>(a, causal, s);
+  if (!v_pow2) launch_q<D, GM, 0>(a, causal, s);
+  else if (a.recall_on) launch_q<D, GM, 2>(a, causal, s);
+  else launch_q<D, GM, 1>(a, causal, s);
+}
+
+template <int D>
+void launch_q_d(const AttnQArgs& a, int group_rows, bool causal, bool v_pow2, hipStream_t s) {
+  switch (attn::group_mode(group_rows)) {
+    case attn::kGroupHalf: launch_q<D, attn::kGroupHalf>(a, causal, v_pow2, s); break;
+    case attn::kGroupMulti: launch_q<D, attn::kGroupMulti>(a, causal, v_pow2, s); break;
+    default: launch_q<D, attn::kGroupWave>(a, causal, v_pow2, s); break;
+  }
 }
 
 }  // namespace
@@ -605,7 +628,10 @@ void launch_q(const AttnQArgs& a, bool causal, bool v_pow2, hipStream_t s) {
 hipError_t launch_quant(const ForwardLaunch& f, hipStream_t s) {
   const Geometry& g = f.g;
   const int64_t blocks = (int64_t)g.B * g.H * (g.nqb + 2 * g.nkb);
-  hipLaunchKernelGGL(quant_kernel, dim3((unsigned)blocks), dim3(256), 0, s, f);
+  if (g.D == 128)
+    hipLaunchKernelGGL(quant_kernel<128>, dim3((unsigned)blocks), dim3(256), 0, s, f);
+  else
+    hipLaunchKernelGGL(quant_kernel<64>, dim3((unsigned)blocks), dim3(256), 0, s, f);
   return hipGetLastError();
 }
 
@@ -640,11 +666,10 @@ hipError_t launch_attn_q(const ForwardLaunch& f, hipStream_t s) {
   a.omr = 1.0f - f.recall;
   if (a.recall_on) a.lam_off = 1;
   a.G = f.group_rows;
-  switch (attn::group_mode(f.group_rows)) {
-    case attn::kGroupHalf: launch_q<attn::kGroupHalf>(a, f.causal, f.v_pow2, s); break;
-    case attn::kGroupMulti: launch_q<attn::kGroupMulti>(a, f.causal, f.v_pow2, s); break;
-    default: launch_q<attn::kGroupWave>(a, f.causal, f.v_pow2, s); break;
-  }
+  if (g.D == 128)
+    launch_q_d<128>(a, f.group_rows, f.causal, f.v_pow2, s);
+  else
+    launch_q_d<64>(a, f.group_rows, f.causal, f.v_pow2, s);
   return hipGetLastError();
 }
 

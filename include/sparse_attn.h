@@ -46,7 +46,7 @@
  * - Supported: D in {64, 128}; block_q = 128, block_k = 64; skip groups of
  *   16, 32, 64 or 128 rows; N <= 262144 (4096 key blocks); one
  *   head's rows (N + 64) * stride_n elements under 2 GiB.  The
- *   quantised variants need dtype = SA_BF16 and D = 128.  Anything else
+ *   quantised variants need dtype = SA_BF16 (D 64 or 128).  Anything else
  *   returns SA_ERR_UNSUPPORTED.
  */
 #ifndef SPARSE_ATTN_H

@@ -83,6 +83,16 @@ def test_shapes_and_workspace():
     assert sa.sparse_attn_workspace_size(p) == (0, 0)
 
 
+@pytest.mark.parametrize("prec", ["i8fp8", "i4fp8", "i8mxfp8"])
+@pytest.mark.parametrize("D", [64, 128])
+def test_quantised_modes_take_both_head_dimensions(prec, D):
+    p = sa.make_params(1, 2, 1000, D, prec=prec)
+    nqb, nkb = sa.sparse_attn_mask_shape(p)
+    _, fws = sa.sparse_attn_workspace_size(p)
+    # INT8 Q and K codes, the e4m3 V^T tiles, and the three scale arrays
+    assert fws >= 2 * 2 * 1000 * D + 2 * nkb * D * 64 + 4 * 2 * (nqb + 2 * nkb)
+
+
 @pytest.mark.parametrize("kw,code", [
     (dict(D=96), sa.SA_ERR_UNSUPPORTED),
     (dict(block_q=64), sa.SA_ERR_UNSUPPORTED),
@@ -93,10 +103,8 @@ def test_shapes_and_workspace():
     (dict(lambda_group_rows=48), sa.SA_ERR_UNSUPPORTED),
     (dict(lambda_group_rows=8), sa.SA_ERR_UNSUPPORTED),
     (dict(prec="i8fp8", dtype="f32"), sa.SA_ERR_UNSUPPORTED),
-    (dict(prec="i4fp8", D=64), sa.SA_ERR_UNSUPPORTED),
     (dict(prec=4), sa.SA_ERR_INVALID_ARG),
     (dict(prec="i8mxfp8", dtype="f32"), sa.SA_ERR_UNSUPPORTED),
-    (dict(prec="i8mxfp8", D=64), sa.SA_ERR_UNSUPPORTED),
     (dict(keep_prefix_kblocks=-1), sa.SA_ERR_INVALID_ARG),
     (dict(N=300000), sa.SA_ERR_UNSUPPORTED),
     (dict(strides=(0, 0, 100)), sa.SA_ERR_INVALID_ARG),

@@ -248,6 +248,19 @@ CASES = [
        lam=-2.0, prec="i8mxfp8", group_rows=16),
     wl("mx_lam_off", 148, 1, 2, 1000, 128, grid=(10, 10, 10), tau=0.9, lam=-math.inf,
        prec="i8mxfp8"),
+    # the quantised modes at d = 64 (two 32-wide d chunks per tile)
+    wl("quant_d64", 160, 1, 2, 1000, 64, grid=(10, 10, 10), tau=0.95, lam=-5.0,
+       rule="energy", prec="i8fp8"),
+    wl("quant4_d64_causal", 161, 1, 2, 700, 64, structure="lm", causal=True, tau=0.9,
+       lam=-4.0, prec="i4fp8", keep_prefix_kblocks=1),
+    wl("mx_d64_recall", 162, 2, 1, 800, 64, grid=(8, 10, 10), tau=0.9, prec="i8mxfp8",
+       skip_rule="recall", recall=0.9),
+    wl("mx_d64_g16_causal", 163, 1, 2, 555, 64, structure="lm", causal=True, tau=0.95,
+       lam=-2.0, prec="i8mxfp8", group_rows=16),
+    wl("quant_d64_g64", 164, 1, 2, 900, 64, grid=(9, 10, 10), tau=0.9, lam=-2.0,
+       prec="i8fp8", group_rows=64),
+    wl("mx_d64_g128_lam_off", 165, 1, 2, 515, 64, grid=(5, 103, 1), tau=0.9,
+       lam=-math.inf, prec="i8mxfp8", group_rows=128),
 ]
 
 
@@ -261,7 +274,8 @@ def test_parity_small(w):
 TINY_FAMILIES = [("bf16", 128, False, "native", 32), ("bf16", 64, True, "native", 32),
                  ("f32", 64, False, "native", 32), ("f32", 128, True, "native", 32),
                  ("bf16", 128, False, "i8fp8", 32), ("bf16", 128, True, "i8mxfp8", 32),
-                 ("bf16", 128, False, "native", 16), ("bf16", 128, True, "native", 64)]
+                 ("bf16", 128, False, "native", 16), ("bf16", 128, True, "native", 64),
+                 ("bf16", 64, False, "i8fp8", 32), ("bf16", 64, True, "i8mxfp8", 16)]
 TINY_N = (1, 7, 64, 65, 129)
 
 
