@@ -52,8 +52,8 @@ MEASURED_TRAFFIC = {
     # (kernel kind, workload, Q.K^T mode) -> (source hash, bytes read, bytes written)
     ("bf16", "wan_video", "native"): ("0887a8417af52975", 111_727_592_064, 335_467_200),
     ("bf16", "hunyuan_video", "native"): ("0887a8417af52975", 984_076_220_928, 731_489_312),
-    ("i8fp8", "quant_long", "i8fp8"): ("6ca5dd8bc36e0476", 96_770_212_352, 268_435_456),
-    ("i8fp8", "quant_long", "i8mxfp8"): ("6ca5dd8bc36e0476", 96_730_270_336, 268_435_456),
+    ("i8fp8", "quant_long", "i8fp8"): ("f7a513c61afa49d1", 96_743_362_304, 268_435_456),
+    ("i8fp8", "quant_long", "i8mxfp8"): ("f7a513c61afa49d1", 96_755_833_728, 268_435_456),
     ("pool", "wan_video", "native"): ("4c1ce0d8f8ed753a", 671_001_856, 15_728_640),
     ("pool", "hunyuan_video", "native"): ("4c1ce0d8f8ed753a", 1_463_053_440, 34_308_096),
     ("pool", "quant_long", "i8fp8"): ("4c1ce0d8f8ed753a", 536_935_808, 12_582_912),
