@@ -400,6 +400,38 @@ class Runner:
         fwd = float(np.mean([b.elapsed_time(c) for _, b, c in ev]))
         return total / steps, pred, fwd, wall
 
+    def time_graph(self, steps):
+        """A step (stage one through the allocation-free predict, then stage
+        two) captured once in a HIP graph and replayed: mean time per replay,
+        HIP events on the replay stream; None where the allocation-free
+        predict's scratch cannot hold the problem."""
+        torch, sa = self.torch, self.sa
+        if sa.sparse_attn_workspace_size(self.p)[0] > (64 << 20):
+            return None
+
+        def step():
+            sa.sparse_attn_predict_noalloc(self.p, self.q, self.k, self.mask)
+            self.forward()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step()
+        for _ in range(2):
+            g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+
     def time_pool(self, steps):
         """Mean time of the predictor's pooling kernel alone
         (sparse_attn_pool), HIP events on the launch stream."""
@@ -901,6 +933,11 @@ def run(args, w, leg):
     head = r.decisions(sample)
     head["o_rows"] = sample.take(torch, r.o)
     pool_ms = r.time_pool(max(5, args.steps))
+    try:
+        graph_ms = r.time_graph(max(5, args.steps))
+    except Exception as e:  # noqa: BLE001 -- context only
+        print(f"[bench] graph replay skipped: {e}", file=sys.stderr, flush=True)
+        graph_ms = None
     esz = 2 if w.dtype == "bf16" else 4
     pool_bytes = (2.0 * w.B * w.H * w.N * w.D * esz +
                   4.0 * w.B * w.H * (r.nqb + r.nkb) * w.D)
@@ -1081,6 +1118,10 @@ def run(args, w, leg):
         "oracle_sample": vs_oracle["sample"] if vs_oracle else None,
         "mask_rows_equal_to_oracle": vs_oracle["mask_rows_exact"] if vs_oracle else None,
         "predict_ms": round(m["predict_ms"], 4),
+        "graph_replay": ({"ms_per_step": round(graph_ms, 4),
+                          "what": "sparse_attn_predict_noalloc + sparse_attn_forward captured "
+                                  "once in a HIP graph and replayed (context: value is the "
+                                  "eager path)"} if graph_ms is not None else None),
         "forward_ms": round(m["forward_ms"], 4),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": traffic,
