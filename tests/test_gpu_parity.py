@@ -358,6 +358,42 @@ def random_group_cases(n=8, seed=20261204):
 RANDOM_GROUP_CASES = random_group_cases()
 
 
+def random_quant_cases(n=16, seed=20261205):
+    """Seeded random cases of the quantised forward: Q.K^T mode, head
+    dimension, causality, mask rule, skip rule, skip group, ragged N, batch
+    and heads, tau, lambda and the forced prefix."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for c in range(n):
+        D = int(rng.choice([64, 128]))
+        causal = bool(rng.random() < 0.4)
+        rule = str(rng.choice(["topcdf", "energy", "topk"]))
+        skip_rule = str(rng.choice(["lambda", "lambda", "recall"]))
+        N = int(rng.integers(130, 1100))
+        B, H = int(rng.integers(1, 3)), int(rng.integers(1, 3))
+        kw = dict(tau=float(rng.choice([0.8, 0.9, 0.95])),
+                  lam=float(rng.choice([-5.0, -2.0, -1.0])),
+                  keep_prefix_kblocks=int(rng.integers(0, 3)), rule=rule,
+                  prec=str(rng.choice(["i8fp8", "i4fp8", "i8mxfp8"])),
+                  skip_rule=skip_rule, recall=0.8,
+                  topk_blocks=int(rng.integers(1, 8)) if rule == "topk" else 0,
+                  group_rows=int(rng.choice([16, 32, 64, 128])))
+        if causal:
+            w = wl(f"random_q_{c}", 400 + c, B, H, N, D, structure="lm", causal=True, **kw)
+        else:
+            w = wl(f"random_q_{c}", 400 + c, B, H, N, D, grid=(N, 1, 1), **kw)
+        out.append(w)
+    return out
+
+
+RANDOM_QUANT_CASES = random_quant_cases()
+
+
+@pytest.mark.parametrize("w", RANDOM_QUANT_CASES, ids=[c.name for c in RANDOM_QUANT_CASES])
+def test_parity_random_quant(w):
+    check_case(w)
+
+
 @pytest.mark.parametrize("w", RANDOM_GROUP_CASES, ids=[c.name for c in RANDOM_GROUP_CASES])
 def test_parity_random_groups(w):
     check_case(w)
