@@ -347,11 +347,12 @@ class Runner:
     """Owns the device buffers of one configuration and runs the two calls."""
 
     def __init__(self, sa, torch, w, q, k, v, tau, skip_rule="lambda", recall=1.0, rule=None,
-                 topk_blocks=0, prec=None):
+                 topk_blocks=0, prec=None, lam=None):
         self.sa, self.torch, self.w = sa, torch, w
         self.q, self.k, self.v = q, k, v
         self.o = torch.empty_like(q)
-        kw = dict(dtype=w.dtype, causal=w.causal, tau=tau, lam=w.lam, rule=rule or w.rule,
+        kw = dict(dtype=w.dtype, causal=w.causal, tau=tau, lam=w.lam if lam is None else lam,
+                  rule=rule or w.rule,
                   prec=prec or w.prec, topk_blocks=topk_blocks,
                   keep_prefix_kblocks=w.keep_prefix_kblocks, skip_rule=skip_rule,
                   recall=recall)
@@ -903,12 +904,12 @@ def run(args, w, leg):
     captures = {}  # name -> {"cnt", "bits", "o_rows"} for the CPU-baseline leg
 
     def measure(tau, steps, warmup, skip_rule=None, recall=None, rule=None, topk_blocks=0,
-                tensors=None, prec=None, o_view=None, key=None):
+                tensors=None, prec=None, o_view=None, key=None, lam=None):
         qq, kk, vv = tensors or (q, k, v)
         r = Runner(sa, torch, w, qq, kk, vv, tau,
                    skip_rule=skip_rule or args.skip_rule,
                    recall=args.recall if recall is None else recall, rule=rule,
-                   topk_blocks=topk_blocks, prec=prec)
+                   topk_blocks=topk_blocks, prec=prec, lam=lam)
         ms, pred_ms, fwd_ms, wall = r.time_steps(steps, warmup)
         o_rows = sample.take(torch, o_view(r) if o_view else r.o)
         dec = r.decisions()
@@ -947,6 +948,20 @@ def run(args, w, leg):
 
     sweep, recall_sweep, topk_sweep = [], [], []
     few = max(3, args.steps // 4)
+
+    # the same mask and kernel with the skip switched off (lambda = -inf):
+    # every kept tile multiplies, so the forward is a dense product over the
+    # kept tiles, comparable with a plain GEMM's rate on this chip
+    skip_off = None
+    if not args.no_sweep:
+        rs, ms_ = measure(w.tau, few, 1, lam=float("-inf"))
+        tf = ms_["exec_flops"] / (ms_["forward_ms"] * 1e-3) / 1e12
+        skip_off = {"lambda": "-inf", "forward_ms": round(ms_["forward_ms"], 4),
+                    "pv_skip_fraction": round(ms_["skip"], 5),
+                    "executed_flops_per_launch": ms_["exec_flops"],
+                    "achieved": round(tf, 2), "frac": round(tf / peak, 4)}
+        del rs
+        print(f"[bench] skip off: {skip_off}", file=sys.stderr, flush=True)
 
     def sweep_row(key, ms_, **fields):
         return dict(**fields, key=key, sparsity=round(ms_["sparsity"], 5),
@@ -1046,6 +1061,10 @@ def run(args, w, leg):
             peaks = measured_peaks(torch, dev, sampler, probe)
         except Exception as e:  # noqa: BLE001
             print(f"[bench] reference peaks skipped: {e}", file=sys.stderr, flush=True)
+        if skip_off is not None and peaks and peaks.get("bf16_gemm_8192_tflops") \
+                and w.dtype == "bf16" and w.prec not in QUANT_PRECS:
+            skip_off["vs_bf16_gemm"] = round(skip_off["achieved"] /
+                                             peaks["bf16_gemm_8192_tflops"], 4)
 
     cpu, vs_oracle = None, None
     if leg is not None:
@@ -1123,6 +1142,7 @@ def run(args, w, leg):
                                   "once in a HIP graph and replayed (context: value is the "
                                   "eager path)"} if graph_ms is not None else None),
         "forward_ms": round(m["forward_ms"], 4),
+        "skip_off": skip_off,
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": traffic,
                      "kernel": FORWARD_KERNELS[kind][0],
