@@ -87,7 +87,12 @@ enum { SA_F32 = 0, SA_BF16 = 1 };
  * with a power-of-two V scale per key block: 2^e with e the smallest integer
  * such that absmax <= 448 * 2^e (the E8M0 block scale of the OCP
  * microscaling formats; the pages fix no V scale), V codes e4m3(V / 2^e); the
- * scaled FP8 MFMA applies it in hardware, so the mode is the faster one. */
+ * scaled FP8 MFMA applies it in hardware, so the mode is the faster one.  It
+ * also normalises differently: l (the divisor of O and the l of lse) is the
+ * sum of the quantised weights e4m3(2^8 P) / 2^8 over the kept tiles,
+ * skipped ones included, instead of the sum of P, so that without skips O is
+ * an exact weighted average of V's dequantised codes; the skip decisions are
+ * taken as in SA_PREC_I8_FP8 (SA_SKIP_RECALL's energies from P itself). */
 enum { SA_PREC_NATIVE = 0, SA_PREC_I8_FP8 = 1, SA_PREC_I4_FP8 = 2, SA_PREC_I8_MXFP8 = 3 };
 /* Mask rule of stage one.  TOPCDF: P-hat = softmax of the block scores over
  * the admissible key blocks.  ENERGY: P-hat_j proportional to
