@@ -61,6 +61,11 @@ def decode_skips(bits, cnt):
     ("wan_video", [29], 4, dict(tau=0.99)),
     ("wan_video", [5], 4, dict(rule="topk", topk_blocks=443)),
     ("wan_video", [36], 4, dict(rule="topk", topk_blocks=256)),
+    # the same masks with the skip switched off (lambda = -inf), which the
+    # bench times beside the headline: no group may skip
+    ("wan_video", [21], 4, dict(lam=-math.inf)),
+    ("quant_long", [9], 4, dict(lam=-math.inf)),
+    ("quant_long", [14], 4, dict(prec="i8mxfp8", lam=-math.inf)),
     ("hunyuan_video", [7, 19], 8, {}),
     ("lm_causal", [0, 31], 5, {}),
     ("quant_long", [5], 4, {}),
@@ -140,6 +145,11 @@ def test_fullsize_parity(name, heads, nblocks, over):
                 assert F[i, lst[:n_f[i]]].all()
                 full = bits_h[b, h, i, :, c // 32 + (1 if c % 32 else 0):]
                 assert not full.any()
+    if w.lam == -math.inf and w.skip_rule == "lambda":
+        # lambda = -inf never skips, except groups past the last row of a
+        # partial block, which hold no rows and read as skipped
+        real = -(-(w.N - (nqb - 1) * 128) // w.group_rows)
+        assert not bits_h[:, :, :-1].any() and not bits_h[:, :, -1, :real].any()
 
     tau32 = float(np.float32(w.tau))
     lam32 = float(np.float32(w.lam))
