@@ -93,6 +93,9 @@ def parse():
                          "workload's own)")
     ap.add_argument("--recall", type=float, default=0.95,
                     help="target recall of the recall skip rule")
+    ap.add_argument("--lam", type=float, default=None,
+                    help="lambda of the timed configuration (default: the workload's; "
+                         "--lam=-inf switches the skip off), for per-kernel profiles")
     ap.add_argument("--no-peaks", action="store_true",
                     help="skip the GEMM / copy reference measurements")
     ap.add_argument("--stage", default="all", choices=("all", "cluster"),
@@ -850,6 +853,8 @@ def main():
                   file=sys.stderr)
             sys.exit(2)
         w = make_workload(args.workload, prec=args.prec)
+    if args.lam is not None:
+        w = make_workload(args.workload, prec=w.prec, lam=args.lam)
     leg = None
     if not args.no_cpu_baseline and args.stage == "all":
         # forked now, while nothing in this process has touched the GPU
@@ -952,15 +957,14 @@ def run(args, w, leg):
     # the same mask and kernel with the skip switched off (lambda = -inf):
     # every kept tile multiplies, so the forward is a dense product over the
     # kept tiles, comparable with a plain GEMM's rate on this chip
-    skip_off = None
+    skip_off, r_off = None, None
     if not args.no_sweep:
-        rs, ms_ = measure(w.tau, few, 1, lam=float("-inf"))
+        r_off, ms_ = measure(w.tau, few, 1, lam=float("-inf"))
         tf = ms_["exec_flops"] / (ms_["forward_ms"] * 1e-3) / 1e12
         skip_off = {"lambda": "-inf", "forward_ms": round(ms_["forward_ms"], 4),
                     "pv_skip_fraction": round(ms_["skip"], 5),
                     "executed_flops_per_launch": ms_["exec_flops"],
-                    "achieved": round(tf, 2), "frac": round(tf / peak, 4)}
-        del rs
+                    "achieved": round(tf, 2), "frac": round(tf / peak, 4), "clock": None}
         print(f"[bench] skip off: {skip_off}", file=sys.stderr, flush=True)
 
     def sweep_row(key, ms_, **fields):
@@ -1054,6 +1058,13 @@ def run(args, w, leg):
                                                     4),
                              "source": "s_memtime against s_memrealtime, one wavefront on a "
                                        "side stream during ten forward launches"}
+                if r_off is not None:
+                    ghz = sampler.around(lambda: [r_off.forward() for _ in range(10)], 0.1)
+                    if ghz:
+                        skip_off["clock"] = {
+                            "forward_ghz": round(ghz, 3),
+                            "frac_at_clock": round(skip_off["achieved"] /
+                                                   (peak * ghz / PEAK_CLOCK_GHZ), 4)}
         except Exception as e:  # noqa: BLE001
             print(f"[bench] clock reading skipped: {e}", file=sys.stderr, flush=True)
             sampler = None
@@ -1065,6 +1076,7 @@ def run(args, w, leg):
                 and w.dtype == "bf16" and w.prec not in QUANT_PRECS:
             skip_off["vs_bf16_gemm"] = round(skip_off["achieved"] /
                                              peaks["bf16_gemm_8192_tflops"], 4)
+    r_off = None  # the skip-off leg's buffers
 
     cpu, vs_oracle = None, None
     if leg is not None:
@@ -1121,7 +1133,8 @@ def run(args, w, leg):
         "dtype": "i8/fp8" if w.prec in QUANT_PRECS else w.dtype,
         "data": data_description(w),
         "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "D": w.D,
-                   "causal": w.causal, "tau": w.tau, "lambda": w.lam, "rule": w.rule,
+                   "causal": w.causal, "tau": w.tau,
+                   "lambda": w.lam if math.isfinite(w.lam) else str(w.lam), "rule": w.rule,
                    "block_q": 128, "block_k": 64, "lambda_group_rows": 32,
                    "skip_rule": args.skip_rule,
                    **({"recall": args.recall} if args.skip_rule == "recall" else {}),
