@@ -29,13 +29,15 @@ namespace {
 
 constexpr int kThreads = 256;
 
+// (class, s desc, j asc) order of two packed keys (class << 16 | j); both
+// scores are read whatever the classes (every j < P2 has one), so the
+// comparison is a chain of selects rather than branches
 __device__ __forceinline__ bool sorts_before(int ka, int kb, const double* val) {
   const int ca = ka >> 16, cb = kb >> 16;
-  if (ca != cb) return ca < cb;
   const int ja = ka & 0xffff, jb = kb & 0xffff;
   const double sa_ = val[ja], sb_ = val[jb];
-  if (sa_ != sb_) return sa_ > sb_;
-  return ja < jb;
+  const bool by_s = sa_ != sb_ ? sa_ > sb_ : ja < jb;
+  return ca != cb ? ca < cb : by_s;
 }
 
 __device__ __forceinline__ double block_reduce_max(double v, double* scratch) {
@@ -161,8 +163,9 @@ __global__ __launch_bounds__(kThreads) void mask_kernel(PredictLaunch a, int P2)
         const int hi = lo + stride;
         const int klo = key[lo], khi = key[hi];
         const bool asc = (lo & size) == 0;
-        const bool swap = asc ? sorts_before(khi, klo, val) : sorts_before(klo, khi, val);
-        if (swap) {
+        // swap when kx sorts before ky: one comparison, no divergent arms
+        const int kx = asc ? khi : klo, ky = asc ? klo : khi;
+        if (sorts_before(kx, ky, val)) {
           key[lo] = khi;
           key[hi] = klo;
         }
