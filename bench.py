@@ -50,10 +50,10 @@ METRIC = "dense-equiv attention TFLOPS + sparsity at fixed rel-L1, N=32760 H=40 
 # kernel reports null until it is measured again.
 MEASURED_TRAFFIC = {
     # (kernel kind, workload, Q.K^T mode) -> (source hash, bytes read, bytes written)
-    ("bf16", "wan_video", "native"): ("0887a8417af52975", 111_727_592_064, 335_467_200),
-    ("bf16", "hunyuan_video", "native"): ("0887a8417af52975", 984_076_220_928, 731_489_312),
-    ("i8fp8", "quant_long", "i8fp8"): ("f7a513c61afa49d1", 96_743_362_304, 268_435_456),
-    ("i8fp8", "quant_long", "i8mxfp8"): ("f7a513c61afa49d1", 96_755_833_728, 268_435_456),
+    ("bf16", "wan_video", "native"): ("aba23ef178feac18", 111_721_873_280, 335_469_792),
+    ("bf16", "hunyuan_video", "native"): ("aba23ef178feac18", 983_999_294_976, 731_502_560),
+    ("i8fp8", "quant_long", "i8fp8"): ("18544d539b55e1cd", 96_777_516_928, 268_435_456),
+    ("i8fp8", "quant_long", "i8mxfp8"): ("18544d539b55e1cd", 96_733_693_056, 268_435_456),
     ("pool", "wan_video", "native"): ("4c1ce0d8f8ed753a", 671_001_856, 15_728_640),
     ("pool", "hunyuan_video", "native"): ("4c1ce0d8f8ed753a", 1_463_053_440, 34_308_096),
     ("pool", "quant_long", "i8fp8"): ("4c1ce0d8f8ed753a", 536_935_808, 12_582_912),

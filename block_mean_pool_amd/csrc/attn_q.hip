@@ -193,8 +193,11 @@ typedef int i32x8 __attribute__((ext_vector_type(8)));
 // mode's reading), summed by one more scaled MFMA per tile with an all-ones
 // operand instead of 31 adds per lane.  Mode 2 (the recall rule) still sums
 // the unquantised weights on the VALU for the rule's energies.
+// Two workgroups per CU at d = 128, three at d = 64 (168 VGPRs; the
+// power-of-two mode spills a few registers there and still runs 12 % faster
+// than at two, the absmax mode as fast).
 template <int D, bool CAUSAL, int GM, int PM>
-__global__ __launch_bounds__(256, 2) void attn_q_kernel(AttnQArgs a) {
+__global__ __launch_bounds__(256, D == 64 ? 3 : 2) void attn_q_kernel(AttnQArgs a) {
   constexpr bool VP2 = PM != 0, ROWSUM_VALU = PM != 1;
   // 32-wide d chunks: the K extent of one INT8 Q.K^T MFMA, and the d rows of
   // one FP8 P.V MFMA; a region of four chunks issues the MFMAs of one d chunk
