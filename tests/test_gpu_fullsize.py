@@ -84,6 +84,9 @@ def decode_skips(bits, cnt):
     ("wan_video", [6], 4, dict(H=8, N=66000, grid=(22, 50, 60), skip_rule="recall",
                                recall=0.95, group_rows=128)),
     ("wan_video", [13], 4, dict(group_rows=16)),
+    # the longest sequence the library takes (N = 262144: 4096 key blocks,
+    # the mask kernel's largest sort), three heads, so the V-vote schedule
+    ("wan_video", [0, 2], 3, dict(H=3, N=262144, grid=(16, 128, 128))),
     # half-wavefront groups and four-wavefront groups in the V-vote schedule
     ("wan_video", [4], 4, dict(H=8, N=66000, grid=(22, 50, 60), group_rows=16)),
     ("wan_video", [1], 4, dict(H=8, N=66000, grid=(22, 50, 60), group_rows=128)),
