@@ -278,6 +278,12 @@ def measured_peaks(torch, dev, sampler=None, probe=None):
     return out
 
 
+def json_number(x):
+    """A float for the JSON line: non-finite values (lambda = -inf) as their
+    string, so the line stays strict JSON."""
+    return x if math.isfinite(x) else str(x)
+
+
 def _r3(x):
     return None if x is None else round(x, 3)
 
@@ -1134,7 +1140,7 @@ def run(args, w, leg):
         "data": data_description(w),
         "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "D": w.D,
                    "causal": w.causal, "tau": w.tau,
-                   "lambda": w.lam if math.isfinite(w.lam) else str(w.lam), "rule": w.rule,
+                   "lambda": json_number(w.lam), "rule": w.rule,
                    "block_q": 128, "block_k": 64, "lambda_group_rows": 32,
                    "skip_rule": args.skip_rule,
                    **({"recall": args.recall} if args.skip_rule == "recall" else {}),

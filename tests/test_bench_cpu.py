@@ -48,3 +48,20 @@ def test_source_hash_covers_each_forward_kernel():
     for kind, (_, files) in bench.FORWARD_KERNELS.items():
         assert "attn_common.h" in files
         assert bench.kernel_source_hash(kind) == hashes[kind]
+
+
+def test_lambda_option_switches_the_skip_off(monkeypatch):
+    # --lam=-inf (the skip off, for per-kernel profiles) reaches the
+    # workload; the JSON line names a non-finite lambda as a string, so the
+    # line stays strict JSON
+    import json
+    import math
+    monkeypatch.setattr(sys, "argv", ["bench.py", "--lam=-inf"])
+    args = bench.parse()
+    assert args.lam == -math.inf
+    from synth import make_workload
+    w = make_workload("wan_video", lam=args.lam)
+    assert w.lam == -math.inf
+    line = json.dumps({"lambda": bench.json_number(w.lam)}, allow_nan=False)
+    assert json.loads(line)["lambda"] == "-inf"
+    assert bench.json_number(-5.0) == -5.0
