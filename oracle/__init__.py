@@ -53,6 +53,7 @@ from .sparse_attn_oracle import (  # noqa: F401
 )
 from .quant import (  # noqa: F401
     e4m3_round,
+    e4m3_flip_slack,
     e4m3_encode,
     int8_quantize_blocks,
     int_quantize_blocks,

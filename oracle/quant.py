@@ -64,6 +64,18 @@ def e4m3_round(x) -> np.ndarray:
     return out
 
 
+def e4m3_flip_slack(x, eps) -> np.ndarray:
+    """How far e4m3_round can move when its argument moves by a relative
+    error of at most ``eps`` (elementwise, eps >= 0): e4m3_round(x (1 + eps))
+    - e4m3_round(x (1 - eps)) for x >= 0.  Rounding is monotone, so any value
+    in that interval rounds within this distance of e4m3_round(x); the
+    result is 0 where no rounding boundary lies in the interval.  Used to
+    bound the effect of a code computed in lower precision than here."""
+    x = np.asarray(x, dtype=np.float64)
+    eps = np.asarray(eps, dtype=np.float64)
+    return e4m3_round(x * (1.0 + eps)) - e4m3_round(x * (1.0 - eps))
+
+
 def e4m3_encode(x) -> np.ndarray:
     """Bit patterns (uint8) of e4m3_round(x)."""
     r = e4m3_round(x)
@@ -157,7 +169,7 @@ def fp8_quantize_v_blocks_pow2(V, bk: int):
 def sparse_attention_quant_head(Q, K, V, kept: List[np.ndarray], p: Params,
                                 force_skip: Optional[List[np.ndarray]] = None,
                                 deltas: Optional[list] = None, qmax: int = 127,
-                                v_pow2: bool = False):
+                                v_pow2: bool = False, code_slack: Optional[list] = None):
     """Quantised stage two: the same online softmax, processing order and
     skip rule as the unquantised oracle, with
     S = sm * s_q(i) * s_k(j) * (Qcode . Kcode)  (exact integer dot product) and
@@ -167,6 +179,16 @@ def sparse_attention_quant_head(Q, K, V, kept: List[np.ndarray], p: Params,
     INT8 Q/K codes, 7 for 4-bit ones; ``v_pow2`` takes V's scales from
     fp8_quantize_v_blocks_pow2 and normalises O (and lse) by the running sum
     of the quantised weights.
+    ``code_slack`` (a list, filled per query block) receives, for v_pow2, a
+    per-row bound on how far that sum can move, relative to the sum, when
+    each weight's code e4m3(2^8 P) is taken from P computed in fp32 instead
+    of fp64 (0 for the other modes and for rows with no weight).  With
+    u = 2^-24: the exponent argument (S - m), formed from fp32 factors (a
+    scale that is a product of three, the running max, one fused
+    multiply-add), moves P by at most u (4 |S| + 6 |m| + 16) relative, and
+    the exp2 by a few u more; eps = 2^-21 (|S| + |m|) + 2^-19 covers both
+    with a factor of two to spare, and each code can then move by
+    e4m3_flip_slack of eps.
     Returns (O, lse, skips)."""
     N, d = np.asarray(Q).shape
     sm = p.sm(d)
@@ -185,6 +207,7 @@ def sparse_attention_quant_head(Q, K, V, kept: List[np.ndarray], p: Params,
         m = np.full(nr, -np.inf)
         l = np.zeros(nr)
         lq = np.zeros(nr)     # v_pow2: running sum of the quantised weights
+        lslack = np.zeros(nr)  # code_slack: bound on the change of lq
         acc = np.zeros((nr, d))
         drop = np.zeros(nr)
         sk = np.zeros((len(lst), n_groups), dtype=bool)
@@ -208,6 +231,10 @@ def sparse_attention_quant_head(Q, K, V, kept: List[np.ndarray], p: Params,
             acc = alpha[:, None] * acc
             Pq = e4m3_round(P * 256.0) / 256.0
             lq = alpha * lq + Pq.sum(axis=1)
+            if code_slack is not None:
+                smax = np.where(np.isfinite(S), np.abs(S), 0.0).max(axis=1)
+                eps = 2.0 ** -21 * (smax + np.abs(safe)) + 2.0 ** -19
+                lslack = alpha * lslack + e4m3_flip_slack(P * 256.0, eps[:, None]).sum(axis=1) / 256.0
             delta_r = np.where(np.isfinite(mloc), mloc - safe, -np.inf)
             for g in range(n_groups):
                 gr = slice(g * p.G, min(nr, (g + 1) * p.G))
@@ -224,6 +251,9 @@ def sparse_attention_quant_head(Q, K, V, kept: List[np.ndarray], p: Params,
         skips.append(sk)
         if deltas is not None:
             deltas.append(dl)
+        if code_slack is not None:
+            rel = np.divide(lslack, lq, out=np.zeros(nr), where=lq > 0)
+            code_slack.append(rel if v_pow2 else np.zeros(nr))
         ln = lq if v_pow2 else l
         ok = ln > 0
         O[rows[ok]] = acc[ok] / ln[ok, None]
@@ -231,6 +261,6 @@ def sparse_attention_quant_head(Q, K, V, kept: List[np.ndarray], p: Params,
     return O, lse, skips
 
 
-__all__ = ["e4m3_round", "e4m3_encode", "int8_quantize_blocks", "int_quantize_blocks",
+__all__ = ["e4m3_round", "e4m3_flip_slack", "e4m3_encode", "int8_quantize_blocks", "int_quantize_blocks",
            "fp8_quantize_v_blocks", "pow2_scale", "fp8_quantize_v_blocks_pow2",
            "sparse_attention_quant_head", "math"]

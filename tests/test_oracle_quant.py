@@ -286,3 +286,65 @@ def test_pow2_output_is_a_weighted_average_of_quantised_values():
     vc = np.tile(np.float32([0.5, -1.25, 3.0, 0.0, 2.0, -4.0, 1.0, 0.125]), (N, 1))
     got, _, _ = O.sparse_attention_quant_head(q, k, vc, kept, p, v_pow2=True)
     np.testing.assert_allclose(got, np.tile(vc[0], (N, 1)), rtol=0, atol=1e-12)
+
+
+def test_flip_slack_bounds_every_perturbed_rounding():
+    # e4m3_round is monotone, so every value within a relative eps of x
+    # rounds within e4m3_flip_slack(x, eps) of e4m3_round(x); the slack is 0
+    # on the e4m3 grid (far from a rounding boundary) and one step at a
+    # midpoint
+    rng = np.random.default_rng(41)
+    x = rng.uniform(0.0, 300.0, 20000)
+    eps = 10.0 ** rng.uniform(-7, -2, x.size)
+    slack = O.e4m3_flip_slack(x, eps)
+    base = O.e4m3_round(x)
+    for _ in range(8):
+        r = rng.uniform(-1.0, 1.0, x.size) * eps
+        assert np.all(np.abs(O.e4m3_round(x * (1.0 + r)) - base) <= slack)
+    grid = O.e4m3_round(rng.uniform(1.0, 256.0, 1000))
+    assert np.all(O.e4m3_flip_slack(grid, 1e-4) == 0.0)
+    np.testing.assert_array_equal(O.e4m3_flip_slack(np.array([1.0625, 17.0, 136.0]), 1e-6),
+                                  [0.125, 2.0, 16.0])
+
+
+def test_code_slack_bounds_codes_computed_in_fp32():
+    # One kept tile per query block (128 of them).  The quantised
+    # weights' sum of the power-of-two mode, recomputed with the exponent
+    # argument and exp2 in fp32 (scale = fl(fl(fl(sm log2e) sq) sk), max,
+    # 8 - max, one fused multiply-add), changes some rows' codes; every
+    # row's lse stays within the bound code_slack gives.
+    rng = np.random.default_rng(43)
+    N, d = 16384, 128
+    q = (rng.standard_normal((N, d)) * 2).astype(np.float32)
+    k = (rng.standard_normal((N, d)) * 2).astype(np.float32)
+    v = rng.standard_normal((N, d)).astype(np.float32)
+    sm = float(np.float32(1 / math.sqrt(d)))
+    p = O.Params(BQ=128, BK=64, causal=False, tau=0.9, lam=-math.inf, G=32, sm_scale=sm)
+    nqb = N // 128
+    kept = [np.array([(3 * i + 1) % (N // 64)]) for i in range(nqb)]
+    slack = []
+    _, lse, _ = O.sparse_attention_quant_head(q, k, v, kept, p, v_pow2=True, code_slack=slack)
+    qc, qs = O.int8_quantize_blocks(q, 128)
+    kc, ks = O.int8_quantize_blocks(k, 64)
+    f32 = np.float32
+    c2 = f32(f32(sm) * f32(1.4426950408889634))
+    flips = 0
+    for i in range(nqb):
+        j = int(kept[i][0])
+        rows, cols = slice(i * 128, (i + 1) * 128), slice(j * 64, (j + 1) * 64)
+        dot = qc[rows].astype(np.int64) @ kc[cols].astype(np.int64).T
+        csc = f32(f32(c2 * f32(qs[i])) * f32(ks[j]))
+        x = dot.astype(f32)
+        m2 = (x.max(axis=1) * csc).astype(f32)                    # log2 units
+        cb = (f32(8.0) - m2).astype(f32)
+        arg = (x.astype(np.float64) * float(csc) + cb.astype(np.float64)[:, None]).astype(f32)
+        codes = O.e4m3_round(np.exp2(arg).astype(np.float64))     # 2^8 P
+        lse32 = (m2.astype(np.float64) + np.log2(codes.sum(axis=1) / 256.0)) * math.log(2.0)
+        S = sm * float(qs[i]) * float(ks[j]) * dot.astype(np.float64)
+        rel = slack[i]
+        assert np.all(rel < 1.0)
+        tol = 1e-5 + np.maximum(np.log1p(rel), -np.log1p(-rel))
+        assert np.all(np.abs(lse32 - lse[rows]) <= tol), i
+        # codes taken from the fp64 scores, to show that fp32 moves some
+        flips += int(np.sum(codes != O.e4m3_round(256.0 * np.exp(S - S.max(axis=1)[:, None]))))
+    assert flips > 0
