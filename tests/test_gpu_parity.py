@@ -494,8 +494,13 @@ def test_long_sequence_masks(rule):
     check_case(w, check_out=False)
 
 
-def test_parity_strided_layout():
-    w = wl("strided_bnhd", 109, 2, 3, 600, 128, grid=(6, 10, 10), tau=0.9, lam=-5.0)
+@pytest.mark.parametrize("prec,D", [("native", 128), ("i8fp8", 64), ("i8mxfp8", 128)])
+def test_parity_strided_layout(prec, D):
+    # [B, N, H, D] storage through the B/H/N strides, for the native forward
+    # and for the quantiser and quantised forward, which read Q, K, V and
+    # write O through the same strides
+    w = wl(f"strided_bnhd_{prec}", 109, 2, 3, 600, D, grid=(6, 10, 10), tau=0.9, lam=-5.0,
+           prec=prec)
     check_case(w, layout="bnhd")
 
 
