@@ -183,12 +183,12 @@ def sparse_attention_quant_head(Q, K, V, kept: List[np.ndarray], p: Params,
     per-row bound on how far that sum can move, relative to the sum, when
     each weight's code e4m3(2^8 P) is taken from P computed in fp32 instead
     of fp64 (0 for the other modes and for rows with no weight).  With
-    u = 2^-24: the exponent argument (S - m), formed from fp32 factors (a
-    scale that is a product of three, the running max, one fused
-    multiply-add), moves P by at most u (4 |S| + 6 |m| + 16) relative, and
-    the exp2 by a few u more; eps = 2^-21 (|S| + |m|) + 2^-19 covers both
-    with a factor of two to spare, and each code can then move by
-    e4m3_flip_slack of eps.
+    u = 2^-24: the exponent argument (S - m) in log2 units, formed from fp32
+    values (a scale carrying four roundings: log2(e), sm, s_q, s_k; the
+    running max; 8 - max; one fused multiply-add), moves P by at most
+    u (5 |S| + 7 |m| + 11) relative, and the exp2 by a few u more;
+    eps = 2^-21 (|S| + |m|) + 2^-19 covers both, and each code can then
+    move by e4m3_flip_slack of eps.
     Returns (O, lse, skips)."""
     N, d = np.asarray(Q).shape
     sm = p.sm(d)
