@@ -348,3 +348,13 @@ def test_code_slack_bounds_codes_computed_in_fp32():
         # codes taken from the fp64 scores, to show that fp32 moves some
         flips += int(np.sum(codes != O.e4m3_round(256.0 * np.exp(S - S.max(axis=1)[:, None]))))
     assert flips > 0
+
+
+def test_flip_slack_at_the_ends_of_the_e4m3_range():
+    # subnormals (a fixed quantum of 2^-9): the midpoint 3 * 2^-10 between
+    # 2^-9 and 2^-8 can round either way, 2^-9 itself cannot; zero stays
+    # zero; at the top, values round to 448 and saturate there, so the
+    # midpoint 432 between 416 and 448 has one step of slack and 448 none
+    x = np.array([0.0, 3 * 2.0 ** -10, 2.0 ** -9, 432.0, 448.0, 500.0])
+    np.testing.assert_array_equal(O.e4m3_flip_slack(x, 1e-6),
+                                  [0.0, 2.0 ** -9, 0.0, 32.0, 0.0, 0.0])
